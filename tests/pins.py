@@ -1,0 +1,354 @@
+"""Pins for the CPU oracle: checks against closed forms, brute force and
+independent library routines.  Each check takes the oracle routine under test
+as an argument, so ``test_oracle_mutations.py`` can run the same checks on a
+deliberately broken copy of the oracle and confirm that they fail.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+
+def all_parent_arrays(n: int):
+    """Every valid parent array with n nodes (p[0] = -1, 0 <= p[i] < i)."""
+    for tail in itertools.product(*[range(i) for i in range(1, n)]):
+        yield [-1, *tail]
+
+
+def closure_masks(p) -> list[int]:
+    """Ancestor-or-self sets by transitive closure of the child->parent
+    relation (Warshall), an algorithm independent of parent-pointer walks."""
+    n = len(p)
+    R = [[i == j for j in range(n)] for i in range(n)]
+    for i in range(1, n):
+        R[i][p[i]] = True
+    for k in range(n):
+        for i in range(n):
+            if R[i][k]:
+                for j in range(n):
+                    if R[k][j]:
+                        R[i][j] = True
+    return [sum(1 << j for j in range(n) if R[i][j]) for i in range(n)]
+
+
+def brute_force_walk(p, d, t):
+    """Enumerate every root-to-node path, keep the fully matched ones and take
+    the deepest, ties to the lower end index."""
+    n = len(p)
+    best = None
+    for e in range(n):
+        path = [e]
+        while path[-1] != 0:
+            path.append(p[path[-1]])
+        path = path[::-1]
+        if all(d[path[k]] == t[path[k - 1]] for k in range(1, len(path))):
+            key = (len(path) - 1, -e)
+            if best is None or key > best[0]:
+                best = (key, path)
+    L = best[0][0]
+    path = best[1]
+    return L, path, [t[x] for x in path]
+
+
+def read_golden(name: str):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([c.strip() for c in line.split("|")])
+    return rows
+
+
+def ints(s: str) -> list[int]:
+    return [int(x, 0) for x in s.split()]
+
+
+# ------------------------------------------------------------------- mask
+
+def check_mask_golden(build_masks):
+    for name, par, masks, depths in read_golden("mask_hand_examples.txt"):
+        m, dep = build_masks(np.array([ints(par)], dtype=np.int32))
+        assert [int(x) for x in m[0]] == ints(masks), name
+        assert [int(x) for x in dep[0]] == ints(depths), name
+
+
+def check_mask_closed_forms(build_masks):
+    for n in (1, 2, 6, 33, 63, 64):
+        chain = np.arange(-1, n - 1, dtype=np.int32)[None]
+        m, dep = build_masks(chain)
+        assert [int(x) for x in m[0]] == [(1 << (i + 1)) - 1 for i in range(n)]
+        assert list(dep[0]) == list(range(n))
+        star = np.array([[-1] + [0] * (n - 1)], dtype=np.int32)
+        m, dep = build_masks(star)
+        assert [int(x) for x in m[0]] == [1] + [1 | (1 << i) for i in range(1, n)]
+        assert list(dep[0]) == [0] + [1] * (n - 1)
+
+
+def check_mask_brute_force(build_masks, max_n: int = 7):
+    for n in range(1, max_n + 1):
+        arrs = list(all_parent_arrays(n))
+        m, dep = build_masks(np.array(arrs, dtype=np.int32))
+        for b, p in enumerate(arrs):
+            want = closure_masks(p)
+            assert [int(x) for x in m[b]] == want, p
+            assert [int(x) for x in dep[b]] == [bin(w).count("1") - 1 for w in want], p
+
+
+# ------------------------------------------------------------------- walk
+
+def check_walk_golden(accept_walk):
+    for name, par, d, t, L, path, toks in read_golden("walk_hand_examples.txt"):
+        p = ints(par)
+        n = len(p)
+        al, pn, ot = accept_walk(np.array([p]), np.array([ints(d)]), np.array([ints(t)]))
+        Lw = int(L)
+        assert int(al[0]) == Lw, name
+        assert list(pn[0]) == ints(path) + [-1] * (n - Lw - 1), name
+        assert list(ot[0]) == ints(toks) + [-1] * (n - Lw - 1), name
+
+
+def check_walk_brute_force(accept_walk, max_n: int = 6, draws: int = 4, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    for n in range(1, max_n + 1):
+        arrs = list(all_parent_arrays(n))
+        for _ in range(draws):
+            Vs = int(rng.integers(1, 4))
+            d = rng.integers(0, Vs, size=(len(arrs), n))
+            t = rng.integers(0, Vs, size=(len(arrs), n))
+            al, pn, ot = accept_walk(np.array(arrs), d, t)
+            for b, p in enumerate(arrs):
+                L, path, toks = brute_force_walk(p, list(d[b]), list(t[b]))
+                assert int(al[b]) == L, (p, d[b], t[b])
+                assert list(pn[b][:L + 1]) == path and all(x == -1 for x in pn[b][L + 1:])
+                assert list(ot[b][:L + 1]) == toks and all(x == -1 for x in ot[b][L + 1:])
+
+
+def check_walk_chain_closed_forms(accept_walk):
+    n = 6
+    p = np.arange(-1, n - 1)[None]
+    t = np.array([[11, 12, 13, 14, 15, 16]])
+    all_match = np.array([[0, 11, 12, 13, 14, 15]])
+    al, pn, ot = accept_walk(p, all_match, t)
+    assert int(al[0]) == n - 1
+    assert list(ot[0]) == [11, 12, 13, 14, 15, 16]      # accepted drafts, then the bonus
+    for k in range(1, n):
+        d = all_match.copy()
+        d[0, k] = 999
+        al, pn, ot = accept_walk(p, d, t)
+        assert int(al[0]) == k - 1
+        assert list(pn[0][:k]) == list(range(k))
+    al, pn, ot = accept_walk(np.array([[-1]]), np.array([[5]]), np.array([[7]]))
+    assert int(al[0]) == 0 and list(pn[0]) == [0] and list(ot[0]) == [7]
+
+
+def check_walk_depth_bound_and_greedy(accept_walk, build_masks, seed: int = 1):
+    """L never exceeds the tree's depth; when sibling draft tokens are
+    distinct the longest path is the greedy one (follow the one matching
+    child at every level)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(300):
+        n = int(rng.integers(1, 20))
+        p = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+        t = list(rng.integers(0, 5, size=n))
+        kids = [[] for _ in range(n)]
+        for i in range(1, n):
+            kids[p[i]].append(i)
+        d = [int(rng.integers(0, 1000))] + [0] * (n - 1)
+        for u in range(n):                   # distinct draft tokens among siblings
+            for c, tok in zip(kids[u], rng.permutation(8)):
+                d[c] = int(tok)
+        al, pn, ot = accept_walk(np.array([p]), np.array([d]), np.array([t]))
+        _, dep = build_masks(np.array([p]))
+        assert int(al[0]) <= int(dep[0].max())
+        u, L = 0, 0
+        while True:
+            nxt = [c for c in kids[u] if d[c] == t[u]]
+            assert len(nxt) <= 1
+            if not nxt:
+                break
+            u, L = nxt[0], L + 1
+        assert int(al[0]) == L
+
+
+# --------------------------------------------------------------- argmax
+
+def check_argmax_constructed(vocab_argmax):
+    rows = np.zeros((7, 16), dtype=np.float32)
+    rows[0] = 1.0                                   # all equal -> 0
+    rows[1] = -3.0
+    rows[1, [3, 7]] = 2.5                           # duplicated maxima -> 3
+    rows[2] = np.linspace(-1, 1, 16)
+    rows[2, 9] = 100.0                              # planted spike
+    rows[3] = -1.0
+    rows[3, 5] = -0.0
+    rows[3, 2] = 0.0                                # +0 and -0 compare equal -> 2
+    rows[4] = -np.float32(3.4e38)                   # extreme finite values
+    rows[4, 15] = np.float32(3.4e38)
+    rows[5] = np.arange(16, dtype=np.float32)[::-1]  # strictly decreasing -> 0
+    rows[6] = -2.0
+    rows[6, 1] = -0.0
+    rows[6, 4] = 0.0                                # -0 first, +0 later: still the first -> 1
+    got = vocab_argmax(rows)
+    assert list(got) == [0, 3, 9, 2, 15, 0, 1]
+
+
+def check_argmax_brute_force(vocab_argmax, seed: int = 2):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-3, 4, size=(200, 37)).astype(np.float32)  # many ties
+    x[rng.random(x.shape) < 0.1] = -0.0
+    got = vocab_argmax(x)
+    for r in range(x.shape[0]):
+        best = 0
+        for v in range(1, x.shape[1]):
+            if x[r, v] > x[r, best]:
+                best = v
+        assert int(got[r]) == best
+
+
+# ------------------------------------------------------------- attention
+
+def sdpa_f64(q, k, v, mask, scale):
+    """torch's scaled_dot_product_attention on CPU in float64 (math path),
+    q: [H][M][D], k/v: [H][L][D], mask bool [M][L]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask), scale=scale).numpy()
+
+
+def rand_case(rng, B, N, Hq, Hkv, D, P, S_extra=3, tree="random"):
+    if tree == "chain":
+        parents = np.tile(np.arange(-1, N - 1), (B, 1)).astype(np.int32)
+    elif tree == "star":
+        parents = np.tile(np.array([-1] + [0] * (N - 1)), (B, 1)).astype(np.int32)
+    else:
+        parents = np.stack([[-1] + [int(rng.integers(0, i)) for i in range(1, N)]
+                            for _ in range(B)]).astype(np.int32)
+    prefix = np.asarray(P, dtype=np.int32).reshape(-1)
+    if prefix.size == 1:
+        prefix = np.full(B, int(prefix[0]), dtype=np.int32)
+    S = int(prefix.max()) + N + S_extra
+    q = rng.standard_normal((B, N, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    return parents, prefix, q, k, v
+
+
+def check_attention_chain_is_causal(tree_attention, seed: int = 3):
+    """A chain-shaped tree equals bottom-right-aligned causal attention over
+    prefix + chain."""
+    rng = np.random.default_rng(seed)
+    for (B, N, Hq, Hkv, D, P) in [(2, 6, 4, 2, 8, 5), (1, 5, 2, 1, 16, 0), (2, 8, 6, 3, 4, [3, 11])]:
+        parents, prefix, q, k, v = rand_case(rng, B, N, Hq, Hkv, D, P, tree="chain")
+        sc = 0.3
+        out, lse = tree_attention(q, k, v, prefix, parents, sc, q_fmt="f32", kv_fmt="f32")
+        g = Hq // Hkv
+        for b in range(B):
+            Pb = int(prefix[b])
+            L = Pb + N
+            causal = np.tril(np.ones((N, L), dtype=bool), k=Pb)
+            kk = np.repeat(k[b, :, :L].astype(np.float64), g, axis=0)
+            vv = np.repeat(v[b, :, :L].astype(np.float64), g, axis=0)
+            qq = q[b].astype(np.float64).transpose(1, 0, 2)      # [Hq][N][D]
+            ref = sdpa_f64(qq, kk, vv, causal, sc).transpose(1, 0, 2)
+            np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+            s = sc * np.einsum("hnd,hld->hnl", qq, kk)
+            s = np.where(causal[None], s, -np.inf)
+            ref_lse = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy().transpose(1, 0)
+            np.testing.assert_allclose(lse[b], ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def check_attention_one_node_is_decode(tree_attention, seed: int = 4):
+    """A one-node tree equals plain decode attention over P+1 keys."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, D = 3, 4, 2, 8
+    parents, prefix, q, k, v = rand_case(rng, B, 1, Hq, Hkv, D, [0, 7, 20])
+    out, _ = tree_attention(q, k, v, prefix, parents, 0.25, q_fmt="f32", kv_fmt="f32")
+    for b in range(B):
+        L = int(prefix[b]) + 1
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            ref = sdpa_f64(q[b, :, h][None].astype(np.float64), k[b, kvh, :L][None].astype(np.float64),
+                           v[b, kvh, :L][None].astype(np.float64), np.ones((1, L), dtype=bool), 0.25)
+            np.testing.assert_allclose(out[b, 0, h], ref[0, 0], rtol=1e-12, atol=1e-12)
+
+
+def check_attention_node_locality(tree_attention, seed: int = 5):
+    """Each node's output equals causal attention over the prefix plus its own
+    root-to-node chain (K/V rows gathered from the cache)."""
+    rng = np.random.default_rng(seed)
+    for (B, N, Hq, Hkv, D, P) in [(2, 9, 4, 2, 8, [6, 0]), (1, 16, 2, 2, 4, 13), (1, 7, 3, 1, 5, 2)]:
+        parents, prefix, q, k, v = rand_case(rng, B, N, Hq, Hkv, D, P)
+        out, _ = tree_attention(q, k, v, prefix, parents, 0.5, q_fmt="f32", kv_fmt="f32")
+        g = Hq // Hkv
+        for b in range(B):
+            Pb = int(prefix[b])
+            for i in range(N):
+                chain = [i]
+                while parents[b][chain[-1]] != -1:
+                    chain.append(int(parents[b][chain[-1]]))
+                rows = list(range(Pb)) + [Pb + j for j in sorted(chain)]
+                for h in range(Hq):
+                    kk = k[b, h // g, rows].astype(np.float64)[None]
+                    vv = v[b, h // g, rows].astype(np.float64)[None]
+                    qq = q[b, i, h].astype(np.float64)[None, None]
+                    ref = sdpa_f64(qq, kk, vv, np.ones((1, len(rows)), dtype=bool), 0.5)
+                    np.testing.assert_allclose(out[b, i, h], ref[0, 0], rtol=1e-12, atol=1e-12)
+
+
+def check_attention_gqa_is_mha(tree_attention, seed: int = 6):
+    """GQA equals MHA after repeating each KV head over its query group."""
+    rng = np.random.default_rng(seed)
+    B, N, Hq, Hkv, D = 2, 7, 6, 2, 8
+    parents, prefix, q, k, v = rand_case(rng, B, N, Hq, Hkv, D, [4, 9])
+    out, lse = tree_attention(q, k, v, prefix, parents, 0.3, q_fmt="f32", kv_fmt="f32")
+    g = Hq // Hkv
+    out2, lse2 = tree_attention(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), prefix, parents,
+                                0.3, q_fmt="f32", kv_fmt="f32")
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def check_attention_closed_form(tree_attention):
+    """P = 0, N = 2 (root and one child), D = 1, sm_scale = 1: the root sees
+    only its own key; the child sees both."""
+    q = np.array([[[[0.5]], [[1.0]]]], dtype=np.float32)           # [1][2][1][1]
+    k = np.array([[[[2.0], [-1.0]]]], dtype=np.float32)             # [1][1][2][1]
+    v = np.array([[[[3.0], [7.0]]]], dtype=np.float32)
+    out, lse = tree_attention(q, k, v, np.array([0]), np.array([[-1, 0]]), 1.0, q_fmt="f32", kv_fmt="f32")
+    assert out[0, 0, 0, 0] == 3.0
+    assert lse[0, 0, 0] == 1.0                                      # 0.5 * 2
+    e0, e1 = math.exp(2.0), math.exp(-1.0)
+    assert abs(out[0, 1, 0, 0] - (3.0 * e0 + 7.0 * e1) / (e0 + e1)) < 1e-14
+    assert abs(lse[0, 1, 0] - math.log(e0 + e1)) < 1e-14
+    # two siblings under the root: each sees the root and itself only
+    q3 = np.ones((1, 3, 1, 1), dtype=np.float32)
+    k3 = np.array([[[[0.0], [1.0], [2.0]]]], dtype=np.float32)
+    v3 = np.array([[[[1.0], [10.0], [100.0]]]], dtype=np.float32)
+    out3, _ = tree_attention(q3, k3, v3, np.array([0]), np.array([[-1, 0, 0]]), 1.0, q_fmt="f32", kv_fmt="f32")
+    e = math.exp
+    assert abs(out3[0, 1, 0, 0] - (1.0 + 10.0 * e(1)) / (1 + e(1))) < 1e-12
+    assert abs(out3[0, 2, 0, 0] - (1.0 + 100.0 * e(2)) / (1 + e(2))) < 1e-12
+
+
+def check_attention_ignores_rows_past_tree(tree_attention, seed: int = 7):
+    """Cache rows at or beyond P_b + N belong to nobody: filling them with NaN
+    changes nothing."""
+    rng = np.random.default_rng(seed)
+    parents, prefix, q, k, v = rand_case(rng, 2, 5, 2, 1, 4, [3, 8], S_extra=4)
+    out, _ = tree_attention(q, k, v, prefix, parents, 0.7, q_fmt="f32", kv_fmt="f32")
+    k2, v2 = k.copy(), v.copy()
+    for b in range(2):
+        k2[b, :, int(prefix[b]) + 5:] = np.nan
+        v2[b, :, int(prefix[b]) + 5:] = np.nan
+    out2, _ = tree_attention(q, k2, v2, prefix, parents, 0.7, q_fmt="f32", kv_fmt="f32")
+    np.testing.assert_array_equal(out, out2)
