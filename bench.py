@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Verify-step throughput on one MI355X.
+
+One step = the whole verify hot path for one batch of synthetic inputs that
+are already resident in HBM: ancestor-mask build, tree-masked split-KV
+attention, per-node vocabulary argmax, accept walk.  The default workload is
+the batch-8 lookahead-5 chain in bf16 (32 query heads over 8 KV heads,
+head dim 128, 2048-token prefixes, 32000-token vocabulary).
+
+Timing: W untimed warm-up steps, then K steps timed with torch.cuda
+synchronisation on both sides.  Each step replays a HIP graph holding the four
+library calls for one of R input replicas; R is chosen so that the replicas
+together exceed the GPU's last-level (MALL) cache, so every step streams its
+K/V and logits from HBM.
+
+The dominant kernel (the tree attention) is also timed on its own with HIP
+events on the stream that runs it: a graph of back-to-back attention calls
+over the replicas, elapsed time / number of calls.  Its algorithmic bytes
+(each K/V byte of every request's prefix+tree once per KV head, Q, outputs,
+masks) over that time give roofline.achieved.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+METRIC = "tree-verify steps/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
+DEFAULT_WORKLOAD = "chain6_b8_h32x8_d128_p2048_bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="workload name or index 0-4")
+    ap.add_argument("--no-graph", action="store_true", help="launch the four calls eagerly each step")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the argmax on a second stream, concurrent with the attention")
+    ap.add_argument("--replica-bytes", type=float, default=1.0e9,
+                    help="total bytes of input replicas to rotate through (defeats the MALL)")
+    ap.add_argument("--attn-calls", type=int, default=200, help="calls in the attention timing graph")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def workload(name):
+    import synth
+    if name.isdigit():
+        return synth.WORKLOADS[int(name)]
+    return synth.workload_by_name(name)
+
+
+def algorithmic_bytes(w, prefix_lens):
+    """Bytes each step must move, by kernel (each input read once, each output
+    written once)."""
+    kv_elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    q_elem = {"f32": 4, "bf16": 2}[w.q_dtype]
+    B, N = w.B, w.N
+    tokens = int(sum(int(p) + N for p in prefix_lens))
+    kv = tokens * w.Hkv * w.D * 2 * kv_elem
+    q = B * N * w.Hq * w.D * q_elem
+    attn = kv + 2 * q + 8 * B * N + 4 * B + 4 * B * N * w.Hq + (8 * w.Hkv if w.kv_dtype == "e4m3" else 0)
+    argmax = B * N * w.V * 4 + 4 * B * N
+    mask = 16 * B * N
+    walk = 28 * B * N + 4 * B
+    flops = 4 * w.D * w.Hq * N * tokens
+    return dict(attention=attn, kv=kv, argmax=argmax, mask=mask, walk=walk,
+                step=attn + argmax + mask + walk, attn_flops=flops, tokens=tokens)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_attention_verify_parent_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wname):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x, seconds):
+    """The CPU oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from tests.gpu_util import oracle_views
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    w = x["workload"]
+    qo, ko, vo = oracle_views(x)
+    logits = x["logits"].numpy()
+    B, N = w.B, w.N
+
+    def run(nreq):
+        sl = slice(0, nreq)
+        oracle.verify_step(x["parents"][sl], x["draft_tokens"][sl], x["prefix_lens"][sl], qo[sl], ko[sl],
+                           vo[sl], logits[: nreq * N], x["sm_scale"], q_fmt=w.q_dtype, kv_fmt=w.kv_dtype,
+                           k_scale=x["k_scale"], v_scale=x["v_scale"], V=w.V)
+
+    t0 = time.perf_counter()
+    run(1)
+    one = time.perf_counter() - t0
+    if one * B <= seconds:
+        reps, done, t0 = 0, 0.0, time.perf_counter()
+        while done < seconds:
+            run(B)
+            reps += 1
+            done = time.perf_counter() - t0
+        return dict(value=reps / done, unit="steps/s", cores=int(cores), kind="oracle",
+                    sample=f"{reps} full steps ({B} requests each), {done:.1f} s")
+    nreq = max(1, min(B, int(seconds / max(one, 1e-9))))
+    t0 = time.perf_counter()
+    run(nreq)
+    dt = time.perf_counter() - t0
+    return dict(value=(nreq / B) / dt, unit="steps/s", cores=int(cores), kind="oracle",
+                sample=f"{nreq} of {B} requests of one step ({dt:.1f} s), scaled to a full step")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the verify step is measured per GPU and this build "
+              "has no multi-GPU path (requests would shard across GPUs with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import tree_attention_verify_parent_amd as st
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    st.lib()
+    dev = torch.device("cuda:0")
+    w = workload(args.workload)
+    x = synth.make_inputs(w)
+    B, N = w.B, w.N
+    bytes_ = algorithmic_bytes(w, x["prefix_lens"])
+
+    # ---- inputs in HBM, replicated so the rotation exceeds the MALL
+    per_replica = (x["q"].numel() * x["q"].element_size() + 2 * x["k_cache"].numel() * x["k_cache"].element_size()
+                   + x["logits"].numel() * 4)
+    free = torch.cuda.mem_get_info()[0]
+    R = int(max(1, min(64, math.ceil(args.replica_bytes / per_replica), (0.5 * free) // per_replica)))
+    parents = torch.from_numpy(x["parents"]).to(dev)
+    draft = torch.from_numpy(x["draft_tokens"]).to(dev)
+    prefix = torch.from_numpy(x["prefix_lens"]).to(dev)
+    ks = None if x["k_scale"] is None else torch.from_numpy(x["k_scale"]).to(dev)
+    vs = None if x["v_scale"] is None else torch.from_numpy(x["v_scale"]).to(dev)
+    qs, kcs, vcs, lgs = [], [], [], []
+    q0, k0, v0, l0 = (x["q"].to(dev), x["k_cache"].to(dev), x["v_cache"].to(dev), x["logits"].to(dev))
+    for r in range(R):
+        qs.append(q0 if r == 0 else q0.clone())
+        kcs.append(k0 if r == 0 else k0.clone())
+        vcs.append(v0 if r == 0 else v0.clone())
+        lgs.append(l0 if r == 0 else l0.clone())
+
+    anc = torch.empty((B, N), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q0)
+    lse = torch.empty((B, N, w.Hq), dtype=torch.float32, device=dev)
+    amax = torch.empty(B * N, dtype=torch.int32, device=dev)
+    acc_len = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_bytes = st.attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, w.S_max)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream(device=dev) if args.overlap else None
+
+    def attention(r):
+        st.tree_attn_verify(qs[r], kcs[r], vcs[r], prefix, anc, x["sm_scale"], k_scale=ks, v_scale=vs,
+                            out=out, lse=lse, workspace=ws, err=err)
+
+    def step(r):
+        st.tree_mask_build(parents, anc_mask=anc, depth=depth, err=err)
+        if side is not None:
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                st.vocab_argmax(lgs[r], out=amax)
+            attention(r)
+            main.wait_stream(side)
+        else:
+            attention(r)
+            st.vocab_argmax(lgs[r], out=amax)
+        st.accept_walk(parents, anc, draft, amax.view(B, N), w.V, accept_len=acc_len, path_nodes=path,
+                       out_tokens=toks, err=err)
+
+    # eager warm-up (loads kernels), then correctness sanity of the result
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise SystemExit(f"device error word 0x{int(err.item()):x}")
+
+    graphs = None
+    if not args.no_graph:
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_steps(k, start=0):
+        for i in range(start, start + k):
+            if graphs is not None:
+                graphs[i % R].replay()
+            else:
+                step(i % R)
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    run_steps(args.steps, args.warmup)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    steps_per_s = args.steps / wall
+
+    # ---- dominant kernel: back-to-back attention calls, HIP events on the
+    # stream that runs them
+    calls = max(args.attn_calls, R)
+    ag = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ag):
+        for c in range(calls):
+            attention(c % R)
+    torch.cuda.synchronize()
+    ag.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(reps):
+        ag.replay()
+    a1.record()
+    torch.cuda.synchronize()
+    attn_us = a0.elapsed_time(a1) * 1e3 / (reps * calls)
+
+    hbm_bound = not (w.kv_dtype == "bf16" and w.group * w.N > 312)
+    if hbm_bound:
+        achieved = bytes_["attention"] / (attn_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    else:
+        achieved = bytes_["attn_flops"] / (attn_us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "spec_tree_attn_verify (split-KV attention + split merge)"
+    roof["launch_us"] = round(attn_us, 3)
+    roof["bytes_per_launch"] = bytes_["attention"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, args.cpu_baseline_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.kv_dtype == "f32" else ("bf16" if w.kv_dtype == "bf16" else "bf16+e4m3kv"),
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "tree_nodes": N, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "prefix": [w.prefix_lo, w.prefix_hi], "vocab": w.V,
+                   "graph": graphs is not None, "overlap": bool(args.overlap), "replicas": R},
+        "tree_tokens_per_s": round(steps_per_s * B * N, 1),
+        "step_hbm_gbs": round(bytes_["step"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(bytes_["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "ms_per_step_events": round(ev_ms, 5),
+        "accept_len_mean": round(float(acc_len.float().mean().item()), 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * spectree -- speculative-decoding tree verify step for AMD CDNA4 (gfx950).
+ *
+ * A draft model proposes a tree of tokens; the target model checks the whole
+ * tree in one parallel pass and keeps the longest prefix it agrees with
+ * (Aurora, chernovdev.ru / everytik.com mirrors, section 2 "serve-to-train
+ * flywheel": the inference server verifies the draft's proposal in parallel;
+ * Runtime Draft Model Training, moreh.io, "Overview").  One verify step is:
+ *
+ *   spec_tree_mask_build   parent array -> 64-bit ancestor-or-self masks
+ *   spec_tree_attn_verify  tree-masked split-KV attention over the KV cache
+ *   spec_vocab_argmax      per-node argmax of the target logits
+ *   spec_accept_walk       longest matched root-to-node path -> accepted tokens
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or synchronises; each call validates its host-side
+ *     arguments, enqueues kernels on `stream` and returns.
+ *   - Inputs are read only; outputs are fully overwritten.  Inputs and outputs
+ *     must not alias.
+ *   - A non-SPEC_OK return means nothing was enqueued (except SPEC_ERR_HIP,
+ *     which reports a failed launch).
+ *   - Errors that only the data can show are found on the device and OR'ed
+ *     into *err_word (nullable; the caller zeroes it before the call and reads
+ *     it after synchronising).  A request whose data is flagged gets
+ *     unspecified outputs; other requests are unaffected.
+ *   - Calls are thread safe; the library holds no state.
+ *
+ * Tree layout (a reading: the pages describe the mask only as following "the
+ * causal structure of the speculative tree", Aurora section 2, closing
+ * paragraph): request b has N nodes, parents[b][0] == -1 is the root (the
+ * last committed token) and 0 <= parents[b][i] < i.  A node attends to the
+ * request's whole KV prefix plus its ancestors and itself.
+ */
+#ifndef SPECTREE_H
+#define SPECTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = 1,      /* a required pointer is NULL                         */
+  SPEC_ERR_SHAPE = 2,     /* a size is out of range or inconsistent             */
+  SPEC_ERR_DTYPE = 3,     /* unsupported dtype or dtype pair                    */
+  SPEC_ERR_WORKSPACE = 4, /* workspace missing or smaller than required         */
+  SPEC_ERR_HIP = 5,       /* a kernel launch failed                             */
+  SPEC_ERR_ALIGN = 6      /* a pointer is not 16-byte aligned where required    */
+} spec_status;
+
+typedef enum {
+  SPEC_F32 = 0,
+  SPEC_BF16 = 1,
+  SPEC_FP8_E4M3 = 2       /* OCP FP8 E4M3 ("e4m3fn"): bias 7, no inf, max 448 */
+} spec_dtype;
+
+/* Device-detected data errors, OR'ed into *err_word. */
+#define SPEC_DERR_ROOT   1u  /* parents[b][0] != -1                          */
+#define SPEC_DERR_PARENT 2u  /* parents[b][i] not in [0, i) for some i >= 1   */
+#define SPEC_DERR_PREFIX 4u  /* prefix_lens[b] < 0 or prefix_lens[b]+N > S_max */
+#define SPEC_DERR_TOKEN  8u  /* a draft token or target argmax not in [0, V)  */
+
+#define SPEC_MAX_NODES 64
+
+/*
+ * spec_tree_mask_build -- ancestor-or-self bitmasks of each draft tree.
+ *
+ * The custom attention mask that follows the speculative tree's causal
+ * structure (Aurora section 2, closing paragraph on tree attention), packed
+ * as one 64-bit word per node.
+ *
+ *   parents   int32[B][N]   parent index of each node (see tree layout above)
+ *   B         >= 1          requests
+ *   N         1..64         nodes per request
+ *   anc_mask  uint64[B][N]  out: bit j of anc_mask[b][i] set iff node j is node
+ *                           i or one of its ancestors
+ *   depth     int32[B][N]   out, nullable: edges from the root to node i
+ *   err_word  uint32*       nullable: SPEC_DERR_ROOT / SPEC_DERR_PARENT
+ *   stream    HIP stream to enqueue on
+ */
+spec_status spec_tree_mask_build(const int32_t* parents, int B, int N,
+                                 uint64_t* anc_mask, int32_t* depth,
+                                 uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_tree_attn_workspace_bytes -- scratch needed by spec_tree_attn_verify
+ * for these sizes (0 when the launch needs none).  Pure function of its
+ * arguments; returns 0 for sizes spec_tree_attn_verify would reject.
+ */
+size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max);
+
+/*
+ * spec_tree_attn_verify -- tree-masked attention of every draft node.
+ *
+ * The target model checks all proposed tokens in one parallel pass (Runtime
+ * Draft Model Training, "Overview"), each node's query seeing the request's
+ * KV-cache prefix plus only its own ancestors and itself (Aurora section 2,
+ * tree attention).  For request b, node i, query head h, kv head
+ * kvh = h / (Hq/Hkv), with P = prefix_lens[b]:
+ *     keys c in [0, P)                        : the prefix, always visible
+ *     keys c = P + j, j in [0, N)             : tree node j, visible iff bit j
+ *                                               of anc_mask[b][i] is set
+ *     s_c = sm_scale * <q[b][i][h], K[b][kvh][c]>
+ *     out[b][i][h] = sum_c softmax(s)_c * V[b][kvh][c]
+ *     lse[b][i][h] = log sum_c exp(s_c)
+ * Cache rows >= P + N are never read.
+ *
+ *   q          [B][N][Hq][D] of q_dtype (SPEC_F32 or SPEC_BF16), 16-B aligned
+ *   k_cache,
+ *   v_cache    [B][Hkv][S_max][D] of kv_dtype, 16-B aligned; tree node j of
+ *              request b is row prefix_lens[b] + j
+ *   k_scale,
+ *   v_scale    float[Hkv]: per-KV-head dequantisation scales; required iff
+ *              kv_dtype == SPEC_FP8_E4M3 (K = code * k_scale[kvh]), else ignored
+ *   prefix_lens int32[B]
+ *   anc_mask   uint64[B][N] from spec_tree_mask_build
+ *   D          64 or 128
+ *   sm_scale   softmax scale (typically 1/sqrt(D))
+ *   out        [B][N][Hq][D] of q_dtype, 16-B aligned
+ *   lse        float[B][N][Hq], nullable
+ *   workspace  >= spec_tree_attn_workspace_bytes(...) bytes, 16-B aligned;
+ *              may be NULL when that size is 0.  Contents need no
+ *              initialisation; concurrent calls must not share it.
+ *   err_word   nullable: SPEC_DERR_PREFIX
+ * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * Results are deterministic: the split-K merge runs in a fixed order.
+ */
+spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype,
+                                  const void* k_cache, const void* v_cache, spec_dtype kv_dtype,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                  int B, int N, int Hq, int Hkv, int D, int S_max,
+                                  float sm_scale, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes,
+                                  uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_vocab_argmax -- per-row argmax of float32 logits.
+ *
+ * Under greedy verification the target's token at a node is the argmax of
+ * its logits (the target "verifies" the draft: Aurora section 2).  Ties go
+ * to the lowest index; -0.0 and +0.0 compare equal.  Logits must be finite.
+ *
+ *   logits     float[rows][row_stride], row r's V logits at logits + r*row_stride
+ *   rows       >= 1;  V >= 1;  row_stride >= V
+ *   out_idx    int32[rows]
+ */
+spec_status spec_vocab_argmax(const float* logits, int64_t rows, int64_t V, int64_t row_stride,
+                              int32_t* out_idx, hipStream_t stream);
+
+/*
+ * spec_accept_walk -- accepted path, tokens and acceptance length per request.
+ *
+ * Acceptance length is the number of draft tokens the target accepts in one
+ * verification step (Runtime Draft Model Training, "Evaluation").  Node
+ * i >= 1 matches when draft_tokens[b][i] == target_argmax[b][parents[b][i]];
+ * a node is accepted when every node on its root path (root excluded)
+ * matches; the accepted path ends at the deepest accepted node, ties going to
+ * the lowest node index.
+ *
+ *   parents        int32[B][N]
+ *   anc_mask       uint64[B][N] from spec_tree_mask_build
+ *   draft_tokens   int32[B][N]  (node 0's token is never compared)
+ *   target_argmax  int32[B][N]  (spec_vocab_argmax of the [B*N][V] logits)
+ *   V              vocabulary size (token range check)
+ *   accept_len     int32[B]     out: L = accepted draft tokens, 0 <= L <= depth
+ *   path_nodes     int32[B][N]  out: node at depth k of the path, k = 0..L; -1 after
+ *   out_tokens     int32[B][N]  out: target_argmax along the path, k = 0..L (the
+ *                               L accepted tokens, then the bonus token); -1 after
+ *   err_word       nullable: SPEC_DERR_ROOT / _PARENT / _TOKEN
+ */
+spec_status spec_accept_walk(const int32_t* parents, const uint64_t* anc_mask,
+                             const int32_t* draft_tokens, const int32_t* target_argmax,
+                             int B, int N, int V,
+                             int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                             uint32_t* err_word, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* spec_status_string(spec_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECTREE_H */

@@ -92,28 +92,8 @@ def _kv_rows(cache, b: int, kvh: int, L: int, fmt: str, scale) -> np.ndarray:
     return _as_f64(rows, fmt)
 
 
-def tree_attention_bh(q, k_cache, v_cache, prefix_lens, parents, sm_scale, b, h, *,
-                      q_fmt, kv_fmt, k_scale=None, v_scale=None):
-    """Outputs of all N nodes of request b for query head h.
-
-    q: [B][N][Hq][D] (float32 values, or uint16 bf16 bit patterns);
-    k_cache/v_cache: [B][Hkv][S_max][D] (float32, uint16 bf16 bits or uint8
-    e4m3 codes).  Returns (out float64[N][D], lse float64[N]).
-    """
-    B, N, Hq, D = q.shape
-    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
-    if Hq % Hkv:
-        raise ValueError("Hq must be a multiple of Hkv")
-    g = Hq // Hkv
-    kvh = h // g
-    P = int(prefix_lens[b])
-    L = P + N
-    if P < 0 or L > S_max:
-        raise ValueError(f"prefix {P} + {N} nodes does not fit {S_max} cache rows")
-    A = dense_tree_mask(parents[b], P)
-    Kf = _kv_rows(k_cache, b, kvh, L, kv_fmt, k_scale)
-    Vf = _kv_rows(v_cache, b, kvh, L, kv_fmt, v_scale)
-    Q = _as_f64(np.asarray(q[b, :, h, :]), q_fmt)            # [N][D]
+def _attend(Q, Kf, Vf, A, sm_scale):
+    """Q [N][D], Kf/Vf [L][D] float64, A bool[N][L] -> (out [N][D], lse [N])."""
     s = float(sm_scale) * (Q @ Kf.T)                         # [N][L]
     s = np.where(A, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
@@ -125,16 +105,52 @@ def tree_attention_bh(q, k_cache, v_cache, prefix_lens, parents, sm_scale, b, h,
     return out, lse
 
 
+def _request(q, k_cache, prefix_lens, b):
+    B, N, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    P = int(prefix_lens[b])
+    if P < 0 or P + N > S_max:
+        raise ValueError(f"prefix {P} + {N} nodes does not fit {S_max} cache rows")
+    return P, P + N, Hq // Hkv
+
+
+def tree_attention_bh(q, k_cache, v_cache, prefix_lens, parents, sm_scale, b, h, *,
+                      q_fmt, kv_fmt, k_scale=None, v_scale=None):
+    """Outputs of all N nodes of request b for query head h.
+
+    q: [B][N][Hq][D] (float32 values, or uint16 bf16 bit patterns);
+    k_cache/v_cache: [B][Hkv][S_max][D] (float32, uint16 bf16 bits or uint8
+    e4m3 codes).  Returns (out float64[N][D], lse float64[N]).
+    """
+    P, L, g = _request(q, k_cache, prefix_lens, b)
+    kvh = h // g
+    A = dense_tree_mask(parents[b], P)
+    Kf = _kv_rows(k_cache, b, kvh, L, kv_fmt, k_scale)
+    Vf = _kv_rows(v_cache, b, kvh, L, kv_fmt, v_scale)
+    Q = _as_f64(np.asarray(q[b, :, h, :]), q_fmt)            # [N][D]
+    return _attend(Q, Kf, Vf, A, sm_scale)
+
+
 def tree_attention(q, k_cache, v_cache, prefix_lens, parents, sm_scale, *,
                    q_fmt, kv_fmt, k_scale=None, v_scale=None):
-    """All outputs: (out float64[B][N][Hq][D], lse float64[B][N][Hq])."""
+    """All outputs: (out float64[B][N][Hq][D], lse float64[B][N][Hq]).
+
+    Same arithmetic as tree_attention_bh for every (b, h); the exact upcast
+    of a kv head's rows is done once and shared by the heads of its group.
+    """
     B, N, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
     out = np.empty((B, N, Hq, D), dtype=np.float64)
     lse = np.empty((B, N, Hq), dtype=np.float64)
     for b in range(B):
-        for h in range(Hq):
-            o, l = tree_attention_bh(q, k_cache, v_cache, prefix_lens, parents, sm_scale, b, h,
-                                     q_fmt=q_fmt, kv_fmt=kv_fmt, k_scale=k_scale, v_scale=v_scale)
-            out[b, :, h, :] = o
-            lse[b, :, h] = l
+        P, L, g = _request(q, k_cache, prefix_lens, b)
+        A = dense_tree_mask(parents[b], P)
+        for kvh in range(Hkv):
+            Kf = _kv_rows(k_cache, b, kvh, L, kv_fmt, k_scale)
+            Vf = _kv_rows(v_cache, b, kvh, L, kv_fmt, v_scale)
+            for h in range(kvh * g, (kvh + 1) * g):
+                Q = _as_f64(np.asarray(q[b, :, h, :]), q_fmt)
+                out[b, :, h, :], lse[b, :, h] = _attend(Q, Kf, Vf, A, sm_scale)
     return out, lse

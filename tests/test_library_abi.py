@@ -1,0 +1,108 @@
+"""The C-ABI library loads and exports every symbol that include/spectree.h
+declares; host-side argument checks reject bad calls before any launch.
+CPU only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verify_parent_amd as st
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spectree.h")
+
+SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_DTYPE, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP, SPEC_ERR_ALIGN = range(7)
+FAKE = ctypes.c_void_p(0x1000)        # never dereferenced: every call below fails host checks first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(st.library_path):
+        pytest.skip("libspectree.so not built")
+    return st.lib()
+
+
+def test_header_declares_the_four_steps():
+    names = declared_functions()
+    for n in ("spec_tree_mask_build", "spec_tree_attn_verify", "spec_vocab_argmax", "spec_accept_walk",
+              "spec_tree_attn_workspace_bytes", "spec_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert sorted(st.EXPORTS) == sorted(declared_functions())
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.spec_status_string(s).decode().startswith("SPEC_")
+    assert b"unknown" in L.spec_status_string(99)
+
+
+def test_workspace_bytes_is_pure_and_rejects_bad_shapes(L):
+    f = L.spec_tree_attn_workspace_bytes
+    assert f(8, 6, 32, 8, 128, 2054) == f(8, 6, 32, 8, 128, 2054) > 0       # split path
+    assert f(64, 16, 64, 8, 128, 4112) == 0                                # one split per request
+    for bad in [(0, 6, 32, 8, 128, 2054), (8, 0, 32, 8, 128, 2054), (8, 65, 32, 8, 128, 2054),
+                (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 96, 2054), (8, 6, 32, 8, 128, 5)]:
+        assert f(*bad) == 0, bad
+
+
+def test_mask_build_host_checks(L):
+    assert L.spec_tree_mask_build(None, 1, 6, FAKE, None, None, None) == SPEC_ERR_NULL
+    assert L.spec_tree_mask_build(FAKE, 1, 6, None, None, None, None) == SPEC_ERR_NULL
+    assert L.spec_tree_mask_build(FAKE, 0, 6, FAKE, None, None, None) == SPEC_ERR_SHAPE
+    assert L.spec_tree_mask_build(FAKE, 1, 0, FAKE, None, None, None) == SPEC_ERR_SHAPE
+    assert L.spec_tree_mask_build(FAKE, 1, 65, FAKE, None, None, None) == SPEC_ERR_SHAPE
+
+
+def test_accept_walk_host_checks(L):
+    args = [FAKE] * 4
+    outs = [FAKE] * 3
+    assert L.spec_accept_walk(None, *args[1:], 1, 6, 10, *outs, None, None) == SPEC_ERR_NULL
+    assert L.spec_accept_walk(*args, 1, 6, 10, None, FAKE, FAKE, None, None) == SPEC_ERR_NULL
+    assert L.spec_accept_walk(*args, 1, 65, 10, *outs, None, None) == SPEC_ERR_SHAPE
+    assert L.spec_accept_walk(*args, 1, 6, 0, *outs, None, None) == SPEC_ERR_SHAPE
+
+
+def test_argmax_host_checks(L):
+    assert L.spec_vocab_argmax(None, 4, 10, 10, FAKE, None) == SPEC_ERR_NULL
+    assert L.spec_vocab_argmax(FAKE, 0, 10, 10, FAKE, None) == SPEC_ERR_SHAPE
+    assert L.spec_vocab_argmax(FAKE, 4, 10, 9, FAKE, None) == SPEC_ERR_SHAPE
+    assert L.spec_vocab_argmax(FAKE, 4, 0, 10, FAKE, None) == SPEC_ERR_SHAPE
+
+
+def _attn(L, q=FAKE, qd=1, k=FAKE, v=FAKE, kvd=1, ks=None, vs=None, shape=(8, 6, 32, 8, 128, 2054),
+          out=FAKE, ws=None, wsb=0):
+    return L.spec_tree_attn_verify(q, qd, k, v, kvd, ks, vs, FAKE, FAKE, *shape, 0.088, out, None, ws,
+                                   wsb, None, None)
+
+
+def test_attention_host_checks(L):
+    assert _attn(L, q=None) == SPEC_ERR_NULL
+    assert _attn(L, out=None) == SPEC_ERR_NULL
+    assert _attn(L, qd=0, kvd=1) == SPEC_ERR_DTYPE                  # f32 q with bf16 kv
+    assert _attn(L, qd=2, kvd=2) == SPEC_ERR_DTYPE                  # fp8 q
+    assert _attn(L, qd=1, kvd=2) == SPEC_ERR_NULL                   # fp8 kv needs scales
+    assert _attn(L, shape=(8, 6, 30, 8, 128, 2054)) == SPEC_ERR_SHAPE    # Hq % Hkv
+    assert _attn(L, shape=(8, 6, 32, 8, 96, 2054)) == SPEC_ERR_SHAPE     # D
+    assert _attn(L, shape=(8, 65, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE   # N
+    assert _attn(L, shape=(8, 6, 32, 8, 128, 5)) == SPEC_ERR_SHAPE       # S_max < N
+    assert _attn(L, q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
+    assert _attn(L) == SPEC_ERR_WORKSPACE                            # split path needs scratch
+    need = L.spec_tree_attn_workspace_bytes(8, 6, 32, 8, 128, 2054)
+    assert _attn(L, ws=FAKE, wsb=need - 1) == SPEC_ERR_WORKSPACE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(st.SpecError):
+        st.tree_mask_build(torch.zeros((1, 6), dtype=torch.int32))

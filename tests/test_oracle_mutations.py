@@ -78,9 +78,9 @@ MUTANTS = {
                            lambda o: pins.check_attention_node_locality(o.attention.tree_attention)),
     "attn_tree_rows_off_by_one": ([("attention", "A[i, P + j] = True", "A[i, P + j - 1] = True")],
                                   lambda o: pins.check_attention_chain_is_causal(o.attention.tree_attention)),
-    "attn_kv_head_mod": ([("attention", "kvh = h // g", "kvh = h % Hkv")],
+    "attn_kv_head_mod": ([("attention", "for h in range(kvh * g, (kvh + 1) * g):", "for h in range(kvh, Hq, Hkv):")],
                          lambda o: pins.check_attention_chain_is_causal(o.attention.tree_attention)),
-    "attn_no_scale": ([("attention", "s = float(sm_scale) * (Q @ Kf.T)", "s = Q @ Kf.T")],
+    "attn_no_scale": ([("attention", "s = float(sm_scale) * (Q @ Kf.T)                         # [N][L]", "s = Q @ Kf.T")],
                       lambda o: pins.check_attention_chain_is_causal(o.attention.tree_attention)),
     "attn_k_for_v": ([("attention", "out = w @ Vf", "out = w @ Kf")],
                      lambda o: pins.check_attention_one_node_is_decode(o.attention.tree_attention)),

@@ -1,0 +1,191 @@
+"""spectree: speculative-decoding tree verify step on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libspectree.so`` (``include/spectree.h``).  The
+functions here only marshal arguments: every step runs in the library's HIP
+kernels, on the caller's current torch stream.  Torch is used for device
+memory and streams only.  There is no CPU fallback: if the library or a GPU
+is missing, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify",
+    "vocab_argmax", "accept_walk", "verify_step", "DERR_ROOT", "DERR_PARENT", "DERR_PREFIX",
+    "DERR_TOKEN", "library_path",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libspectree.so")
+
+SPEC_F32, SPEC_BF16, SPEC_FP8_E4M3 = 0, 1, 2
+DERR_ROOT, DERR_PARENT, DERR_PREFIX, DERR_TOKEN = 1, 2, 4, 8
+MAX_NODES = 64
+
+_DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3fn: SPEC_FP8_E4M3}
+
+EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
+           "spec_vocab_argmax", "spec_accept_walk", "spec_status_string"]
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspectree.so (built in-tree by ``build.py``) or raise."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise SpecError(f"{library_path} is missing: build it with "
+                        "`python -m tree_attention_verify_parent_amd.build`")
+    L = ctypes.CDLL(library_path)
+    c_i, c_p, c_i64, c_sz, c_f = ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.spec_tree_mask_build.argtypes = [c_p, c_i, c_i, c_p, c_p, c_p, c_p]
+    L.spec_tree_mask_build.restype = c_i
+    L.spec_tree_attn_workspace_bytes.argtypes = [c_i] * 6
+    L.spec_tree_attn_workspace_bytes.restype = c_sz
+    L.spec_tree_attn_verify.argtypes = [c_p, c_i, c_p, c_p, c_i, c_p, c_p, c_p, c_p,
+                                        c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_sz,
+                                        c_p, c_p]
+    L.spec_tree_attn_verify.restype = c_i
+    L.spec_vocab_argmax.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_p]
+    L.spec_vocab_argmax.restype = c_i
+    L.spec_accept_walk.argtypes = [c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p]
+    L.spec_accept_walk.restype = c_i
+    L.spec_status_string.argtypes = [c_i]
+    L.spec_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SpecError(lib().spec_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise SpecError("spectree takes device tensors only")
+    if not t.is_contiguous():
+        raise SpecError("spectree takes contiguous tensors only")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _err_word(err: Optional[torch.Tensor], device) -> torch.Tensor:
+    if err is not None:
+        return err
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def tree_mask_build(parents: torch.Tensor, *, anc_mask=None, depth=None, err=None, stream=None):
+    """parents int32[B][N] -> (anc_mask int64[B][N] (uint64 bit patterns),
+    depth int32[B][N], err int32[1])."""
+    B, N = parents.shape
+    dev = parents.device
+    anc_mask = torch.empty((B, N), dtype=torch.int64, device=dev) if anc_mask is None else anc_mask
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev) if depth is None else depth
+    err = _err_word(err, dev)
+    _check(lib().spec_tree_mask_build(_ptr(parents), B, N, _ptr(anc_mask), _ptr(depth), _ptr(err),
+                                      _stream(stream)))
+    return anc_mask, depth, err
+
+
+def attn_workspace_bytes(B, N, Hq, Hkv, D, S_max) -> int:
+    return int(lib().spec_tree_attn_workspace_bytes(B, N, Hq, Hkv, D, S_max))
+
+
+def tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc_mask, sm_scale, *, k_scale=None,
+                     v_scale=None, out=None, lse=None, want_lse=True, workspace=None, err=None,
+                     stream=None):
+    """Tree-masked attention.  q [B][N][Hq][D] (f32 or bf16); caches
+    [B][Hkv][S_max][D] (f32, bf16 or float8_e4m3fn); returns (out, lse, err)."""
+    B, N, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    if q.dtype not in _DTYPE or k_cache.dtype not in _DTYPE or v_cache.dtype != k_cache.dtype:
+        raise SpecError(f"unsupported dtypes q={q.dtype} kv={k_cache.dtype}/{v_cache.dtype}")
+    if tuple(k_cache.shape) != (B, Hkv, S_max, D) or tuple(v_cache.shape) != (B, Hkv, S_max, D):
+        raise SpecError("k_cache / v_cache must be [B][Hkv][S_max][D] matching q")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    ws_need = attn_workspace_bytes(B, N, Hq, Hkv, D, S_max)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, dev)
+    _check(lib().spec_tree_attn_verify(
+        _ptr(q), _DTYPE[q.dtype], _ptr(k_cache), _ptr(v_cache), _DTYPE[k_cache.dtype],
+        _ptr(k_scale), _ptr(v_scale), _ptr(prefix_lens), _ptr(anc_mask),
+        B, N, Hq, Hkv, D, S_max, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _ptr(err), _stream(stream)))
+    return out, lse, err
+
+
+def vocab_argmax(logits: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:
+    """logits float32[rows][V] (row stride may exceed V) -> int32[rows]."""
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise SpecError("logits must be a float32 [rows][V] tensor with unit column stride")
+    rows, V = logits.shape
+    out = torch.empty(rows, dtype=torch.int32, device=logits.device) if out is None else out
+    _check(lib().spec_vocab_argmax(ctypes.c_void_p(logits.data_ptr()), rows, V, logits.stride(0),
+                                   _ptr(out), _stream(stream)))
+    return out
+
+
+def accept_walk(parents, anc_mask, draft_tokens, target_argmax, V, *, accept_len=None,
+                path_nodes=None, out_tokens=None, err=None, stream=None):
+    """Returns (accept_len int32[B], path_nodes int32[B][N], out_tokens int32[B][N], err)."""
+    B, N = parents.shape
+    dev = parents.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    path_nodes = torch.empty((B, N), dtype=torch.int32, device=dev) if path_nodes is None else path_nodes
+    out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
+    err = _err_word(err, dev)
+    _check(lib().spec_accept_walk(_ptr(parents), _ptr(anc_mask), _ptr(draft_tokens), _ptr(target_argmax),
+                                  B, N, int(V), _ptr(accept_len), _ptr(path_nodes), _ptr(out_tokens),
+                                  _ptr(err), _stream(stream)))
+    return accept_len, path_nodes, out_tokens, err
+
+
+def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *,
+                k_scale=None, v_scale=None, debug=False, stream=None):
+    """One verify step on the GPU: mask -> attention -> argmax -> accept walk.
+
+    All four calls are enqueued on one stream; nothing synchronises unless
+    ``debug`` is set, in which case the device error word is read and a
+    non-zero value raises.
+    """
+    dev = q.device
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    anc, depth, _ = tree_mask_build(parents, err=err, stream=stream)
+    out, lse, _ = tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc, sm_scale, k_scale=k_scale,
+                                   v_scale=v_scale, err=err, stream=stream)
+    t = vocab_argmax(logits, stream=stream)
+    B, N = parents.shape
+    L, path, toks, _ = accept_walk(parents, anc, draft_tokens, t.view(B, N), logits.shape[1], err=err,
+                                   stream=stream)
+    res = dict(mask=anc, depth=depth, out=out, lse=lse, argmax=t, accept_len=L, path_nodes=path,
+               out_tokens=toks, err=err)
+    if debug:
+        e = int(err.item())
+        if e:
+            raise SpecError(f"device data error bits 0x{e:x}")
+    return res
