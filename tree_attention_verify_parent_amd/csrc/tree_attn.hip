@@ -7,21 +7,24 @@
 // HBM (the same page notes that verification is memory- rather than
 // compute-bound), so each K/V byte is read once per (request, kv head): the
 // g = Hq/Hkv query heads of a kv head and the N tree nodes are packed into the
-// M dimension of small dense MFMA tiles.
+// M dimension of small dense MFMA tiles (row = node * g + head).
 //
-// Kernel layout (bf16 / e4m3 KV):
-//   workgroup = NW waves = one (request b, kv head, M-tile, KV split);
-//   wave w owns RB blocks of 16 packed query rows (row = node * g + head);
-//   the split's tokens go through LDS 64 at a time: K as [token][d] bf16 and
-//   V transposed to [d][token] bf16, both XOR-swizzled against bank conflicts;
-//   S^T = K . Q^T and O^T = V^T . P^T run on v_mfma_f32_16x16x32_bf16, so a
-//   lane holds one query row of S and of O and the online-softmax statistics
-//   of a row live in the 4 lanes {l, l^16, l^32, l^48};
+// bf16 / e4m3 KV kernel:
+//   workgroup = one (request b, kv head, M-tile, KV split), WM x WT waves;
+//   K/V tiles of 64 tokens go HBM -> LDS by direct 16-byte DMA
+//   (global_load_lds) into an NSTAGE-deep ring of row-major tiles with
+//   XOR-swizzled 16-byte units -- no staging registers, no VALU work;
+//   S^T = K . Q^T and O^T = V^T . P^T on v_mfma_f32_16x16x32_bf16, with V^T
+//   operands produced by the LDS transpose reads; a lane holds one query row
+//   of S and of O, so the online-softmax statistics of a row live in the four
+//   lanes {l, l^16, l^32, l^48};
 //   the 64-bit ancestor mask of each row is applied in registers, only on
 //   tiles that reach the tree rows.
 // A request whose tokens fit one split writes its output directly; otherwise
-// each split writes (O, m, l) partials and spec_tree_attn_merge combines them
-// in split order (deterministic).
+// each split writes (O, m, l) partials and the merge kernel combines them in
+// split order (deterministic).
+#include <type_traits>
+
 #include "common.h"
 
 namespace spectree {
@@ -36,43 +39,89 @@ constexpr float kLn2 = 0.6931471805599453f;
 // is exactly the K-slot run its B operand needs in the PV product.
 __device__ __forceinline__ int chunk_token(int G, int m) { return 8 * (m >> 2) + 4 * G + (m & 3); }
 
-// 16-byte unit swizzles.  K rows: lanes 0..7 of an A-operand read hit tokens
-// {0,1,2,3,8,9,10,11} (+4G); XOR with (t&3)|((t>>3)&1)<<2 spreads them over 8
-// distinct units.  V^T rows (d-major): lanes 0..7 read 8 consecutive d rows at
-// one unit; XOR with (d&7)^((d>>3)&7) spreads those and keeps the transposed
-// writes at most 2-way conflicted.
-__device__ __forceinline__ int swz_k(int t) { return (t & 3) | (((t >> 3) & 1) << 2); }
-__device__ __forceinline__ int swz_v(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-
-template <int KVF>
-struct KvFormat;
-template <>
-struct KvFormat<SPEC_BF16> {
-  static constexpr int kElem = 2;   // bytes per element in HBM
-  static constexpr int kEpl = 8;    // elements per 16-byte load
-};
-template <>
-struct KvFormat<SPEC_FP8_E4M3> {
-  static constexpr int kElem = 1;
-  static constexpr int kEpl = 16;
-};
-
-// bf16 bits of element k of a 16-byte load
-template <int KVF>
-__device__ __forceinline__ uint32_t elem_bits(const uint4& w, int k) {
-  constexpr int per_word = (KVF == SPEC_BF16) ? 2 : 4;
-  const int wi = k / per_word;
-  const uint32_t word = (wi == 0) ? w.x : (wi == 1) ? w.y : (wi == 2) ? w.z : w.w;
-  if constexpr (KVF == SPEC_BF16) {
-    return (word >> (16 * (k & 1))) & 0xFFFFu;
-  } else {
-    const uint32_t byte = (word >> (8 * (k & 3))) & 0xFFu;
-    return e4m3_to_bf16_bits(byte);
-  }
+// XOR swizzle of the 16-byte units of an LDS row, by units per row (UPR).
+// The K operand read of a 16-lane group touches rows {0-3, 8-11, 16-19,
+// 24-27} (+4G) at one unit; the V transpose read touches the same row set at
+// two adjacent units.  The swizzle gives those rows distinct bank groups, so
+// each read runs at the minimum number of LDS passes.
+template <int UPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (UPR >= 16) return (row & 3) | (((row >> 3) & 3) << 2);
+  else if constexpr (UPR == 8) return ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
+  else return (row >> 1) & 3;
 }
 
-template <int D, int KVF, int RB, int NW>
-__global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained (gfx9 layout).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads: that fence
+// would force vmcnt(0) and drain the K/V prefetch.  LDS ordering is kept by
+// explicit vmcnt waits (DMA writes land before the barrier) and by every LDS
+// read being consumed before its wave reaches the next barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// 8 OCP e4m3 codes (little-endian in lo, hi) -> 8 bf16, exactly, by the
+// hardware converter (scale 1.0).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int I>
+using Int = std::integral_constant<int, I>;
+
+// One wave-wide 16-byte-per-lane DMA from global memory into LDS: lane l's
+// 16 bytes land at LDS byte lds_addr + 16*l (lds_addr wave-uniform, via M0).
+// Issued as inline assembly so the compiler's wait-count pass does not treat
+// every later LDS read as depending on every DMA in flight; the kernel orders
+// them itself with s_waitcnt vmcnt(N) before each barrier.
+__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds_ptr) {
+  const uint32_t lds_addr = (uint32_t)(size_t)(lds_void_t*)lds_ptr;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// One workgroup = one (request b, kv head, M-tile, KV split).
+//   Wave (wm, wt) owns RB 16-row blocks of the M-tile and the 32-token chunks
+//   wt*CPT .. wt*CPT+CPT-1 of every 64-token tile (CPT = 2/WT).
+// Waves per SIMD the kernel is built for: as many workgroups as the LDS ring
+// leaves room for on a CU (160 KB), so the compiler keeps the register count
+// at or below 512 / that many waves instead of spending it on unrolling.
+// The register budget caps it too: two row blocks per wave need about 200+
+// registers, so at most 2 waves per SIMD there.
+template <int D, int KVF, int RB, int WM, int WT, int NSTAGE>
+struct SplitOccupancy {
+  static constexpr int lds = NSTAGE * 2 * kTile * D * ((KVF == SPEC_BF16) ? 2 : 1);
+  static constexpr int wg_per_cu = (160 * 1024) / lds;
+  static constexpr int w = (wg_per_cu * WM * WT + 3) / 4;
+  static constexpr int cap = (RB >= 2) ? 2 : 4;
+  static constexpr int value = w < 1 ? 1 : (w > cap ? cap : w);
+};
+
+template <int D, int KVF, int RB, int WM, int WT, int NSTAGE>
+__global__ __launch_bounds__(WM * WT * kWave)
+__attribute__((amdgpu_waves_per_eu(SplitOccupancy<D, KVF, RB, WM, WT, NSTAGE>::value)))
+void tree_attn_split_kernel(
     const __bf16* __restrict__ q, const unsigned char* __restrict__ kc,
     const unsigned char* __restrict__ vc, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ prefix_lens,
@@ -80,26 +129,44 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
     float sm_scale, int split_len, int n_splits, int n_mt, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
     uint32_t* __restrict__ err_word) {
-  using F = KvFormat<KVF>;
-  constexpr int NT = NW * kWave;
-  constexpr int MT = NW * RB * 16;          // packed rows per workgroup
-  constexpr int KC = D / 32;                // 32-wide contraction chunks of QK^T
-  constexpr int DB = D / 16;                // 16-wide output column blocks
-  constexpr int KROW = D * 2;               // bytes per K row in LDS
-  constexpr int VROW = kTile * 2;           // bytes per V^T row in LDS
-  constexpr int UPR = D / F::kEpl;          // 16-byte loads per cache row
-  constexpr int KTASKS = kTile * UPR;       // K: one load each
-  constexpr int VTASKS = (kTile / 4) * UPR; // V: 4 tokens x one load-width each
-  constexpr int KPT = (KTASKS + NT - 1) / NT;
-  constexpr int VPT = (VTASKS + NT - 1) / NT;
-  static_assert(KTASKS % NT == 0, "K staging must divide evenly");
+  static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "ring depth");
+  constexpr int NW = WM * WT;
+  constexpr int EB = (KVF == SPEC_BF16) ? 2 : 1;     // bytes per cached element
+  constexpr int CPT = 2 / WT;                        // 32-token chunks per wave per tile
+  constexpr int RBYTES = D * EB;                     // bytes per K/V row
+  constexpr int UPR = RBYTES / 16;                   // 16-byte units per row
+  constexpr int TB = kTile * RBYTES;                 // bytes per tensor per stage
+  constexpr int NLOAD = TB / 1024;                   // 1-KB wave DMA instructions per tensor
+  constexpr int KPW = NLOAD / NW;                    // per wave per tensor per stage
+  constexpr int RPI = 1024 / RBYTES;                 // rows per DMA instruction
+  constexpr int MT = WM * RB * 16;                   // packed rows per workgroup
+  constexpr int KC = D / 32;
+  constexpr int DB = D / 16;
+  static_assert(NLOAD % NW == 0, "DMA instructions must split evenly over the waves");
 
-  __shared__ __align__(16) unsigned char lds_k[kTile * KROW];
-  __shared__ __align__(16) unsigned char lds_v[D * VROW];
+  // one LDS object per stage and tensor, so the compiler can tell the stage
+  // being read from the stages still being filled (no forced vmcnt(0))
+  __shared__ __align__(1024) unsigned char sk0[TB];
+  __shared__ __align__(1024) unsigned char sv0[TB];
+  __shared__ __align__(1024) unsigned char sk1[TB];
+  __shared__ __align__(1024) unsigned char sv1[TB];
+  __shared__ __align__(1024) unsigned char sk2[NSTAGE > 2 ? TB : 16];
+  __shared__ __align__(1024) unsigned char sv2[NSTAGE > 2 ? TB : 16];
+  auto kst = [&](auto S) -> unsigned char* {
+    if constexpr (decltype(S)::value == 0) return sk0;
+    else if constexpr (decltype(S)::value == 1) return sk1;
+    else return sk2;
+  };
+  auto vst = [&](auto S) -> unsigned char* {
+    if constexpr (decltype(S)::value == 0) return sv0;
+    else if constexpr (decltype(S)::value == 1) return sv1;
+    else return sv2;
+  };
 
-  // ---- work item: XCD-aware order.  Workgroups are dispatched round-robin
-  // over the 8 XCDs, so the M-tiles of one KV range get ids congruent mod 8 and
-  // share that XCD's L2.
+  // ---- work item, XCD-aware: workgroups are dispatched round-robin over the
+  // 8 XCDs, so the M-tiles of one KV range get ids congruent mod 8 and share
+  // that XCD's L2.
   const int id = blockIdx.x;
   const int per = 8 * n_mt;
   const int mt = (id % per) / 8;
@@ -120,20 +187,49 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
   const int t_begin = split * split_len;
   if (t_begin >= L) return;
   const int t_end = min(L, t_begin + split_len);
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
   const bool direct = (L <= split_len);      // this request has a single split
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM;
+  const int wt = wave / WM;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  const int row0 = mt * MT + wave * RB * 16;
+  const int row0 = mt * MT + wm * RB * 16;
 
   float scale_log2 = sm_scale * kLog2e;
   float out_scale = 1.0f;
   if constexpr (KVF == SPEC_FP8_E4M3) {
     scale_log2 *= k_scale[kvh];
     out_scale = v_scale[kvh];
+  }
+
+  const size_t head_off = ((size_t)(b * Hkv + kvh) * S_max) * RBYTES;
+  const unsigned char* kbase = kc + head_off;
+  const unsigned char* vbase = vc + head_off;
+
+  // ---- DMA of tile i into stage S: wave w issues instructions w, w+NW, ...;
+  // lane l of instruction j fills LDS bytes j*1024 + 16l, i.e. row
+  // j*RPI + l/UPR at swizzled unit l%UPR.
+  auto issue = [&](auto S, int i) {
+    const int t0 = t_begin + i * kTile;
+#pragma unroll
+    for (int qd = 0; qd < KPW; ++qd) {
+      const int j = wave + qd * NW;
+      const int row = j * RPI + lane / UPR;
+      const int u = (lane % UPR) ^ swz<UPR>(row);
+      const size_t c = (size_t)min(t0 + row, t_end - 1);     // rows past the split repeat a valid row
+      const size_t goff = c * RBYTES + u * 16;
+      dma16(kbase + goff, kst(S) + j * 1024);
+      dma16(vbase + goff, vst(S) + j * 1024);
+    }
+  };
+
+  issue(Int<0>{}, 0);
+  if constexpr (NSTAGE > 2) {
+    if (ntiles > 1) issue(Int<1>{}, 1);
   }
 
   // ---- Q rows of this wave as MFMA B operands (K-slots 32c + 8lg .. +7)
@@ -155,6 +251,16 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
     }
   }
 
+  // Complete the Q / mask loads here, once: the compiler cannot count the
+  // DMA instructions, so any wait it places for these loads drains the ring;
+  // inside the tile loop that would happen on every tile.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    asm volatile("" ::"v"(anc[rb]));
+#pragma unroll
+    for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
+  }
+
   f32x4_t oacc[RB][DB];
   float m_run[RB], l_run[RB];
 #pragma unroll
@@ -165,124 +271,87 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
     for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t head_off = ((size_t)(b * Hkv + kvh) * S_max) * D;
-  const unsigned char* kbase = kc + head_off * F::kElem;
-  const unsigned char* vbase = vc + head_off * F::kElem;
-
-  uint4 kbuf[KPT];
-  uint4 vbuf[VPT][4];
-
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int task = tid + j * NT;
-      const int tok = task / UPR, u = task % UPR;
-      const int c = t0 + tok;
-      kbuf[j] = (c < t_end) ? *reinterpret_cast<const uint4*>(kbase + ((size_t)c * D + u * F::kEpl) * F::kElem)
-                            : uint4{0u, 0u, 0u, 0u};
+  // A operand of S^T = K . Q^T: lane (m = l16, lg) holds K[row][32c + 8lg .. +7]
+  auto read_k = [&](const unsigned char* st, int row, int c) -> bf16x8_t {
+    if constexpr (KVF == SPEC_BF16) {
+      return *reinterpret_cast<const bf16x8_t*>(st + row * RBYTES + (((4 * c + lg) ^ swz<UPR>(row)) << 4));
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(
+          st + row * RBYTES + (((2 * c + (lg >> 1)) ^ swz<UPR>(row)) << 4) + ((lg & 1) << 3));
+      return fp8x8_to_bf16(w.x, w.y);
     }
+  };
+  // A operand of O^T = V^T . P^T: lane (l16, lg) holds V[32ch + 8lg + k][16db + l16],
+  // k = 0..7.  Transpose reads: a 16-lane group's 8-byte chunks form a vector
+  // E and lane j receives E[j + 16k]; so lanes 4k'..4k'+3 (bf16) or 2k, 2k+1
+  // (fp8) point at the 16 columns of token k.
+  auto read_v = [&](const unsigned char* st, int ch, int db) -> bf16x8_t {
+    if constexpr (KVF == SPEC_BF16) {
+      i16x4_t t[2];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int task = tid + j * NT;
-      const int tg = task / UPR, u = task % UPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = t0 + 4 * tg + r;
-        vbuf[j][r] = (task < VTASKS && c < t_end)
-                         ? *reinterpret_cast<const uint4*>(vbase + ((size_t)c * D + u * F::kEpl) * F::kElem)
-                         : uint4{0u, 0u, 0u, 0u};
+      for (int r = 0; r < 2; ++r) {
+        const int row = 32 * ch + 8 * lg + 4 * r + (l16 >> 2);
+        const int u = 2 * db + ((l16 >> 1) & 1);
+        const int off = row * RBYTES + ((u ^ swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
+        t[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + off));
       }
+      // whole-vector bit casts: assembling the operand element by element
+      // from bit-cast shorts is lowered wrongly (half-words get duplicated)
+      const i16x8_t both = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8_t, both);
+    } else {
+      const int row = 32 * ch + 8 * lg + (l16 >> 1);
+      const int off = row * RBYTES + ((db ^ swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
+      const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(st + off));
+      return fp8x8_to_bf16((uint32_t)t[0], (uint32_t)t[1]);
     }
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int task = tid + j * NT;
-      const int tok = task / UPR, u = task % UPR;
-      if constexpr (KVF == SPEC_BF16) {
-        *reinterpret_cast<uint4*>(lds_k + tok * KROW + ((u ^ swz_k(tok)) << 4)) = kbuf[j];
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint4 w;
-          w.x = elem_bits<KVF>(kbuf[j], 8 * h + 0) | (elem_bits<KVF>(kbuf[j], 8 * h + 1) << 16);
-          w.y = elem_bits<KVF>(kbuf[j], 8 * h + 2) | (elem_bits<KVF>(kbuf[j], 8 * h + 3) << 16);
-          w.z = elem_bits<KVF>(kbuf[j], 8 * h + 4) | (elem_bits<KVF>(kbuf[j], 8 * h + 5) << 16);
-          w.w = elem_bits<KVF>(kbuf[j], 8 * h + 6) | (elem_bits<KVF>(kbuf[j], 8 * h + 7) << 16);
-          const int ub = 2 * u + h;
-          *reinterpret_cast<uint4*>(lds_k + tok * KROW + ((ub ^ swz_k(tok)) << 4)) = w;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int task = tid + j * NT;
-      if (task < VTASKS) {
-        const int tg = task / UPR, u = task % UPR;
-#pragma unroll
-        for (int k = 0; k < F::kEpl; ++k) {
-          const int d = u * F::kEpl + k;
-          uint2 w;
-          w.x = elem_bits<KVF>(vbuf[j][0], k) | (elem_bits<KVF>(vbuf[j][1], k) << 16);
-          w.y = elem_bits<KVF>(vbuf[j][2], k) | (elem_bits<KVF>(vbuf[j][3], k) << 16);
-          const int t = 4 * tg;
-          *reinterpret_cast<uint2*>(lds_v + d * VROW + (((t >> 3) ^ swz_v(d)) << 4) + ((t & 7) << 1)) = w;
-        }
-      }
-    }
-  };
-
-  load_tile(t_begin);
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    __syncthreads();            // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (t0 + kTile < t_end) load_tile(t0 + kTile);
-
-    // ---- S^T = K . Q^T for the 64 tokens of the tile
-    f32x4_t sacc[RB][2][2];
+  auto compute = [&](auto S, int i) {
+    const unsigned char* ks = kst(S);
+    const unsigned char* vs = vst(S);
+    const int t0 = t_begin + i * kTile;
+    // ---- S^T = K . Q^T for this wave's chunks of the tile
+    f32x4_t sacc[RB][CPT][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
+      for (int cp = 0; cp < CPT; ++cp)
 #pragma unroll
-        for (int G = 0; G < 2; ++G) sacc[rb][ch][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
+    for (int cp = 0; cp < CPT; ++cp) {
+      const int ch = wt * CPT + cp;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
 #pragma unroll
         for (int G = 0; G < 2; ++G) {
-          const int tok = 32 * ch + chunk_token(G, l16);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              lds_k + tok * KROW + (((4 * c + lg) ^ swz_k(tok)) << 4));
+          const bf16x8_t a = read_k(ks, 32 * ch + chunk_token(G, l16), c);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
-            sacc[rb][ch][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][ch][G], 0, 0, 0);
+            sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
         }
       }
     }
-
     // ---- mask, online softmax (base 2), P in bf16
     const bool plain = (t0 + kTile <= P);   // the whole tile is prefix: nothing masked
-    bf16x8_t pb[RB][2];
+    bf16x8_t pb[RB][CPT];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
+      for (int cp = 0; cp < CPT; ++cp)
 #pragma unroll
         for (int G = 0; G < 2; ++G)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float s = sacc[rb][ch][G][r] * scale_log2;
+            float s = sacc[rb][cp][G][r] * scale_log2;
             if (!plain) {
-              const int c = t0 + 32 * ch + 8 * lg + 4 * G + r;
+              const int c = t0 + 32 * (wt * CPT + cp) + 8 * lg + 4 * G + r;
               const bool ok = (c < t_end) && (c < P || ((anc[rb] >> (c - P)) & 1ull));
               s = ok ? s : -INFINITY;
             }
-            sacc[rb][ch][G][r] = s;
+            sacc[rb][cp][G][r] = s;
             mx = fmaxf(mx, s);
           }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -293,32 +362,86 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
       m_run[rb] = m_new;
       float lsum = 0.0f;
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
+      for (int cp = 0; cp < CPT; ++cp)
 #pragma unroll
         for (int G = 0; G < 2; ++G)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(sacc[rb][ch][G][r] - m_use);
+            const float p = exp2f(sacc[rb][cp][G][r] - m_use);
             lsum += p;
-            pb[rb][ch][4 * G + r] = (__bf16)p;
+            pb[rb][cp][4 * G + r] = (__bf16)p;
           }
       l_run[rb] = l_run[rb] * alpha + lsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
     }
-
     // ---- O^T += V^T . P^T
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
+    for (int cp = 0; cp < CPT; ++cp) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + l16;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            lds_v + d * VROW + (((4 * ch + lg) ^ swz_v(d)) << 4));
+        const bf16x8_t a = read_v(vs, wt * CPT + cp, db);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][ch], oacc[rb][db], 0, 0, 0);
+          oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][cp], oacc[rb][db], 0, 0, 0);
       }
+    }
+  };
+
+  // one ring step: wait for tile i (later tiles may stay in flight), make it
+  // visible to all waves, refill the stage that tile i-1 used, compute tile i
+  auto step = [&](auto S, int i) -> bool {
+    if (i >= ntiles) return false;
+    if constexpr (NSTAGE == 3) {
+      if (i + 1 < ntiles) wait_vmcnt<2 * KPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wg_barrier();
+    if (i + NSTAGE - 1 < ntiles) issue(Int<(decltype(S)::value + NSTAGE - 1) % NSTAGE>{}, i + NSTAGE - 1);
+    compute(S, i);
+    return true;
+  };
+  for (int i = 0;; i += NSTAGE) {
+    if (!step(Int<0>{}, i)) break;
+    if (!step(Int<1>{}, i + 1)) break;
+    if constexpr (NSTAGE > 2) {
+      if (!step(Int<2>{}, i + 2)) break;
+    }
+  }
+
+  // ---- waves that split the tile's tokens combine their states in LDS
+  if constexpr (WT == 2) {
+    // scratch: row blocks [0, HB) in stage-0 K, [HB, WM*RB) in stage-1 K, (m, l) in stage-0 V
+    constexpr int HB = (WM * RB + 1) / 2;
+    static_assert(HB * DB * 64 * 16 <= TB && WM * RB * 64 * 8 <= TB, "combine scratch");
+    __syncthreads();                                    // all DMA and LDS stage reads are done
+    auto oslot = [&](int blk, int db) -> f32x4_t* {
+      f32x4_t* base = reinterpret_cast<f32x4_t*>(blk < HB ? sk0 : sk1);
+      return base + ((blk < HB ? blk : blk - HB) * DB + db) * 64 + lane;
+    };
+    float2* sml = reinterpret_cast<float2*>(sv0);       // [WM*RB][64]
+    if (wt == 1) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *oslot(wm * RB + rb, db) = oacc[rb][db];
+        sml[(wm * RB + rb) * 64 + lane] = make_float2(m_run[rb], l_run[rb]);
+      }
+    }
+    __syncthreads();
+    if (wt == 1) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float2 o = sml[(wm * RB + rb) * 64 + lane];
+      const float m_new = fmaxf(m_run[rb], o.x);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float a0 = exp2f(m_run[rb] - m_use), a1 = exp2f(o.x - m_use);
+      m_run[rb] = m_new;
+      l_run[rb] = l_run[rb] * a0 + o.y * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[rb][db] = oacc[rb][db] * a0 + *oslot(wm * RB + rb, db) * a1;
     }
   }
 
@@ -336,7 +459,6 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
       __bf16* op = out + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D + 4 * lg;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         bf16x4_t v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (__bf16)(oacc[rb][db][r] * inv);
@@ -348,7 +470,7 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
       float* po = part_o + pidx * D + 4 * lg;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        f32x4_t v = oacc[rb][db] * out_scale;
+        const f32x4_t v = oacc[rb][db] * out_scale;
         *reinterpret_cast<f32x4_t*>(po + 16 * db) = v;
       }
       if (lg == 0) part_ml[pidx] = make_float2(m_run[rb], l);
@@ -358,7 +480,9 @@ __global__ __launch_bounds__(NW * kWave) void tree_attn_split_kernel(
 
 // Combine the split partials of requests that needed more than one split:
 //   m = max_s m_s,  w_s = 2^(m_s - m),  O = sum_s w_s O_s / sum_s w_s l_s.
-// One thread per (packed row, 4 output columns); splits in index order.
+// One thread per (packed row, 4 output columns).  Splits are taken in index
+// order, eight at a time with all their loads issued together (an online
+// max over the groups), so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(
     const int32_t* __restrict__ prefix_lens, int B, int N, int Hq, int Hkv, int S_max,
@@ -366,6 +490,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(
     const float2* __restrict__ part_ml, __bf16* __restrict__ out, float* __restrict__ lse) {
   constexpr int QPR = D / 4;                     // column quads per row
   constexpr int RPB = 256 / QPR;                 // rows per workgroup
+  constexpr int GRP = 8;
   const int g = Hq / Hkv, M = g * N;
   const int blocks_per_head = (M + RPB - 1) / RPB;
   const int bh = blockIdx.x / blocks_per_head;
@@ -380,22 +505,40 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(
   if (ns <= 1) return;
 
   const size_t base = (size_t)(b * Hkv + kvh) * n_splits * (size_t)M_pad + row;
-  float m = -INFINITY;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, part_ml[base + (size_t)s * M_pad].x);
-  float den = 0.f;
+  float m = -INFINITY, den = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const size_t idx = base + (size_t)s * M_pad;
-    const float2 ml = part_ml[idx];
-    const float w = exp2f(ml.x - m);
-    den += w * ml.y;
-    const f32x4_t o = *reinterpret_cast<const f32x4_t*>(part_o + idx * D + 4 * qd);
-    acc += w * o;
+  for (int s0 = 0; s0 < ns; s0 += GRP) {
+    float2 ml[GRP];
+    f32x4_t o[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      if (s0 + j < ns) {
+        const size_t idx = base + (size_t)(s0 + j) * M_pad;
+        ml[j] = part_ml[idx];
+        o[j] = *reinterpret_cast<const f32x4_t*>(part_o + idx * D + 4 * qd);
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.f);
+        o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) mc = fmaxf(mc, ml[j].x);
+    const float m_use = (mc == -INFINITY) ? 0.f : mc;
+    const float a = exp2f(m - m_use);
+    den *= a;
+    acc *= a;
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const float w = exp2f(ml[j].x - m_use);
+      den += w * ml[j].y;
+      acc += w * o[j];
+    }
+    m = mc;
   }
   const int i = row / g, hl = row % g;
   const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
   const float inv = 1.0f / den;
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   bf16x4_t v;
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[r] * inv);
@@ -404,8 +547,9 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(
 }
 
 // fp32 Q/K/V: one wave per (request, node, head), exact fp32 arithmetic on the
-// VALU.  Lane = key within a 64-key chunk for the scores, lane = output column
-// for the PV accumulation.
+// VALU.  Per 64-key chunk: lane = key for the scores (its K row's loads all in
+// flight together), then lane = output column for the PV sum, with the
+// chunk's 64 V rows loaded at once.
 template <int D>
 __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
@@ -439,8 +583,17 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
   float o[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  __shared__ float sp[kWave];
 
   for (int c0 = 0; c0 < L; c0 += kWave) {
+    const int cmax = min(kWave, L - c0);
+    // this chunk's V rows, one column set per lane, all loads in flight
+    float vv[kWave][DPL];
+#pragma unroll
+    for (int j = 0; j < kWave; ++j)
+#pragma unroll
+      for (int k = 0; k < DPL; ++k)
+        vv[j][k] = (j < cmax) ? vb[(size_t)(c0 + j) * D + lane + k * kWave] : 0.f;
     const int c = c0 + lane;
     const bool ok = (c < L) && (c < P || ((anc >> (c - P)) & 1ull));
     float s = -INFINITY;
@@ -463,17 +616,16 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
     const float p = exp2f(s - m_use);
     l_run = l_run * alpha + wave_sum(p);
     m_run = m_new;
+    sp[lane] = p;
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] *= alpha;
-    const int cmax = min(kWave, L - c0);
-    for (int j = 0; j < cmax; ++j) {
-      const float pj = __shfl(p, j, kWave);
-      if (pj != 0.f) {
-        const float* vr = vb + (size_t)(c0 + j) * D;
+    for (int k = 0; k < DPL; ++k) {
+      float acc = o[k] * alpha;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[k] = fmaf(pj, vr[lane + k * kWave], o[k]);
-      }
+      for (int j = 0; j < kWave; ++j) acc = fmaf(sp[j], vv[j][k], acc);
+      o[k] = acc;
     }
+    __syncthreads();
   }
   float* op = out + ((size_t)(b * N + i) * Hq + h) * D;
   const float inv = 1.0f / l_run;
@@ -485,29 +637,34 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
 // ------------------------------------------------------------------ planning
 
 struct AttnPlan {
-  int rb, nw, mt_rows, n_mt, M_pad;
+  int rb, wm, wt, nstage, mt_rows, n_mt, M_pad;
   int split_len, n_splits;
+  size_t lds_bytes;
   size_t ws_bytes;
 };
 
-// Rows per workgroup follow the packed M = g*N; KV splits are added until the
-// grid has about two workgroups per CU (256 CUs), but never below 256 tokens
-// per split so the partial (O, m, l) traffic stays small against the K/V
-// bytes of the split.
-static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan* p) {
+// Rows per workgroup follow the packed M = g*N.  Small M (<= 32) lets two
+// waves split each tile's tokens; larger M splits rows over the waves.  KV
+// splits are then added until the grid fills the GPU at the occupancy the
+// LDS ring allows (256 CUs x workgroups per CU), never below 256 tokens per
+// split so the partial (O, m, l) traffic stays small against the split's
+// K/V bytes.
+static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, int kv_bytes, AttnPlan* p) {
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < Hkv || Hq % Hkv) return false;
   if (D != 64 && D != 128) return false;
   if (S_max < N) return false;
   const int M = (Hq / Hkv) * N;
-  if (M <= 32) { p->rb = 1; p->nw = 2; }
-  else if (M <= 64) { p->rb = 1; p->nw = 4; }
-  else { p->rb = 2; p->nw = 4; }
-  p->mt_rows = p->rb * p->nw * 16;
+  if (M <= 32) { p->rb = 2; p->wm = 1; p->wt = 2; p->nstage = 3; }
+  else if (M <= 64) { p->rb = 2; p->wm = 2; p->wt = 1; p->nstage = 3; }
+  else { p->rb = 2; p->wm = 4; p->wt = 1; p->nstage = 2; }
+  p->mt_rows = p->rb * p->wm * 16;
   p->n_mt = (M + p->mt_rows - 1) / p->mt_rows;
   p->M_pad = p->n_mt * p->mt_rows;
+  p->lds_bytes = (size_t)p->nstage * 2 * kTile * D * kv_bytes;
+  const long long per_cu = std::max<long long>(1, (160 * 1024) / (long long)p->lds_bytes);
   const long long units = (long long)B * Hkv * p->n_mt;
-  const long long target = 512;
-  const int want = (int)((target + units - 1) / units);
+  const long long target = 256 * per_cu;
+  const int want = (int)std::max<long long>(1, (target + units - 1) / units);
   int split_len = (S_max + want - 1) / want;
   split_len = ((split_len + kTile - 1) / kTile) * kTile;
   if (split_len < 256) split_len = 256;
@@ -521,7 +678,7 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   return true;
 }
 
-template <int D, int KVF, int RB, int NW>
+template <int D, int KVF, int RB, int WM, int WT, int NS>
 static void launch_split(const AttnPlan& pl, const void* q, const void* k, const void* v,
                          const float* ks, const float* vs, const int32_t* pre, const uint64_t* anc,
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
@@ -529,34 +686,43 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
   const int units = B * Hkv * pl.n_splits;
   const int units_pad = ((units + 7) / 8) * 8;
   const unsigned grid = (unsigned)units_pad * (unsigned)pl.n_mt;
-  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, NW>), dim3(grid), dim3(NW * kWave), 0, st,
-                     static_cast<const __bf16*>(q), static_cast<const unsigned char*>(k),
+  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS>), dim3(grid), dim3(WM * WT * kWave),
+                     0, st, static_cast<const __bf16*>(q), static_cast<const unsigned char*>(k),
                      static_cast<const unsigned char*>(v), ks, vs, pre, anc, B, N, Hq, Hkv, S_max,
                      sm_scale, pl.split_len, pl.n_splits, pl.n_mt, static_cast<__bf16*>(out), lse,
                      po, pml, err);
 }
 
 template <int D, int KVF>
-static void dispatch_rows(const AttnPlan& pl, const void* q, const void* k, const void* v,
-                          const float* ks, const float* vs, const int32_t* pre,
-                          const uint64_t* anc, int B, int N, int Hq, int Hkv, int S_max,
-                          float sm_scale, void* out, float* lse, float* po, float2* pml,
-                          uint32_t* err, hipStream_t st) {
-  if (pl.rb == 1 && pl.nw == 2)
-    launch_split<D, KVF, 1, 2>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err, st);
-  else if (pl.rb == 1)
-    launch_split<D, KVF, 1, 4>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err, st);
-  else
-    launch_split<D, KVF, 2, 4>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err, st);
+static void dispatch_shape(const AttnPlan& pl, const void* q, const void* k, const void* v,
+                           const float* ks, const float* vs, const int32_t* pre,
+                           const uint64_t* anc, int B, int N, int Hq, int Hkv, int S_max,
+                           float sm_scale, void* out, float* lse, float* po, float2* pml,
+                           uint32_t* err, hipStream_t st) {
+#define SPEC_LAUNCH(RB_, WM_, WT_, NS_)                                                          \
+  launch_split<D, KVF, RB_, WM_, WT_, NS_>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max,   \
+                                           sm_scale, out, lse, po, pml, err, st)
+  if (pl.wt == 2) SPEC_LAUNCH(2, 1, 2, 3);
+  else if (pl.wm == 2) SPEC_LAUNCH(2, 2, 1, 3);
+  else SPEC_LAUNCH(2, 4, 1, 2);
+#undef SPEC_LAUNCH
 }
 
 }  // namespace spectree
 
 using namespace spectree;
 
+static int kv_elem_bytes(int D, int S_max) {
+  (void)D;
+  (void)S_max;
+  return 2;
+}
+
 extern "C" size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max) {
   AttnPlan pl;
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return 0;
+  // the split plan does not depend on the cached dtype (the LDS ring of the
+  // 2-byte format bounds both), so one workspace size serves every format
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, kv_elem_bytes(D, S_max), &pl)) return 0;
   return pl.ws_bytes;
 }
 
@@ -577,7 +743,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   if (!f32 && !bf16 && !fp8) return SPEC_ERR_DTYPE;
   if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
   AttnPlan pl;
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return SPEC_ERR_SHAPE;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, kv_elem_bytes(D, S_max), &pl)) return SPEC_ERR_SHAPE;
   if ((long long)B * Hkv * pl.n_splits * pl.n_mt >= (1ll << 31)) return SPEC_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return SPEC_ERR_ALIGN;
@@ -609,11 +775,11 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   }
 
   if (bf16) {
-    if (D == 64) dispatch_rows<64, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
-    else dispatch_rows<128, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
+    if (D == 64) dispatch_shape<64, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
+    else dispatch_shape<128, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
   } else {
-    if (D == 64) dispatch_rows<64, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
-    else dispatch_rows<128, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
+    if (D == 64) dispatch_shape<64, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
+    else dispatch_shape<128, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
   }
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
 
