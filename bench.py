@@ -24,7 +24,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -44,18 +43,38 @@ DEFAULT_WORKLOAD = "chain6_b8_h32x8_d128_p2048_bf16"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=5000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="workload name or index 0-4")
     ap.add_argument("--no-graph", action="store_true", help="launch the four calls eagerly each step")
-    ap.add_argument("--overlap", action="store_true",
-                    help="run the argmax on a second stream, concurrent with the attention")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="run argmax and accept walk on a second stream, concurrent with mask build "
+                         "and attention (default: one stream)")
+    ap.add_argument("--steps-per-graph", type=int, default=25,
+                    help="verify steps captured in one HIP graph (amortises the graph launch)")
+    ap.add_argument("--order", default="mask,attn,argmax,walk",
+                    help="order of the four calls within a step on one stream")
     ap.add_argument("--replica-bytes", type=float, default=1.0e9,
                     help="total bytes of input replicas to rotate through (defeats the MALL)")
     ap.add_argument("--attn-calls", type=int, default=200, help="calls in the attention timing graph")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0,
+                    help="only run a plain float32 elementwise copy that reads and writes this many "
+                         "bytes (5 launches) and exit: the reference point that scales the HBM byte "
+                         "counters of a rocprofv3 --pmc pass")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes):
+    import torch
+    n = int(nbytes) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
 
 
 def workload(name):
@@ -84,12 +103,8 @@ def algorithmic_bytes(w, prefix_lens):
 
 
 def kernel_source_sha():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "tree_attention_verify_parent_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+    from tree_attention_verify_parent_amd.rocprof_summary import source_sha
+    return source_sha(ROOT)
 
 
 def measured_traffic(wname):
@@ -154,6 +169,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import numpy as np
     import torch
 
@@ -199,27 +218,44 @@ def main():
     toks = torch.empty((B, N), dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     ws_bytes = st.attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, w.S_max)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    side = torch.cuda.Stream(device=dev) if args.overlap else None
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # zeroed once, reused
+    side = torch.cuda.Stream(device=dev) if args.two_streams else None
+    ev_mask = torch.cuda.Event()
 
     def attention(r):
         st.tree_attn_verify(qs[r], kcs[r], vcs[r], prefix, anc, x["sm_scale"], k_scale=ks, v_scale=vs,
                             out=out, lse=lse, workspace=ws, err=err)
 
+    order = args.order.split(",")
+    assert sorted(order) == ["argmax", "attn", "mask", "walk"] and order.index("mask") < order.index("attn") \
+        and order.index("mask") < order.index("walk") and order.index("argmax") < order.index("walk"), order
+
     def step(r):
+        if side is None:
+            for name in order:
+                if name == "mask":
+                    st.tree_mask_build(parents, anc_mask=anc, depth=depth, err=err)
+                elif name == "attn":
+                    attention(r)
+                elif name == "argmax":
+                    st.vocab_argmax(lgs[r], out=amax)
+                else:
+                    st.accept_walk(parents, anc, draft, amax.view(B, N), w.V, accept_len=acc_len,
+                                   path_nodes=path, out_tokens=toks, err=err)
+            return
+        # two streams: mask -> attention on the main stream; argmax -> accept
+        # walk (after the mask) on the side stream; joined at the end
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
         st.tree_mask_build(parents, anc_mask=anc, depth=depth, err=err)
-        if side is not None:
-            main = torch.cuda.current_stream()
-            side.wait_stream(main)
-            with torch.cuda.stream(side):
-                st.vocab_argmax(lgs[r], out=amax)
-            attention(r)
-            main.wait_stream(side)
-        else:
-            attention(r)
+        ev_mask.record(main)
+        with torch.cuda.stream(side):
             st.vocab_argmax(lgs[r], out=amax)
-        st.accept_walk(parents, anc, draft, amax.view(B, N), w.V, accept_len=acc_len, path_nodes=path,
-                       out_tokens=toks, err=err)
+            side.wait_event(ev_mask)
+            st.accept_walk(parents, anc, draft, amax.view(B, N), w.V, accept_len=acc_len, path_nodes=path,
+                           out_tokens=toks, err=err)
+        attention(r)
+        main.wait_stream(side)
 
     # eager warm-up (loads kernels), then correctness sanity of the result
     for r in range(R):
@@ -228,21 +264,27 @@ def main():
     if int(err.item()) != 0:
         raise SystemExit(f"device error word 0x{int(err.item()):x}")
 
+    # each graph holds steps_per_graph consecutive steps (replicas rotate
+    # inside it); a step is never split across graphs
+    S = max(1, args.steps_per_graph)
     graphs = None
     if not args.no_graph:
         graphs = []
-        for r in range(R):
+        for gi in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(r)
+                for j in range(S):
+                    step((gi * S + j) % R)
             graphs.append(g)
         torch.cuda.synchronize()
 
     def run_steps(k, start=0):
-        for i in range(start, start + k):
-            if graphs is not None:
+        if graphs is not None:
+            assert k % S == 0, "steps and warmup must be multiples of --steps-per-graph"
+            for i in range(start // S, (start + k) // S):
                 graphs[i % R].replay()
-            else:
+        else:
+            for i in range(start, start + k):
                 step(i % R)
 
     run_steps(args.warmup)
@@ -287,7 +329,7 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4))
     roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "spec_tree_attn_verify (split-KV attention + split merge)"
+    roof["kernel"] = "tree_attn_split_kernel (split-KV tree attention, split merge fused)"
     roof["launch_us"] = round(attn_us, 3)
     roof["bytes_per_launch"] = bytes_["attention"]
 
@@ -310,7 +352,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "tree_nodes": N, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "prefix": [w.prefix_lo, w.prefix_hi], "vocab": w.V,
-                   "graph": graphs is not None, "overlap": bool(args.overlap), "replicas": R},
+                   "graph": graphs is not None, "steps_per_graph": S if graphs is not None else None,
+                   "two_streams": side is not None, "order": args.order, "replicas": R},
         "tree_tokens_per_s": round(steps_per_s * B * N, 1),
         "step_hbm_gbs": round(bytes_["step"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(bytes_["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -124,11 +124,16 @@ size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int 
  *   out        [B][N][Hq][D] of q_dtype, 16-B aligned
  *   lse        float[B][N][Hq], nullable
  *   workspace  >= spec_tree_attn_workspace_bytes(...) bytes, 16-B aligned;
- *              may be NULL when that size is 0.  Contents need no
- *              initialisation; concurrent calls must not share it.
+ *              may be NULL when that size is 0.  It must be zero-filled
+ *              before its first use; every call leaves it ready for the next
+ *              one (its split counters back at zero), so it can be reused
+ *              without clearing.  Calls that overlap in time (other streams)
+ *              must not share one workspace.
  *   err_word   nullable: SPEC_DERR_PREFIX
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Results are deterministic: the split-K merge runs in a fixed order.
+ * Long requests are split over several workgroups; the last one of a
+ * request to finish merges the partial results in the same launch.
  */
 spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype,
                                   const void* k_cache, const void* v_cache, spec_dtype kv_dtype,

@@ -279,3 +279,25 @@ def test_attention_workspace_too_small_is_rejected():
     with pytest.raises(st.SpecError, match="WORKSPACE"):
         st.tree_attn_verify(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc, x["sm_scale"],
                             workspace=ws)
+
+
+def test_attention_workspace_is_reusable_across_calls():
+    """One zero-filled workspace, several calls with different split counts
+    per request: the split counters reset themselves after every call."""
+    w = W[1].replace(B=3, prefix_lo=2500, prefix_hi=2500, V=10, seed=41)
+    x = synth.make_inputs(w, with_logits=False)
+    d = to_device(x)
+    anc, _, _ = st.tree_mask_build(d["parents"])
+    need = st.attn_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    qo, ko, vo = oracle_views(x)
+    for pl in ([2500, 2500, 2500], [10, 1999, 700], [2500, 64, 1300], [2500, 2500, 2500]):
+        pre = np.array(pl, dtype=np.int32)
+        out, lse, err = st.tree_attn_verify(d["q"], d["k_cache"], d["v_cache"], torch.from_numpy(pre).cuda(),
+                                            anc, x["sm_scale"], workspace=ws)
+        torch.cuda.synchronize()
+        assert int(err[0]) == 0
+        ro, rl = oracle.tree_attention(qo, ko, vo, pre, x["parents"], x["sm_scale"], q_fmt="bf16", kv_fmt="bf16")
+        check_attention(out.float().cpu().numpy(), ro, "bf16", f"reuse {pl}")
+        lse_ok(lse.cpu().numpy(), rl)

@@ -128,7 +128,8 @@ def tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc_mask, sm_scale, *, k_
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
     ws_need = attn_workspace_bytes(B, N, Hq, Hkv, D, S_max)
     if workspace is None and ws_need:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        # zero-filled once; the library leaves it zeroed after each call
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     err = _err_word(err, dev)
     _check(lib().spec_tree_attn_verify(

@@ -34,11 +34,15 @@ __global__ __launch_bounds__(NT) void vocab_argmax_kernel(const float* __restric
   if (VEC) {
     const int64_t V4 = V >> 2;
     const f32x4_t* row4 = reinterpret_cast<const f32x4_t*>(row);
-    int64_t base = 0;
-    for (; base + (int64_t)NT * UNROLL <= V4; base += (int64_t)NT * UNROLL) {
+    // every pass issues all UNROLL loads before using any; the last pass is
+    // predicated instead of falling back to one load at a time
+    for (int64_t base = 0; base < V4; base += (int64_t)NT * UNROLL) {
       f32x4_t x[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) x[u] = __builtin_nontemporal_load(&row4[base + u * NT + tid]);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t k = base + u * NT + tid;
+        x[u] = (k < V4) ? __builtin_nontemporal_load(&row4[k]) : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int j = (int)((base + u * NT + tid) << 2);
@@ -47,14 +51,6 @@ __global__ __launch_bounds__(NT) void vocab_argmax_kernel(const float* __restric
         if (x[u].z > best.v) { best.v = x[u].z; best.i = j + 2; }
         if (x[u].w > best.v) { best.v = x[u].w; best.i = j + 3; }
       }
-    }
-    for (int64_t k = base + tid; k < V4; k += NT) {
-      const f32x4_t x = __builtin_nontemporal_load(&row4[k]);
-      const int j = (int)(k << 2);
-      if (x.x > best.v) { best.v = x.x; best.i = j; }
-      if (x.y > best.v) { best.v = x.y; best.i = j + 1; }
-      if (x.z > best.v) { best.v = x.z; best.i = j + 2; }
-      if (x.w > best.v) { best.v = x.w; best.i = j + 3; }
     }
     for (int64_t k = (V4 << 2) + tid; k < V; k += NT) {
       const float x = row[k];
@@ -106,10 +102,10 @@ extern "C" spec_status spec_vocab_argmax(const float* logits, int64_t rows, int6
   // flight; many rows: 256 threads and several workgroups per CU.
   if (rows < 256) {
     if (vec)
-      hipLaunchKernelGGL((vocab_argmax_kernel<1024, 4, true>), dim3((unsigned)rows), dim3(1024), 0,
+      hipLaunchKernelGGL((vocab_argmax_kernel<1024, 8, true>), dim3((unsigned)rows), dim3(1024), 0,
                          stream, logits, V, row_stride, out_idx);
     else
-      hipLaunchKernelGGL((vocab_argmax_kernel<1024, 4, false>), dim3((unsigned)rows), dim3(1024), 0,
+      hipLaunchKernelGGL((vocab_argmax_kernel<1024, 8, false>), dim3((unsigned)rows), dim3(1024), 0,
                          stream, logits, V, row_stride, out_idx);
   } else {
     if (vec)

@@ -21,8 +21,8 @@
 //   the 64-bit ancestor mask of each row is applied in registers, only on
 //   tiles that reach the tree rows.
 // A request whose tokens fit one split writes its output directly; otherwise
-// each split writes (O, m, l) partials and the merge kernel combines them in
-// split order (deterministic).
+// each split writes (O, m, l) partials and the last split to finish combines
+// them in split order (deterministic), in the same launch.
 #include <type_traits>
 
 #include "common.h"
@@ -90,6 +90,54 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 template <int I>
 using Int = std::integral_constant<int, I>;
 
+// Device-scope (all XCDs) relaxed 64-bit store / load of two floats.  The
+// hardware writes these through to the device coherence point and reads them
+// from there, so a partial result written by one workgroup is seen by another
+// workgroup of the same launch on any XCD once the writer's store has
+// completed (vmcnt) and the reader has observed the split counter.
+__device__ __forceinline__ void store_dev(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_dev(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Reductions over the four lanes {l, l^16, l^32, l^48} that share a query
+// row.  v_permlane32_swap / v_permlane16_swap hand every lane the pair {its
+// own value, its partner's}, in either order; max and + are commutative, so
+// all four lanes end with bit-identical results.
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x on the transcendental unit (v_exp_f32): exp2(-inf) = 0, and results
+// below the normal range flush to zero, which only drops weights < 2^-126.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Visibility of the 64 tokens t0 .. t0+63 of a tile to one query row: bit k
+// is set iff token t0+k is in the row's prefix, or is a tree node on the
+// row's ancestor-or-self path, and lies before the split end t_end.
+__device__ __forceinline__ uint64_t tile_visibility(uint64_t anc, int t0, int P, int t_end) {
+  const int pre = P - t0;                         // prefix tokens in the tile (may be <= 0)
+  const uint64_t prefix = pre <= 0 ? 0ull : ((1ull << pre) - 1ull);   // pre < 64 here
+  const uint64_t tree = pre >= 0 ? (anc << pre) : (anc >> (-pre));    // -pre < N <= 64
+  const int lim = t_end - t0;                     // 1 .. 64
+  const uint64_t inside = lim >= 64 ? ~0ull : ((1ull << lim) - 1ull);
+  return (prefix | tree) & inside;
+}
+
 // One wave-wide 16-byte-per-lane DMA from global memory into LDS: lane l's
 // 16 bytes land at LDS byte lds_addr + 16*l (lds_addr wave-uniform, via M0).
 // Issued as inline assembly so the compiler's wait-count pass does not treat
@@ -128,9 +176,9 @@ void tree_attn_split_kernel(
     const uint64_t* __restrict__ anc_mask, int B, int N, int Hq, int Hkv, int S_max,
     float sm_scale, int split_len, int n_splits, int n_mt, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    uint32_t* __restrict__ err_word) {
+    uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word) {
   static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
-  static_assert(NSTAGE == 2 || NSTAGE == 3, "ring depth");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 8, "ring depth");
   constexpr int NW = WM * WT;
   constexpr int EB = (KVF == SPEC_BF16) ? 2 : 1;     // bytes per cached element
   constexpr int CPT = 2 / WT;                        // 32-token chunks per wave per tile
@@ -139,30 +187,18 @@ void tree_attn_split_kernel(
   constexpr int TB = kTile * RBYTES;                 // bytes per tensor per stage
   constexpr int NLOAD = TB / 1024;                   // 1-KB wave DMA instructions per tensor
   constexpr int KPW = NLOAD / NW;                    // per wave per tensor per stage
+  constexpr int PT = 2 * KPW;                        // DMA instructions per wave per tile
   constexpr int RPI = 1024 / RBYTES;                 // rows per DMA instruction
   constexpr int MT = WM * RB * 16;                   // packed rows per workgroup
   constexpr int KC = D / 32;
   constexpr int DB = D / 16;
   static_assert(NLOAD % NW == 0, "DMA instructions must split evenly over the waves");
+  static_assert((NSTAGE - 2) * PT < 64, "tiles in flight must fit the vmcnt counter");
 
-  // one LDS object per stage and tensor, so the compiler can tell the stage
-  // being read from the stages still being filled (no forced vmcnt(0))
-  __shared__ __align__(1024) unsigned char sk0[TB];
-  __shared__ __align__(1024) unsigned char sv0[TB];
-  __shared__ __align__(1024) unsigned char sk1[TB];
-  __shared__ __align__(1024) unsigned char sv1[TB];
-  __shared__ __align__(1024) unsigned char sk2[NSTAGE > 2 ? TB : 16];
-  __shared__ __align__(1024) unsigned char sv2[NSTAGE > 2 ? TB : 16];
-  auto kst = [&](auto S) -> unsigned char* {
-    if constexpr (decltype(S)::value == 0) return sk0;
-    else if constexpr (decltype(S)::value == 1) return sk1;
-    else return sk2;
-  };
-  auto vst = [&](auto S) -> unsigned char* {
-    if constexpr (decltype(S)::value == 0) return sv0;
-    else if constexpr (decltype(S)::value == 1) return sv1;
-    else return sv2;
-  };
+  // the ring: stage s holds K at smem + 2s*TB and V at smem + (2s+1)*TB
+  __shared__ __align__(1024) unsigned char smem[NSTAGE * 2 * TB];
+  auto kst = [&](int st) -> unsigned char* { return smem + (2 * st) * TB; };
+  auto vst = [&](int st) -> unsigned char* { return smem + (2 * st + 1) * TB; };
 
   // ---- work item, XCD-aware: workgroups are dispatched round-robin over the
   // 8 XCDs, so the M-tiles of one KV range get ids congruent mod 8 and share
@@ -213,7 +249,7 @@ void tree_attn_split_kernel(
   // ---- DMA of tile i into stage S: wave w issues instructions w, w+NW, ...;
   // lane l of instruction j fills LDS bytes j*1024 + 16l, i.e. row
   // j*RPI + l/UPR at swizzled unit l%UPR.
-  auto issue = [&](auto S, int i) {
+  auto issue = [&](int st, int i) {
     const int t0 = t_begin + i * kTile;
 #pragma unroll
     for (int qd = 0; qd < KPW; ++qd) {
@@ -222,15 +258,12 @@ void tree_attn_split_kernel(
       const int u = (lane % UPR) ^ swz<UPR>(row);
       const size_t c = (size_t)min(t0 + row, t_end - 1);     // rows past the split repeat a valid row
       const size_t goff = c * RBYTES + u * 16;
-      dma16(kbase + goff, kst(S) + j * 1024);
-      dma16(vbase + goff, vst(S) + j * 1024);
+      dma16(kbase + goff, kst(st) + j * 1024);
+      dma16(vbase + goff, vst(st) + j * 1024);
     }
   };
 
-  issue(Int<0>{}, 0);
-  if constexpr (NSTAGE > 2) {
-    if (ntiles > 1) issue(Int<1>{}, 1);
-  }
+  issue(0, 0);
 
   // ---- Q rows of this wave as MFMA B operands (K-slots 32c + 8lg .. +7)
   bf16x8_t qreg[RB][KC];
@@ -260,6 +293,10 @@ void tree_attn_split_kernel(
 #pragma unroll
     for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
   }
+  // tile 0 has landed with the Q loads; put tiles 1 .. NSTAGE-2 in flight
+#pragma unroll
+  for (int i = 1; i < NSTAGE - 1; ++i)
+    if (i < ntiles) issue(i, i);
 
   f32x4_t oacc[RB][DB];
   float m_run[RB], l_run[RB];
@@ -307,9 +344,9 @@ void tree_attn_split_kernel(
     }
   };
 
-  auto compute = [&](auto S, int i) {
-    const unsigned char* ks = kst(S);
-    const unsigned char* vs = vst(S);
+  auto compute = [&](int st, int i) {
+    const unsigned char* ks = kst(st);
+    const unsigned char* vs = vst(st);
     const int t0 = t_begin + i * kTile;
     // ---- S^T = K . Q^T for this wave's chunks of the tile
     f32x4_t sacc[RB][CPT][2];
@@ -336,8 +373,16 @@ void tree_attn_split_kernel(
     // ---- mask, online softmax (base 2), P in bf16
     const bool plain = (t0 + kTile <= P);   // the whole tile is prefix: nothing masked
     bf16x8_t pb[RB][CPT];
+    float alpha[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      // this lane's 8 tokens of chunk cp sit at bits 32*ch + 8*lg .. +7
+      uint32_t vis8[CPT];
+      if (!plain) {
+        const uint64_t vis = tile_visibility(anc[rb], t0, P, t_end);
+#pragma unroll
+        for (int cp = 0; cp < CPT; ++cp) vis8[cp] = (uint32_t)(vis >> (32 * (wt * CPT + cp) + 8 * lg)) & 0xFFu;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int cp = 0; cp < CPT; ++cp)
@@ -346,19 +391,14 @@ void tree_attn_split_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float s = sacc[rb][cp][G][r] * scale_log2;
-            if (!plain) {
-              const int c = t0 + 32 * (wt * CPT + cp) + 8 * lg + 4 * G + r;
-              const bool ok = (c < t_end) && (c < P || ((anc[rb] >> (c - P)) & 1ull));
-              s = ok ? s : -INFINITY;
-            }
+            if (!plain) s = ((vis8[cp] >> (4 * G + r)) & 1u) ? s : -INFINITY;
             sacc[rb][cp][G][r] = s;
             mx = fmaxf(mx, s);
           }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = row4_max(mx);
       const float m_new = fmaxf(m_run[rb], mx);
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = exp2f(m_run[rb] - m_use);
+      alpha[rb] = fast_exp2(m_run[rb] - m_use);
       m_run[rb] = m_new;
       float lsum = 0.0f;
 #pragma unroll
@@ -367,13 +407,23 @@ void tree_attn_split_kernel(
         for (int G = 0; G < 2; ++G)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(sacc[rb][cp][G][r] - m_use);
+            const float p = fast_exp2(sacc[rb][cp][G][r] - m_use);
             lsum += p;
             pb[rb][cp][4 * G + r] = (__bf16)p;
           }
-      l_run[rb] = l_run[rb] * alpha + lsum;
+      l_run[rb] = l_run[rb] * alpha[rb] + lsum;
+    }
+    // rescale O only when some row's running max moved (alpha != 1): after the
+    // first tiles that is rare, and skipping a multiply by exactly 1 changes
+    // nothing
+    bool moved = false;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+    for (int rb = 0; rb < RB; ++rb) moved |= (alpha[rb] != 1.0f);
+    if (__any(moved)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
     }
     // ---- O^T += V^T . P^T
 #pragma unroll
@@ -388,56 +438,56 @@ void tree_attn_split_kernel(
     }
   };
 
-  // one ring step: wait for tile i (later tiles may stay in flight), make it
-  // visible to all waves, refill the stage that tile i-1 used, compute tile i
-  auto step = [&](auto S, int i) -> bool {
-    if (i >= ntiles) return false;
-    if constexpr (NSTAGE == 3) {
-      if (i + 1 < ntiles) wait_vmcnt<2 * KPW>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
+  // ring: wait for tile i (the tiles after it stay in flight), make it visible
+  // to all waves, refill the stage tile i-1 used, compute tile i
+  int st = 0;
+  for (int i = 0; i < ntiles; ++i) {
+    const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
+    switch (ahead) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1 * PT>(); break;
+      case 2: if constexpr (NSTAGE > 3) wait_vmcnt<2 * PT>(); break;
+      case 3: if constexpr (NSTAGE > 4) wait_vmcnt<3 * PT>(); break;
+      case 4: if constexpr (NSTAGE > 5) wait_vmcnt<4 * PT>(); break;
+      case 5: if constexpr (NSTAGE > 6) wait_vmcnt<5 * PT>(); break;
+      default: if constexpr (NSTAGE > 7) wait_vmcnt<6 * PT>(); break;
     }
     wg_barrier();
-    if (i + NSTAGE - 1 < ntiles) issue(Int<(decltype(S)::value + NSTAGE - 1) % NSTAGE>{}, i + NSTAGE - 1);
-    compute(S, i);
-    return true;
-  };
-  for (int i = 0;; i += NSTAGE) {
-    if (!step(Int<0>{}, i)) break;
-    if (!step(Int<1>{}, i + 1)) break;
-    if constexpr (NSTAGE > 2) {
-      if (!step(Int<2>{}, i + 2)) break;
-    }
+    if (i + NSTAGE - 1 < ntiles) issue(st == 0 ? NSTAGE - 1 : st - 1, i + NSTAGE - 1);
+    compute(st, i);
+    st = (st + 1 == NSTAGE) ? 0 : st + 1;
   }
 
   // ---- waves that split the tile's tokens combine their states in LDS
   if constexpr (WT == 2) {
-    // scratch: row blocks [0, HB) in stage-0 K, [HB, WM*RB) in stage-1 K, (m, l) in stage-0 V
-    constexpr int HB = (WM * RB + 1) / 2;
-    static_assert(HB * DB * 64 * 16 <= TB && WM * RB * 64 * 8 <= TB, "combine scratch");
+    // scratch in the ring: O blocks (1 KB per row block and column block)
+    // first, then (m, l) pairs (512 B per row block)
+    constexpr int OBYTES = WM * RB * DB * 1024;
+    static_assert(OBYTES + WM * RB * 512 <= NSTAGE * 2 * TB, "combine scratch");
     __syncthreads();                                    // all DMA and LDS stage reads are done
+    auto scratch = [&](int off) -> unsigned char* { return smem + off; };
     auto oslot = [&](int blk, int db) -> f32x4_t* {
-      f32x4_t* base = reinterpret_cast<f32x4_t*>(blk < HB ? sk0 : sk1);
-      return base + ((blk < HB ? blk : blk - HB) * DB + db) * 64 + lane;
+      return reinterpret_cast<f32x4_t*>(scratch((blk * DB + db) * 1024)) + lane;
     };
-    float2* sml = reinterpret_cast<float2*>(sv0);       // [WM*RB][64]
+    auto mlslot = [&](int blk) -> float2* {
+      return reinterpret_cast<float2*>(scratch(OBYTES + blk * 512)) + lane;
+    };
     if (wt == 1) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) *oslot(wm * RB + rb, db) = oacc[rb][db];
-        sml[(wm * RB + rb) * 64 + lane] = make_float2(m_run[rb], l_run[rb]);
+        *mlslot(wm * RB + rb) = make_float2(m_run[rb], l_run[rb]);
       }
     }
     __syncthreads();
-    if (wt == 1) return;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float2 o = sml[(wm * RB + rb) * 64 + lane];
+      if (wt == 1) break;                              // combined state lives in the wt == 0 waves
+      const float2 o = *mlslot(wm * RB + rb);
       const float m_new = fmaxf(m_run[rb], o.x);
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float a0 = exp2f(m_run[rb] - m_use), a1 = exp2f(o.x - m_use);
+      const float a0 = fast_exp2(m_run[rb] - m_use), a1 = fast_exp2(o.x - m_use);
       m_run[rb] = m_new;
       l_run[rb] = l_run[rb] * a0 + o.y * a1;
 #pragma unroll
@@ -446,11 +496,11 @@ void tree_attn_split_kernel(
   }
 
   // ---- epilogue: lane holds O^T[16db + 4lg + r][row l16]
+  const size_t unit_rows = (size_t)(b * Hkv + kvh) * n_splits * (size_t)(n_mt * MT);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    float l = l_run[rb];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    if (wt != 0) break;                              // the token-split partner waves hold no result
+    const float l = row4_sum(l_run[rb]);
     const int row = row0 + rb * 16 + l16;
     if (row >= M) continue;
     const int i = row / g, hl = row % g;
@@ -466,84 +516,87 @@ void tree_attn_split_kernel(
       }
       if (lse && lg == 0) lse[(size_t)(b * N + i) * Hq + kvh * g + hl] = (m_run[rb] + log2f(l)) * kLn2;
     } else {
-      const size_t pidx = ((size_t)(b * Hkv + kvh) * n_splits + split) * (size_t)(n_mt * MT) + row;
+      // partials are read by another workgroup (maybe on another XCD) in this
+      // same launch: device-scope stores, written through past this XCD's L2
+      const size_t pidx = unit_rows + (size_t)split * (n_mt * MT) + row;
       float* po = part_o + pidx * D + 4 * lg;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4_t v = oacc[rb][db] * out_scale;
-        *reinterpret_cast<f32x4_t*>(po + 16 * db) = v;
+        store_dev(po + 16 * db, v[0], v[1]);
+        store_dev(po + 16 * db + 2, v[2], v[3]);
       }
-      if (lg == 0) part_ml[pidx] = make_float2(m_run[rb], l);
+      if (lg == 0) store_dev(reinterpret_cast<float*>(part_ml + pidx), m_run[rb], l);
     }
   }
-}
+  if (direct) return;
 
-// Combine the split partials of requests that needed more than one split:
-//   m = max_s m_s,  w_s = 2^(m_s - m),  O = sum_s w_s O_s / sum_s w_s l_s.
-// One thread per (packed row, 4 output columns).  Splits are taken in index
-// order, eight at a time with all their loads issued together (an online
-// max over the groups), so the result is deterministic.
-template <int D>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(
-    const int32_t* __restrict__ prefix_lens, int B, int N, int Hq, int Hkv, int S_max,
-    int split_len, int n_splits, int M_pad, const float* __restrict__ part_o,
-    const float2* __restrict__ part_ml, __bf16* __restrict__ out, float* __restrict__ lse) {
-  constexpr int QPR = D / 4;                     // column quads per row
-  constexpr int RPB = 256 / QPR;                 // rows per workgroup
-  constexpr int GRP = 8;
-  const int g = Hq / Hkv, M = g * N;
-  const int blocks_per_head = (M + RPB - 1) / RPB;
-  const int bh = blockIdx.x / blocks_per_head;
-  const int b = bh / Hkv, kvh = bh % Hkv;
-  const int row = (blockIdx.x % blocks_per_head) * RPB + threadIdx.x / QPR;
-  const int qd = threadIdx.x % QPR;
-  if (row >= M) return;
-  const int P = prefix_lens[b];
-  if (P < 0 || P > S_max - N) return;
-  const int L = P + N;
+  // ---- split merge, fused: the last workgroup of this (request, kv head,
+  // M-tile) to finish combines every split's partial, in split order, so the
+  // result does not depend on which workgroup that is.  The per-unit counter
+  // lives in the workspace; it starts at zero and the merging workgroup
+  // resets it, leaving the workspace ready for the next call.
+  wait_vmcnt<0>();                                   // this lane's partial stores have completed
+  __syncthreads();                                   // ... for every lane; every wave is done with the ring
+  uint32_t* s_last = reinterpret_cast<uint32_t*>(smem);
   const int ns = (L + split_len - 1) / split_len;
-  if (ns <= 1) return;
-
-  const size_t base = (size_t)(b * Hkv + kvh) * n_splits * (size_t)M_pad + row;
-  float m = -INFINITY, den = 0.f;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += GRP) {
-    float2 ml[GRP];
-    f32x4_t o[GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      if (s0 + j < ns) {
-        const size_t idx = base + (size_t)(s0 + j) * M_pad;
-        ml[j] = part_ml[idx];
-        o[j] = *reinterpret_cast<const f32x4_t*>(part_o + idx * D + 4 * qd);
-      } else {
-        ml[j] = make_float2(-INFINITY, 0.f);
-        o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    float mc = m;
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) mc = fmaxf(mc, ml[j].x);
-    const float m_use = (mc == -INFINITY) ? 0.f : mc;
-    const float a = exp2f(m - m_use);
-    den *= a;
-    acc *= a;
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const float w = exp2f(ml[j].x - m_use);
-      den += w * ml[j].y;
-      acc += w * o[j];
-    }
-    m = mc;
+  uint32_t* cnt = counters + (size_t)(b * Hkv + kvh) * n_mt + mt;
+  if (tid == 0) {
+    const uint32_t seen = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    *s_last = (seen == (uint32_t)(ns - 1)) ? 1u : 0u;
   }
-  const int i = row / g, hl = row % g;
-  const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
-  const float inv = 1.0f / den;
-  bf16x4_t v;
+  __syncthreads();
+  if (!*s_last) return;
+  constexpr int QPR = D / 4;                         // column quads per row
+  constexpr int GRP = 8;
+  for (int item = tid; item < MT * QPR; item += NW * kWave) {
+    const int row = mt * MT + item / QPR;
+    const int qd = item % QPR;
+    if (row >= M) continue;
+    const size_t base = unit_rows + row;
+    float m = -INFINITY, den = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += GRP) {
+      float2 ml[GRP];
+      f32x4_t o[GRP];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[r] * inv);
-  *reinterpret_cast<bf16x4_t*>(out + orow * D + 4 * qd) = v;
-  if (lse && qd == 0) lse[orow] = (m + log2f(den)) * kLn2;
+      for (int j = 0; j < GRP; ++j) {
+        if (s0 + j < ns) {
+          const size_t idx = base + (size_t)(s0 + j) * (n_mt * MT);
+          ml[j] = load_dev(reinterpret_cast<const float*>(part_ml + idx));
+          const float2 lo = load_dev(part_o + idx * D + 4 * qd);
+          const float2 hi = load_dev(part_o + idx * D + 4 * qd + 2);
+          o[j] = f32x4_t{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          ml[j] = make_float2(-INFINITY, 0.f);
+          o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float mc = m;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) mc = fmaxf(mc, ml[j].x);
+      const float m_use = (mc == -INFINITY) ? 0.f : mc;
+      const float a = fast_exp2(m - m_use);
+      den *= a;
+      acc *= a;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const float w = fast_exp2(ml[j].x - m_use);
+        den += w * ml[j].y;
+        acc += w * o[j];
+      }
+      m = mc;
+    }
+    const int i = row / g, hl = row % g;
+    const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
+    const float inv = 1.0f / den;
+    bf16x4_t v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[r] * inv);
+    *reinterpret_cast<bf16x4_t*>(out + orow * D + 4 * qd) = v;
+    if (lse && qd == 0) lse[orow] = (m + log2f(den)) * kLn2;
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // fp32 Q/K/V: one wave per (request, node, head), exact fp32 arithmetic on the
@@ -639,32 +692,37 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
 struct AttnPlan {
   int rb, wm, wt, nstage, mt_rows, n_mt, M_pad;
   int split_len, n_splits;
-  size_t lds_bytes;
   size_t ws_bytes;
 };
 
-// Rows per workgroup follow the packed M = g*N.  Small M (<= 32) lets two
-// waves split each tile's tokens; larger M splits rows over the waves.  KV
-// splits are then added until the grid fills the GPU at the occupancy the
-// LDS ring allows (256 CUs x workgroups per CU), never below 256 tokens per
-// split so the partial (O, m, l) traffic stays small against the split's
-// K/V bytes.
+// Rows per workgroup follow the packed M = g*N.  Small M (<= 32) lets the
+// waves also split each tile's tokens (a 3-stage K/V ring, one workgroup per
+// CU); larger M splits rows over the waves (a 2-stage ring, two workgroups per
+// CU, so two waves share each SIMD).  KV splits are then added until the grid
+// has about one workgroup per resident slot (256 CUs), never below 256
+// tokens per split so the partial (O, m, l) traffic stays small against the
+// split's K/V bytes.  The split plan does not depend on the cached dtype, so
+// one workspace size serves every format.
 static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, int kv_bytes, AttnPlan* p) {
+  (void)kv_bytes;
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < Hkv || Hq % Hkv) return false;
   if (D != 64 && D != 128) return false;
   if (S_max < N) return false;
   const int M = (Hq / Hkv) * N;
-  if (M <= 32) { p->rb = 2; p->wm = 1; p->wt = 2; p->nstage = 3; }
-  else if (M <= 64) { p->rb = 2; p->wm = 2; p->wt = 1; p->nstage = 3; }
+  if (M <= 32) { p->rb = 1; p->wm = 2; p->wt = 2; p->nstage = 3; }
+  else if (M <= 64) { p->rb = 2; p->wm = 2; p->wt = 1; p->nstage = 2; }
   else { p->rb = 2; p->wm = 4; p->wt = 1; p->nstage = 2; }
+  const int stage_bytes = 2 * kTile * D * 2;               // bf16 sizing for the split policy
+  const long long per_cu = std::max(1, std::min(2, (160 * 1024) / (p->nstage * stage_bytes)));
+  long long target_wgs = 256 * per_cu;
+#ifdef SPEC_PLAN_HOOK
+  SPEC_PLAN_HOOK(p, M, target_wgs);
+#endif
   p->mt_rows = p->rb * p->wm * 16;
   p->n_mt = (M + p->mt_rows - 1) / p->mt_rows;
   p->M_pad = p->n_mt * p->mt_rows;
-  p->lds_bytes = (size_t)p->nstage * 2 * kTile * D * kv_bytes;
-  const long long per_cu = std::max<long long>(1, (160 * 1024) / (long long)p->lds_bytes);
   const long long units = (long long)B * Hkv * p->n_mt;
-  const long long target = 256 * per_cu;
-  const int want = (int)std::max<long long>(1, (target + units - 1) / units);
+  const int want = (int)std::max<long long>(1, (target_wgs + units - 1) / units);
   int split_len = (S_max + want - 1) / want;
   split_len = ((split_len + kTile - 1) / kTile) * kTile;
   if (split_len < 256) split_len = 256;
@@ -673,7 +731,8 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, int kv_by
   p->ws_bytes = 0;
   if (p->n_splits > 1) {
     const size_t rows = (size_t)B * Hkv * p->n_splits * p->M_pad;
-    p->ws_bytes = rows * (size_t)D * sizeof(float) + rows * sizeof(float2) + 256;
+    const size_t counters = (size_t)B * Hkv * p->n_mt;
+    p->ws_bytes = rows * (size_t)D * sizeof(float) + rows * sizeof(float2) + counters * sizeof(uint32_t);
   }
   return true;
 }
@@ -682,7 +741,8 @@ template <int D, int KVF, int RB, int WM, int WT, int NS>
 static void launch_split(const AttnPlan& pl, const void* q, const void* k, const void* v,
                          const float* ks, const float* vs, const int32_t* pre, const uint64_t* anc,
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
-                         float* lse, float* po, float2* pml, uint32_t* err, hipStream_t st) {
+                         float* lse, float* po, float2* pml, uint32_t* cnt, uint32_t* err,
+                         hipStream_t st) {
   const int units = B * Hkv * pl.n_splits;
   const int units_pad = ((units + 7) / 8) * 8;
   const unsigned grid = (unsigned)units_pad * (unsigned)pl.n_mt;
@@ -690,39 +750,55 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
                      0, st, static_cast<const __bf16*>(q), static_cast<const unsigned char*>(k),
                      static_cast<const unsigned char*>(v), ks, vs, pre, anc, B, N, Hq, Hkv, S_max,
                      sm_scale, pl.split_len, pl.n_splits, pl.n_mt, static_cast<__bf16*>(out), lse,
-                     po, pml, err);
+                     po, pml, cnt, err);
 }
 
+// Whether an instantiation is buildable: the ring fits the LDS, the tiles in
+// flight fit the vmcnt counter, the DMA splits evenly over the waves and the
+// token-split combine has scratch room.
+template <int D, int KVF, int RB, int WM, int WT, int NS>
+constexpr bool split_fits() {
+  constexpr int TB = kTile * D * ((KVF == SPEC_BF16) ? 2 : 1);
+  constexpr int NW = WM * WT;
+  constexpr int NLOAD = TB / 1024;
+  if (NS * 2 * TB > 160 * 1024) return false;
+  if (NLOAD % NW != 0) return false;
+  if ((NS - 2) * 2 * (NLOAD / NW) >= 64) return false;
+  if (WT == 2 && WM * RB * (D / 16) * 1024 + WM * RB * 512 > NS * 2 * TB) return false;
+  return true;
+}
+
+// (RB, WM, WT, NSTAGE) instantiations the planner may pick.
+#ifndef SPEC_SPLIT_PLANS
+#define SPEC_SPLIT_PLANS(X) X(1, 2, 2, 3) X(2, 2, 1, 2) X(2, 4, 1, 2)
+#endif
+
 template <int D, int KVF>
-static void dispatch_shape(const AttnPlan& pl, const void* q, const void* k, const void* v,
+static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, const void* v,
                            const float* ks, const float* vs, const int32_t* pre,
                            const uint64_t* anc, int B, int N, int Hq, int Hkv, int S_max,
                            float sm_scale, void* out, float* lse, float* po, float2* pml,
-                           uint32_t* err, hipStream_t st) {
-#define SPEC_LAUNCH(RB_, WM_, WT_, NS_)                                                          \
-  launch_split<D, KVF, RB_, WM_, WT_, NS_>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max,   \
-                                           sm_scale, out, lse, po, pml, err, st)
-  if (pl.wt == 2) SPEC_LAUNCH(2, 1, 2, 3);
-  else if (pl.wm == 2) SPEC_LAUNCH(2, 2, 1, 3);
-  else SPEC_LAUNCH(2, 4, 1, 2);
-#undef SPEC_LAUNCH
+                           uint32_t* cnt, uint32_t* err, hipStream_t st) {
+#define SPEC_TRY(RB_, WM_, WT_, NS_)                                                               \
+  if constexpr (split_fits<D, KVF, RB_, WM_, WT_, NS_>()) {                                        \
+    if (pl.rb == RB_ && pl.wm == WM_ && pl.wt == WT_ && pl.nstage == NS_) {                        \
+      launch_split<D, KVF, RB_, WM_, WT_, NS_>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, \
+                                               sm_scale, out, lse, po, pml, cnt, err, st);        \
+      return true;                                                                                 \
+    }                                                                                              \
+  }
+  SPEC_SPLIT_PLANS(SPEC_TRY)
+#undef SPEC_TRY
+  return false;
 }
 
 }  // namespace spectree
 
 using namespace spectree;
 
-static int kv_elem_bytes(int D, int S_max) {
-  (void)D;
-  (void)S_max;
-  return 2;
-}
-
 extern "C" size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max) {
   AttnPlan pl;
-  // the split plan does not depend on the cached dtype (the LDS ring of the
-  // 2-byte format bounds both), so one workspace size serves every format
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, kv_elem_bytes(D, S_max), &pl)) return 0;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, 2, &pl)) return 0;
   return pl.ws_bytes;
 }
 
@@ -743,7 +819,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   if (!f32 && !bf16 && !fp8) return SPEC_ERR_DTYPE;
   if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
   AttnPlan pl;
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, kv_elem_bytes(D, S_max), &pl)) return SPEC_ERR_SHAPE;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, f32 ? 4 : (bf16 ? 2 : 1), &pl)) return SPEC_ERR_SHAPE;
   if ((long long)B * Hkv * pl.n_splits * pl.n_mt >= (1ll << 31)) return SPEC_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return SPEC_ERR_ALIGN;
@@ -765,6 +841,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
 
   float* po = nullptr;
   float2* pml = nullptr;
+  uint32_t* cnt = nullptr;
   if (pl.ws_bytes) {
     if (!workspace) return SPEC_ERR_WORKSPACE;
     if (workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
@@ -772,30 +849,20 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
     const size_t rows = (size_t)B * Hkv * pl.n_splits * pl.M_pad;
     po = static_cast<float*>(workspace);
     pml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + rows * D * sizeof(float));
+    cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + rows * D * sizeof(float) +
+                                      rows * sizeof(float2));
   }
 
+  bool launched;
   if (bf16) {
-    if (D == 64) dispatch_shape<64, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
-    else dispatch_shape<128, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
+    if (D == 64) launched = dispatch_shape<64, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
+    else launched = dispatch_shape<128, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
   } else {
-    if (D == 64) dispatch_shape<64, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
-    else dispatch_shape<128, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, err_word, stream);
+    if (D == 64) launched = dispatch_shape<64, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
+    else launched = dispatch_shape<128, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
   }
+  if (!launched) return SPEC_ERR_SHAPE;
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
 
-  if (pl.n_splits > 1) {
-    const int M = (Hq / Hkv) * N;
-    const int rpb = 256 / (D / 4);
-    const unsigned grid = (unsigned)(B * Hkv) * (unsigned)((M + rpb - 1) / rpb);
-    if (D == 64)
-      hipLaunchKernelGGL(tree_attn_merge_kernel<64>, dim3(grid), dim3(256), 0, stream, prefix_lens, B,
-                         N, Hq, Hkv, S_max, pl.split_len, pl.n_splits, pl.M_pad, po, pml,
-                         static_cast<__bf16*>(out), lse);
-    else
-      hipLaunchKernelGGL(tree_attn_merge_kernel<128>, dim3(grid), dim3(256), 0, stream, prefix_lens, B,
-                         N, Hq, Hkv, S_max, pl.split_len, pl.n_splits, pl.M_pad, po, pml,
-                         static_cast<__bf16*>(out), lse);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-  }
   return SPEC_OK;
 }

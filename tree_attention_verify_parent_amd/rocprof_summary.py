@@ -1,0 +1,140 @@
+"""Summarise rocprofv3 result databases into short text tables.
+
+    python -m tree_attention_verify_parent_amd.rocprof_summary stats DIR [--cmd "..."]
+        per-kernel call count and average / min / max duration (kernel trace)
+    python -m tree_attention_verify_parent_amd.rocprof_summary pmc DIR [--cmd "..."]
+        per-kernel average of every collected counter (one --pmc pass)
+    python -m tree_attention_verify_parent_amd.rocprof_summary traffic \\
+            FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --kernel NAME --copy-bytes BYTES --out JSON
+        HBM bytes per launch of NAME from a FETCH_SIZE pass and a WRITE_SIZE pass,
+        each scaled by what the same counter reads for a plain elementwise copy
+        that reads and writes BYTES bytes (bench.py --copy-calibration BYTES,
+        profiled with the same counter).
+
+DIR is a rocprofv3 output directory (-d); every *_results.db below it is read.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+
+SHORT = ("tree_attn_split_kernel", "tree_attn_f32_kernel", "vocab_argmax_kernel", "accept_walk_kernel",
+         "tree_mask_build_kernel")
+
+
+def short_name(name: str) -> str:
+    for k in SHORT:
+        if k in name:
+            tpl = name.split(k, 1)[1]
+            return k + (tpl[:tpl.find("(")] if tpl.startswith("<") else "")
+    if "elementwise" in name.lower():
+        return "elementwise:" + name[:56]
+    return name[:70]
+
+
+def dbs(d):
+    out = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not out:
+        raise SystemExit(f"no *_results.db under {d}")
+    return out
+
+
+def kernel_stats(d):
+    agg = collections.defaultdict(list)
+    for db in dbs(d):
+        c = sqlite3.connect(db)
+        for name, start, end in c.execute("select name, start, end from kernels"):
+            agg[short_name(name)].append((end - start) / 1e3)
+    return agg
+
+
+def pmc(d):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for db in dbs(d):
+        c = sqlite3.connect(db)
+        cols = [r[1] for r in c.execute("pragma table_info(counters_collection)")]
+        ci = {n: i for i, n in enumerate(cols)}
+        kname = "kernel_name" if "kernel_name" in ci else "name"
+        for r in c.execute("select * from counters_collection"):
+            agg[short_name(r[ci[kname]])][r[ci["counter_name"]]].append(float(r[ci["value"]]))
+    return agg
+
+
+def source_sha(root):
+    h = hashlib.sha256()
+    csrc = os.path.join(root, "tree_attention_verify_parent_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", choices=["stats", "pmc", "traffic"])
+    ap.add_argument("dirs", nargs="+")
+    ap.add_argument("--cmd", default="")
+    ap.add_argument("--kernel", default="tree_attn_split_kernel")
+    ap.add_argument("--copy-bytes", type=float, default=0)
+    ap.add_argument("--out", default="")
+    a = ap.parse_args(argv)
+    if a.cmd:
+        print(f"command: {a.cmd}")
+    if a.mode == "stats":
+        agg = kernel_stats(a.dirs[0])
+        tot = sum(sum(v) for v in agg.values())
+        print(f"{'kernel':58s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
+        for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{k:58s} {len(v):7d} {sum(v)/len(v):9.3f} {min(v):9.3f} {max(v):9.3f} {100*sum(v)/tot:6.1f}")
+    elif a.mode == "pmc":
+        agg = pmc(a.dirs[0])
+        for k, ctrs in sorted(agg.items()):
+            n = max(len(v) for v in ctrs.values())
+            vals = ", ".join(f"{c}={sum(v)/len(v):.4g}" for c, v in sorted(ctrs.items()))
+            print(f"{k} ({n} dispatches): {vals}")
+    else:
+        if len(a.dirs) != 4:
+            raise SystemExit("traffic needs FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR")
+        fetch, write, cfetch, cwrite = (pmc(d) for d in a.dirs)
+
+        def avg(agg, kern, ctr):
+            for k, ctrs in agg.items():
+                if k.startswith(kern) and ctr in ctrs:
+                    v = ctrs[ctr]
+                    return sum(v) / len(v)
+            raise SystemExit(f"no {ctr} for {kern}")
+
+        def copy_avg(agg, ctr):
+            best = None
+            for k, ctrs in agg.items():
+                if k.startswith("elementwise:") and ctr in ctrs:
+                    v = sum(ctrs[ctr]) / len(ctrs[ctr])
+                    best = v if best is None else max(best, v)
+            if best is None:
+                raise SystemExit(f"no copy kernel with {ctr}")
+            return best
+
+        kf, kw = avg(fetch, a.kernel, "FETCH_SIZE"), avg(write, a.kernel, "WRITE_SIZE")
+        cf, cw = copy_avg(cfetch, "FETCH_SIZE"), copy_avg(cwrite, "WRITE_SIZE")
+        # the copy reads and writes copy_bytes each: bytes per counter unit
+        f_scale, w_scale = a.copy_bytes / cf, a.copy_bytes / cw
+        res = dict(kernel=a.kernel, fetch_counter=kf, write_counter=kw, copy_fetch_counter=cf,
+                   copy_write_counter=cw, copy_bytes=a.copy_bytes, fetch_scale=f_scale, write_scale=w_scale,
+                   fetch_bytes=kf * f_scale, write_bytes=kw * w_scale,
+                   bytes_per_launch=kf * f_scale + kw * w_scale,
+                   kernel_source_sha=source_sha(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))),
+                   command=a.cmd)
+        print(json.dumps(res, indent=1))
+        if a.out:
+            with open(a.out, "w") as f:
+                json.dump(res, f, indent=1)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
