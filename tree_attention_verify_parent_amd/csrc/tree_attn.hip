@@ -152,15 +152,17 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
 // One workgroup = one (request b, kv head, M-tile, KV split).
 //   Wave (wm, wt) owns RB 16-row blocks of the M-tile and the 32-token chunks
 //   wt*CPT .. wt*CPT+CPT-1 of every 64-token tile (CPT = 2/WT).
-// Waves per SIMD the kernel is built for: as many workgroups as the LDS ring
-// leaves room for on a CU (160 KB), so the compiler keeps the register count
-// at or below 512 / that many waves instead of spending it on unrolling.
-// The register budget caps it too: two row blocks per wave need about 200+
-// registers, so at most 2 waves per SIMD there.
-template <int D, int KVF, int RB, int WM, int WT, int NSTAGE>
+// Waves per SIMD the kernel is built for: the planner puts as many
+// workgroups on a CU as a bf16 ring leaves room for in the 160 KB LDS (at
+// most 2; the same count for every cache format, so one workspace size serves
+// all), and the compiler may spend 512 / that many waves registers per wave.
+// Two row blocks per wave need about 200+ registers, so at most 2 waves per
+// SIMD there.
+template <int D, int RB, int WM, int WT, int NSTAGE>
 struct SplitOccupancy {
-  static constexpr int lds = NSTAGE * 2 * kTile * D * ((KVF == SPEC_BF16) ? 2 : 1);
-  static constexpr int wg_per_cu = (160 * 1024) / lds;
+  static constexpr int ring_bf16 = NSTAGE * 2 * kTile * D * 2;
+  static constexpr int fit = (160 * 1024) / ring_bf16;
+  static constexpr int wg_per_cu = fit < 1 ? 1 : (fit > 2 ? 2 : fit);
   static constexpr int w = (wg_per_cu * WM * WT + 3) / 4;
   static constexpr int cap = (RB >= 2) ? 2 : 4;
   static constexpr int value = w < 1 ? 1 : (w > cap ? cap : w);
@@ -168,7 +170,7 @@ struct SplitOccupancy {
 
 template <int D, int KVF, int RB, int WM, int WT, int NSTAGE>
 __global__ __launch_bounds__(WM * WT * kWave)
-__attribute__((amdgpu_waves_per_eu(SplitOccupancy<D, KVF, RB, WM, WT, NSTAGE>::value)))
+__attribute__((amdgpu_waves_per_eu(SplitOccupancy<D, RB, WM, WT, NSTAGE>::value)))
 void tree_attn_split_kernel(
     const __bf16* __restrict__ q, const unsigned char* __restrict__ kc,
     const unsigned char* __restrict__ vc, const float* __restrict__ k_scale,
@@ -214,17 +216,12 @@ void tree_attn_split_kernel(
   const int g = Hq / Hkv;
   const int M = g * N;
 
-  const int P = prefix_lens[b];
-  if (P < 0 || P > S_max - N) {
-    if (threadIdx.x == 0 && split == 0 && mt == 0) flag_error(err_word, SPEC_DERR_PREFIX);
-    return;
-  }
-  const int L = P + N;
+  // The split's token range as far as it can be known before the prefix
+  // length arrives: the first ring tiles are fetched for it right away, so the
+  // load of prefix_lens[b] does not delay the K/V stream.
   const int t_begin = split * split_len;
-  if (t_begin >= L) return;
-  const int t_end = min(L, t_begin + split_len);
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  const bool direct = (L <= split_len);      // this request has a single split
+  const int t_spec = min(S_max, t_begin + split_len);
+  const int ntiles_spec = (t_spec - t_begin + kTile - 1) / kTile;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -249,6 +246,7 @@ void tree_attn_split_kernel(
   // ---- DMA of tile i into stage S: wave w issues instructions w, w+NW, ...;
   // lane l of instruction j fills LDS bytes j*1024 + 16l, i.e. row
   // j*RPI + l/UPR at swizzled unit l%UPR.
+  int t_lim = t_spec;                        // rows at or past t_lim repeat row t_lim - 1
   auto issue = [&](int st, int i) {
     const int t0 = t_begin + i * kTile;
 #pragma unroll
@@ -256,14 +254,20 @@ void tree_attn_split_kernel(
       const int j = wave + qd * NW;
       const int row = j * RPI + lane / UPR;
       const int u = (lane % UPR) ^ swz<UPR>(row);
-      const size_t c = (size_t)min(t0 + row, t_end - 1);     // rows past the split repeat a valid row
+      const size_t c = (size_t)min(t0 + row, t_lim - 1);
       const size_t goff = c * RBYTES + u * 16;
       dma16(kbase + goff, kst(st) + j * 1024);
       dma16(vbase + goff, vst(st) + j * 1024);
     }
   };
 
-  issue(0, 0);
+  // tiles 0 .. NSTAGE-2 go in flight first, so the start-up latency below
+  // is spent fetching the whole ring rather than one tile
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < ntiles_spec) issue(i, i);
+
+  const int P = prefix_lens[b];
 
   // ---- Q rows of this wave as MFMA B operands (K-slots 32c + 8lg .. +7)
   bf16x8_t qreg[RB][KC];
@@ -286,17 +290,38 @@ void tree_attn_split_kernel(
 
   // Complete the Q / mask loads here, once: the compiler cannot count the
   // DMA instructions, so any wait it places for these loads drains the ring;
-  // inside the tile loop that would happen on every tile.
+  // inside the tile loop that would happen on every tile.  Here it only waits
+  // for the tiles issued above, which the loop needs first anyway.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     asm volatile("" ::"v"(anc[rb]));
 #pragma unroll
     for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
   }
-  // tile 0 has landed with the Q loads; put tiles 1 .. NSTAGE-2 in flight
+  wait_vmcnt<0>();   // usually already met by the wait above; a wave with no Q rows has none
+  if (P < 0 || P > S_max - N) {
+    if (tid == 0 && split == 0 && mt == 0) flag_error(err_word, SPEC_DERR_PREFIX);
+    return;
+  }
+  const int L = P + N;
+  if (t_begin >= L) return;
+  const int t_end = min(L, t_spec);
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+  const bool direct = (L <= split_len);      // this request has a single split
+  if (t_end < t_spec) {
+    // The tiles fetched ahead loaded cache rows at or past the request's end,
+    // which hold arbitrary bits.  Those tokens get zero weight, but 0 * NaN is
+    // NaN in the PV product, so their V rows are cleared.
 #pragma unroll
-  for (int i = 1; i < NSTAGE - 1; ++i)
-    if (i < ntiles) issue(i, i);
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      if (i >= ntiles_spec) break;
+      const int first = max(t_end - (t_begin + i * kTile), 0);
+      for (int off = first * RBYTES + tid * 16; off < TB; off += NW * kWave * 16)
+        *reinterpret_cast<uint4*>(vst(i) + off) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+  }
+  t_lim = t_end;
 
   f32x4_t oacc[RB][DB];
   float m_run[RB], l_run[RB];
@@ -547,54 +572,82 @@ void tree_attn_split_kernel(
   }
   __syncthreads();
   if (!*s_last) return;
+  // Every load of the merge is independent and each costs a trip to the
+  // device coherence point, so they are issued together: a thread owns IPT
+  // (row, column quad) items and loads, per round, BATCH items x SG splits of
+  // partial O plus each split's (m, l) for the item's row; rounds over further
+  // splits rescale the running sums (online softmax over the splits).
+  constexpr int NT = NW * kWave;
   constexpr int QPR = D / 4;                         // column quads per row
-  constexpr int GRP = 8;
-  for (int item = tid; item < MT * QPR; item += NW * kWave) {
-    const int row = mt * MT + item / QPR;
-    const int qd = item % QPR;
-    if (row >= M) continue;
-    const size_t base = unit_rows + row;
-    float m = -INFINITY, den = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ns; s0 += GRP) {
-      float2 ml[GRP];
-      f32x4_t o[GRP];
+  static_assert((MT * QPR) % NT == 0, "merge items split evenly over the threads");
+  constexpr int IPT = MT * QPR / NT;                 // items per thread
+  constexpr int BATCH = IPT < 8 ? IPT : 8;
+  constexpr int SG = 16 / BATCH;                     // splits per load round
+  static_assert(IPT % BATCH == 0, "merge batches");
+  const size_t split_rows = (size_t)n_mt * MT;       // partial rows per split
+  const size_t tile_base = unit_rows + (size_t)mt * MT;
 #pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        if (s0 + j < ns) {
-          const size_t idx = base + (size_t)(s0 + j) * (n_mt * MT);
-          ml[j] = load_dev(reinterpret_cast<const float*>(part_ml + idx));
-          const float2 lo = load_dev(part_o + idx * D + 4 * qd);
-          const float2 hi = load_dev(part_o + idx * D + 4 * qd + 2);
-          o[j] = f32x4_t{lo.x, lo.y, hi.x, hi.y};
-        } else {
-          ml[j] = make_float2(-INFINITY, 0.f);
-          o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-      float mc = m;
+  for (int k0 = 0; k0 < IPT; k0 += BATCH) {
+    float m[BATCH], den[BATCH];
+    f32x4_t acc[BATCH];
 #pragma unroll
-      for (int j = 0; j < GRP; ++j) mc = fmaxf(mc, ml[j].x);
-      const float m_use = (mc == -INFINITY) ? 0.f : mc;
-      const float a = fast_exp2(m - m_use);
-      den *= a;
-      acc *= a;
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        const float w = fast_exp2(ml[j].x - m_use);
-        den += w * ml[j].y;
-        acc += w * o[j];
-      }
-      m = mc;
+    for (int k = 0; k < BATCH; ++k) {
+      m[k] = -INFINITY;
+      den[k] = 0.f;
+      acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int i = row / g, hl = row % g;
-    const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
-    const float inv = 1.0f / den;
-    bf16x4_t v;
+    for (int s0 = 0; s0 < ns; s0 += SG) {
+      float2 ml[SG][BATCH];
+      f32x4_t o[SG][BATCH];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = (__bf16)(acc[r] * inv);
-    *reinterpret_cast<bf16x4_t*>(out + orow * D + 4 * qd) = v;
-    if (lse && qd == 0) lse[orow] = (m + log2f(den)) * kLn2;
+      for (int j = 0; j < SG; ++j)
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const int item = tid + (k0 + k) * NT;
+          const int r = item / QPR, qd = item % QPR;
+          ml[j][k] = make_float2(-INFINITY, 0.f);
+          o[j][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (s0 + j < ns && mt * MT + r < M) {
+            const size_t prow = tile_base + (size_t)(s0 + j) * split_rows + r;
+            ml[j][k] = load_dev(reinterpret_cast<const float*>(part_ml + prow));
+            const float2 lo = load_dev(part_o + prow * D + 4 * qd);
+            const float2 hi = load_dev(part_o + prow * D + 4 * qd + 2);
+            o[j][k] = f32x4_t{lo.x, lo.y, hi.x, hi.y};
+          }
+        }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        float mc = m[k];
+#pragma unroll
+        for (int j = 0; j < SG; ++j) mc = fmaxf(mc, ml[j][k].x);
+        const float m_use = (mc == -INFINITY) ? 0.f : mc;
+        const float a = fast_exp2(m[k] - m_use);
+        den[k] *= a;
+        acc[k] *= a;
+#pragma unroll
+        for (int j = 0; j < SG; ++j) {
+          const float w = fast_exp2(ml[j][k].x - m_use);
+          den[k] += w * ml[j][k].y;
+          acc[k] += w * o[j][k];
+        }
+        m[k] = mc;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int item = tid + (k0 + k) * NT;
+      const int r = item / QPR, qd = item % QPR;
+      const int row = mt * MT + r;
+      if (row >= M) continue;
+      const int i = row / g, hl = row % g;
+      const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
+      const float inv = 1.0f / den[k];
+      bf16x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[k][e] * inv);
+      *reinterpret_cast<bf16x4_t*>(out + orow * D + 4 * qd) = v;
+      if (lse && qd == 0) lse[orow] = (m[k] + log2f(den[k])) * kLn2;
+    }
   }
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
