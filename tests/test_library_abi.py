@@ -49,10 +49,16 @@ def test_status_strings(L):
 
 def test_workspace_bytes_is_pure_and_rejects_bad_shapes(L):
     f = L.spec_tree_attn_workspace_bytes
-    assert f(8, 6, 32, 8, 128, 2054) == f(8, 6, 32, 8, 128, 2054) > 0       # split path
-    assert f(64, 16, 64, 8, 128, 4112) == 0                                # one split per request
+    assert f(8, 6, 32, 8, 128, 2054) == f(8, 6, 32, 8, 128, 2054) > 0
+    # two partial slots of M_pad x (D + 2) floats per unit, one counter per (request, kv head, M-tile):
+    # 256 units of one 32-row tile for M = 24; 512 units of one 128-row tile for M = 128
+    assert f(8, 6, 32, 8, 128, 2054) == 2 * 256 * 32 * (128 * 4 + 8) + 8 * 8 * 4
+    assert f(64, 16, 64, 8, 128, 4112) == 2 * 512 * 128 * (128 * 4 + 8) + 64 * 8 * 4
+    assert f(1024, 6, 32, 8, 128, 2 ** 21 - 1) > 0
     for bad in [(0, 6, 32, 8, 128, 2054), (8, 0, 32, 8, 128, 2054), (8, 65, 32, 8, 128, 2054),
-                (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 96, 2054), (8, 6, 32, 8, 128, 5)]:
+                (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 96, 2054), (8, 6, 32, 8, 128, 5),
+                (1025, 6, 32, 8, 128, 2054), (1024, 6, 32, 8, 128, 2 ** 21),
+                (1, 6, 1024, 1024, 128, 2 ** 21)]:
         assert f(*bad) == 0, bad
 
 

@@ -90,19 +90,31 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 template <int I>
 using Int = std::integral_constant<int, I>;
 
-// Device-scope (all XCDs) relaxed 64-bit store / load of two floats.  The
-// hardware writes these through to the device coherence point and reads them
-// from there, so a partial result written by one workgroup is seen by another
-// workgroup of the same launch on any XCD once the writer's store has
-// completed (vmcnt) and the reader has observed the split counter.
-__device__ __forceinline__ void store_dev(float* p, float a, float b) {
-  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope (all XCDs) stores and loads of partial results through buffer
+// instructions with the SC1 cache policy: the hardware writes these through
+// to the device coherence point and reads them from there, so data written by
+// one workgroup is seen by another workgroup of the same launch on any XCD
+// once the writer's store has completed (vmcnt) and the reader has observed
+// the split counter.  Out-of-range offsets read zero and drop stores.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kSC1 = 16;                           // cache-policy bit: device scope
+constexpr int kRsrcWord3 = 0x00020000;             // raw 32-bit buffer, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
 }
-__device__ __forceinline__ float2 load_dev(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+__device__ __forceinline__ void store_dev4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kSC1);
+}
+__device__ __forceinline__ void store_dev2(__amdgpu_buffer_rsrc_t r, int off, float a, float b) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(a), __float_as_uint(b)}, r, off, 0, kSC1);
+}
+__device__ __forceinline__ f32x4_t load_dev4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1));
+}
+__device__ __forceinline__ float2 load_dev2(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1);
+  return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
 }
 
 // Reductions over the four lanes {l, l^16, l^32, l^48} that share a query
@@ -149,6 +161,13 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
                : "memory", "m0");
 }
 
+// The same for 4 bytes per lane: lane l's dword lands at lds_addr + 4*l.
+__device__ __forceinline__ void dma4(const void* gptr, const void* lds_ptr) {
+  const uint32_t lds_addr = (uint32_t)(size_t)(lds_void_t*)lds_ptr;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // One workgroup = one (request b, kv head, M-tile, KV split).
 //   Wave (wm, wt) owns RB 16-row blocks of the M-tile and the 32-token chunks
 //   wt*CPT .. wt*CPT+CPT-1 of every 64-token tile (CPT = 2/WT).
@@ -160,12 +179,26 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
 // SIMD there.
 template <int D, int RB, int WM, int WT, int NSTAGE>
 struct SplitOccupancy {
-  static constexpr int ring_bf16 = NSTAGE * 2 * kTile * D * 2;
+  static constexpr int ring_bf16 = NSTAGE * 2 * kTile * D * 2 + 4 * 1024 + 16;
   static constexpr int fit = (160 * 1024) / ring_bf16;
   static constexpr int wg_per_cu = fit < 1 ? 1 : (fit > 2 ? 2 : fit);
   static constexpr int w = (wg_per_cu * WM * WT + 3) / 4;
   static constexpr int cap = (RB >= 2) ? 2 : 4;
   static constexpr int value = w < 1 ? 1 : (w > cap ? cap : w);
+};
+
+// A piece of work never starts or ends closer than this many tokens to either
+// end of its (request, kv head) sequence: a unit boundary that would leave a
+// shorter remainder moves to that end.
+constexpr int kMinPiece = 128;
+// Requests per launch: every workgroup keeps a table of their lengths in LDS.
+constexpr int kMaxBatch = 1024;
+
+// One (request, kv head) token sequence of the concatenated work stream:
+// request b, kv head kvh, L = P_b + N tokens, starting at stream offset start.
+struct Seg {
+  int b, kvh, L;
+  long long start;
 };
 
 template <int D, int KVF, int RB, int WM, int WT, int NSTAGE>
@@ -176,7 +209,7 @@ void tree_attn_split_kernel(
     const unsigned char* __restrict__ vc, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ prefix_lens,
     const uint64_t* __restrict__ anc_mask, int B, int N, int Hq, int Hkv, int S_max,
-    float sm_scale, int split_len, int n_splits, int n_mt, __bf16* __restrict__ out,
+    float sm_scale, int n_units, int n_mt, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
     uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word) {
   static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
@@ -195,461 +228,625 @@ void tree_attn_split_kernel(
   constexpr int KC = D / 32;
   constexpr int DB = D / 16;
   static_assert(NLOAD % NW == 0, "DMA instructions must split evenly over the waves");
-  static_assert((NSTAGE - 2) * PT < 64, "tiles in flight must fit the vmcnt counter");
+  static_assert((NSTAGE - 1) * PT < 64, "tiles in flight must fit the vmcnt counter");
+
 
   // the ring: stage s holds K at smem + 2s*TB and V at smem + (2s+1)*TB
   __shared__ __align__(1024) unsigned char smem[NSTAGE * 2 * TB];
+  __shared__ int s_cum[kMaxBatch + 1];
+  __shared__ uint32_t s_last;
   auto kst = [&](int st) -> unsigned char* { return smem + (2 * st) * TB; };
   auto vst = [&](int st) -> unsigned char* { return smem + (2 * st + 1) * TB; };
 
-  // ---- work item, XCD-aware: workgroups are dispatched round-robin over the
-  // 8 XCDs, so the M-tiles of one KV range get ids congruent mod 8 and share
-  // that XCD's L2.
+  // ---- work unit, XCD-aware: workgroups are dispatched round-robin over the
+  // 8 XCDs, so the M-tiles of one unit get ids congruent mod 8 and share that
+  // XCD's L2.
   const int id = blockIdx.x;
   const int per = 8 * n_mt;
   const int mt = (id % per) / 8;
-  const int unit = (id / per) * 8 + (id % 8);
-  if (unit >= B * Hkv * n_splits) return;
-  const int split = unit % n_splits;
-  const int kvh = (unit / n_splits) % Hkv;
-  const int b = unit / (n_splits * Hkv);
+  const int u = (id / per) * 8 + (id % 8);
+  if (u >= n_units) return;
   const int g = Hq / Hkv;
   const int M = g * N;
 
-  // The split's token range as far as it can be known before the prefix
-  // length arrives: the first ring tiles are fetched for it right away, so the
-  // load of prefix_lens[b] does not delay the K/V stream.
-  const int t_begin = split * split_len;
-  const int t_spec = min(S_max, t_begin + split_len);
-  const int ntiles_spec = (t_spec - t_begin + kTile - 1) / kTile;
+  const int lane0 = threadIdx.x & 63;
+  const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % WM;
-  const int wt = wave / WM;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
-  const int row0 = mt * MT + wm * RB * 16;
-
-  float scale_log2 = sm_scale * kLog2e;
-  float out_scale = 1.0f;
-  if constexpr (KVF == SPEC_FP8_E4M3) {
-    scale_log2 *= k_scale[kvh];
-    out_scale = v_scale[kvh];
-  }
-
-  const size_t head_off = ((size_t)(b * Hkv + kvh) * S_max) * RBYTES;
-  const unsigned char* kbase = kc + head_off;
-  const unsigned char* vbase = vc + head_off;
-
-  // ---- DMA of tile i into stage S: wave w issues instructions w, w+NW, ...;
-  // lane l of instruction j fills LDS bytes j*1024 + 16l, i.e. row
-  // j*RPI + l/UPR at swizzled unit l%UPR.
-  int t_lim = t_spec;                        // rows at or past t_lim repeat row t_lim - 1
-  auto issue = [&](int st, int i) {
-    const int t0 = t_begin + i * kTile;
+  // ---- DMA of one 64-token tile (tokens t0 .. t0+63 of the sequence at
+  // kbase / vbase; rows at or past t_end repeat row t_end - 1) into stage st:
+  // wave w issues instructions w, w+NW, ...; lane l of instruction j fills LDS
+  // bytes j*1024 + 16l, i.e. row j*RPI + l/UPR at swizzled unit l%UPR.
+  auto dma_tile = [&](const unsigned char* kbase, const unsigned char* vbase, int t0, int t_end, int st,
+                      int wave, int lane) {
 #pragma unroll
     for (int qd = 0; qd < KPW; ++qd) {
       const int j = wave + qd * NW;
       const int row = j * RPI + lane / UPR;
-      const int u = (lane % UPR) ^ swz<UPR>(row);
-      const size_t c = (size_t)min(t0 + row, t_lim - 1);
-      const size_t goff = c * RBYTES + u * 16;
+      const int unit16 = (lane % UPR) ^ swz<UPR>(row);
+      const size_t c = (size_t)min(t0 + row, t_end - 1);
+      const size_t goff = c * RBYTES + unit16 * 16;
       dma16(kbase + goff, kst(st) + j * 1024);
       dma16(vbase + goff, vst(st) + j * 1024);
     }
   };
 
-  // tiles 0 .. NSTAGE-2 go in flight first, so the start-up latency below
-  // is spent fetching the whole ring rather than one tile
-#pragma unroll
-  for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < ntiles_spec) issue(i, i);
-
-  const int P = prefix_lens[b];
-
-  // ---- Q rows of this wave as MFMA B operands (K-slots 32c + 8lg .. +7)
+  // ---- Q rows of a wave as MFMA B operands (K-slots 32c + 8lg .. +7) and
+  // the rows' ancestor masks, for sequence (b, kvh)
   bf16x8_t qreg[RB][KC];
   uint64_t anc[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = row0 + rb * 16 + l16;
-    if (row < M) {
-      const int i = row / g, hl = row % g;
-      const __bf16* qp = q + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D + 8 * lg;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * c);
-      anc[rb] = anc_mask[(size_t)b * N + i];
-    } else {
-#pragma unroll
-      for (int c = 0; c < KC; ++c) qreg[rb][c] = bf16x8_t{};
-      anc[rb] = 0ull;
-    }
-  }
-
-  // Complete the Q / mask loads here, once: the compiler cannot count the
-  // DMA instructions, so any wait it places for these loads drains the ring;
-  // inside the tile loop that would happen on every tile.  Here it only waits
-  // for the tiles issued above, which the loop needs first anyway.
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    asm volatile("" ::"v"(anc[rb]));
-#pragma unroll
-    for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
-  }
-  wait_vmcnt<0>();   // usually already met by the wait above; a wave with no Q rows has none
-  if (P < 0 || P > S_max - N) {
-    if (tid == 0 && split == 0 && mt == 0) flag_error(err_word, SPEC_DERR_PREFIX);
-    return;
-  }
-  const int L = P + N;
-  if (t_begin >= L) return;
-  const int t_end = min(L, t_spec);
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  const bool direct = (L <= split_len);      // this request has a single split
-  if (t_end < t_spec) {
-    // The tiles fetched ahead loaded cache rows at or past the request's end,
-    // which hold arbitrary bits.  Those tokens get zero weight, but 0 * NaN is
-    // NaN in the PV product, so their V rows are cleared.
-#pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i) {
-      if (i >= ntiles_spec) break;
-      const int first = max(t_end - (t_begin + i * kTile), 0);
-      for (int off = first * RBYTES + tid * 16; off < TB; off += NW * kWave * 16)
-        *reinterpret_cast<uint4*>(vst(i) + off) = make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
-  }
-  t_lim = t_end;
-
-  f32x4_t oacc[RB][DB];
-  float m_run[RB], l_run[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // A operand of S^T = K . Q^T: lane (m = l16, lg) holds K[row][32c + 8lg .. +7]
-  auto read_k = [&](const unsigned char* st, int row, int c) -> bf16x8_t {
-    if constexpr (KVF == SPEC_BF16) {
-      return *reinterpret_cast<const bf16x8_t*>(st + row * RBYTES + (((4 * c + lg) ^ swz<UPR>(row)) << 4));
-    } else {
-      const uint2 w = *reinterpret_cast<const uint2*>(
-          st + row * RBYTES + (((2 * c + (lg >> 1)) ^ swz<UPR>(row)) << 4) + ((lg & 1) << 3));
-      return fp8x8_to_bf16(w.x, w.y);
-    }
-  };
-  // A operand of O^T = V^T . P^T: lane (l16, lg) holds V[32ch + 8lg + k][16db + l16],
-  // k = 0..7.  Transpose reads: a 16-lane group's 8-byte chunks form a vector
-  // E and lane j receives E[j + 16k]; so lanes 4k'..4k'+3 (bf16) or 2k, 2k+1
-  // (fp8) point at the 16 columns of token k.
-  auto read_v = [&](const unsigned char* st, int ch, int db) -> bf16x8_t {
-    if constexpr (KVF == SPEC_BF16) {
-      i16x4_t t[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = 32 * ch + 8 * lg + 4 * r + (l16 >> 2);
-        const int u = 2 * db + ((l16 >> 1) & 1);
-        const int off = row * RBYTES + ((u ^ swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
-        t[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + off));
-      }
-      // whole-vector bit casts: assembling the operand element by element
-      // from bit-cast shorts is lowered wrongly (half-words get duplicated)
-      const i16x8_t both = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      return __builtin_bit_cast(bf16x8_t, both);
-    } else {
-      const int row = 32 * ch + 8 * lg + (l16 >> 1);
-      const int off = row * RBYTES + ((db ^ swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
-      const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(st + off));
-      return fp8x8_to_bf16((uint32_t)t[0], (uint32_t)t[1]);
-    }
-  };
-
-  auto compute = [&](int st, int i) {
-    const unsigned char* ks = kst(st);
-    const unsigned char* vs = vst(st);
-    const int t0 = t_begin + i * kTile;
-    // ---- S^T = K . Q^T for this wave's chunks of the tile
-    f32x4_t sacc[RB][CPT][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cp = 0; cp < CPT; ++cp)
-#pragma unroll
-        for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cp = 0; cp < CPT; ++cp) {
-      const int ch = wt * CPT + cp;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-#pragma unroll
-        for (int G = 0; G < 2; ++G) {
-          const bf16x8_t a = read_k(ks, 32 * ch + chunk_token(G, l16), c);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
-        }
-      }
-    }
-    // ---- mask, online softmax (base 2), P in bf16
-    const bool plain = (t0 + kTile <= P);   // the whole tile is prefix: nothing masked
-    bf16x8_t pb[RB][CPT];
-    float alpha[RB];
+  auto load_q = [&](int b, int kvh, int row0, int l16, int lg) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // this lane's 8 tokens of chunk cp sit at bits 32*ch + 8*lg .. +7
-      uint32_t vis8[CPT];
-      if (!plain) {
-        const uint64_t vis = tile_visibility(anc[rb], t0, P, t_end);
+      const int row = row0 + rb * 16 + l16;
+      if (row < M) {
+        const int i = row / g, hl = row % g;
+        const __bf16* qp = q + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D + 8 * lg;
 #pragma unroll
-        for (int cp = 0; cp < CPT; ++cp) vis8[cp] = (uint32_t)(vis >> (32 * (wt * CPT + cp) + 8 * lg)) & 0xFFu;
+        for (int c = 0; c < KC; ++c) qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * c);
+        anc[rb] = anc_mask[(size_t)b * N + i];
+      } else {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qreg[rb][c] = bf16x8_t{};
+        anc[rb] = 0ull;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int cp = 0; cp < CPT; ++cp)
-#pragma unroll
-        for (int G = 0; G < 2; ++G)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float s = sacc[rb][cp][G][r] * scale_log2;
-            if (!plain) s = ((vis8[cp] >> (4 * G + r)) & 1u) ? s : -INFINITY;
-            sacc[rb][cp][G][r] = s;
-            mx = fmaxf(mx, s);
-          }
-      mx = row4_max(mx);
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      alpha[rb] = fast_exp2(m_run[rb] - m_use);
-      m_run[rb] = m_new;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int cp = 0; cp < CPT; ++cp)
-#pragma unroll
-        for (int G = 0; G < 2; ++G)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(sacc[rb][cp][G][r] - m_use);
-            lsum += p;
-            pb[rb][cp][4 * G + r] = (__bf16)p;
-          }
-      l_run[rb] = l_run[rb] * alpha[rb] + lsum;
     }
-    // rescale O only when some row's running max moved (alpha != 1): after the
-    // first tiles that is rare, and skipping a multiply by exactly 1 changes
-    // nothing
-    bool moved = false;
+  };
+
+  // ---- Speculative start.  The lengths are not known until prefix_lens has
+  // been read and summed, which takes microseconds; in the common case where
+  // every request fills its cache (P_b = S_max - N) the unit's first piece is
+  // already known from the sizes alone, so its first tiles are fetched now.
+  // If the real lengths give another first piece, those tiles are drained and
+  // discarded (they only read in-bounds cache rows).
+  // Unit v's nominal start v*T/n (any deterministic monotone rule serves: all
+  // workgroups evaluate the same one), in fp64 rather than a slow 64-bit
+  // integer division.
+  auto share = [](int v, long long T, int n) -> long long { return (long long)((double)v * (double)T / (double)n); };
+  const long long Tg = (long long)B * Hkv * S_max;
+  const int n_actg = (int)max(1ll, min((long long)n_units, Tg / kMinPiece));
+  // sequence index of stream offset x when every sequence is S_max long
+  auto seg_g = [&](long long x) -> int {
+    int sgi = (int)((double)x / (double)S_max);
+    if ((long long)(sgi + 1) * S_max <= x) ++sgi;
+    if ((long long)sgi * S_max > x) --sgi;
+    return sgi;
+  };
+  auto bnd_g = [&](int v) -> long long {
+    if (v <= 0) return 0;
+    if (v >= n_actg) return Tg;
+    const long long x = share(v, Tg, n_actg);
+    const long long st = (long long)seg_g(x) * S_max;
+    const int lx = (((int)(x - st) + kTile / 2) / kTile) * kTile;
+    if (lx < kMinPiece) return st;
+    if (S_max - lx < kMinPiece) return st + S_max;
+    return st + lx;
+  };
+  // Wave 0 first fetches the prefix lengths into LDS (raw, in s_cum) with
+  // dword DMAs, ahead of its share of the guessed tiles, so it can wait for
+  // them alone below; a compiler-visible load would make it wait for the
+  // tiles too.
+  if (wave0 == 0)
+    for (int c0 = 0; c0 < B; c0 += kWave) dma4(prefix_lens + min(c0 + lane0, B - 1), &s_cum[c0]);
+  int g_seg = -1, g_begin = 0, g_end = 0, g_tiles = 0;
+  if (u < n_actg) {
+    const long long xg = bnd_g(u), xge = bnd_g(u + 1);
+    if (xg < xge) {
+      g_seg = seg_g(xg);
+      g_begin = (int)(xg - (long long)g_seg * S_max);
+      g_end = (int)min((long long)S_max, xge - (long long)g_seg * S_max);
+      const size_t off = (size_t)g_seg * S_max * RBYTES;
+      g_tiles = min(NSTAGE - 1, (g_end - g_begin + kTile - 1) / kTile);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) moved |= (alpha[rb] != 1.0f);
-    if (__any(moved)) {
+      for (int i = 0; i < NSTAGE - 1; ++i)
+        if (i < g_tiles) dma_tile(kc + off, vc + off, g_begin + i * kTile, g_end, i, wave0, lane0);
+      load_q(g_seg / Hkv, g_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
+    }
+  }
+
+  // ---- The work stream: the (request, kv head) sequences back to back, in
+  // request-major order; unit v of n_units owns stream tokens
+  // [bnd(v), bnd(v+1)), about an equal share, so ragged prefix lengths do not
+  // leave some workgroups with twice the work of others.  Every workgroup
+  // derives the same boundaries from a table of exclusive prefix sums of the
+  // per-request token counts (0 for a request whose prefix length is
+  // invalid: it is flagged once and skipped).
+  if (wave0 == 0) {
+    // the prefix lengths have landed once only the guessed tiles are in flight
+    switch (g_tiles) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1 * PT>(); break;
+      case 2: if constexpr (NSTAGE > 2) wait_vmcnt<2 * PT>(); break;
+      case 3: if constexpr (NSTAGE > 3) wait_vmcnt<3 * PT>(); break;
+      case 4: if constexpr (NSTAGE > 4) wait_vmcnt<4 * PT>(); break;
+      case 5: if constexpr (NSTAGE > 5) wait_vmcnt<5 * PT>(); break;
+      case 6: if constexpr (NSTAGE > 6) wait_vmcnt<6 * PT>(); break;
+      default: if constexpr (NSTAGE > 7) wait_vmcnt<7 * PT>(); break;
+    }
+    asm volatile("" ::: "memory");
+    int carry = 0;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const int bb = c0 + lane0;
+      int lb = 0;
+      if (bb < B) {
+        const int pb = s_cum[bb];
+        if (pb >= 0 && pb <= S_max - N) lb = pb + N;
+        else if (u == 0 && mt == 0) flag_error(err_word, SPEC_DERR_PREFIX);
+      }
+      int incl = lb;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (lane0 >= d) incl += t;
+      }
+      if (bb < B) s_cum[bb] = carry + incl - lb;
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (lane0 == 0) s_cum[B] = carry;
+  }
+  __syncthreads();
+  const long long T = (long long)Hkv * __builtin_amdgcn_readfirstlane(s_cum[B]);
+  // units of at least kMinPiece tokens, fewer of them if the stream is short
+  const int n_act = (int)max(1ll, min((long long)n_units, T / kMinPiece));
+
+  // The sequence holding stream offset x (0 <= x < T): the last request b with
+  // Hkv * s_cum[b] <= x (searched 64 table entries at a time, first over
+  // every 64th entry), then the kv head within it.
+  auto find = [&](long long x) -> Seg {
+    int blk = 0;
+    const int nblk = B / kWave + 1;                  // blocks of the B + 1 entries
+    if (nblk > 1) {
+      const bool le = lane0 < nblk && (long long)Hkv * s_cum[min(lane0 * kWave, B)] <= x;
+      blk = __popcll(__ballot(le)) - 1;
+    }
+    const int e = min(blk * kWave + lane0, B);
+    const bool le2 = blk * kWave + lane0 <= B && (long long)Hkv * s_cum[e] <= x;
+    const int bsel = blk * kWave + __popcll(__ballot(le2)) - 1;
+    const int cb = __builtin_amdgcn_readfirstlane(s_cum[bsel]);
+    const int lb = __builtin_amdgcn_readfirstlane(s_cum[bsel + 1]) - cb;
+    const long long base = (long long)Hkv * cb;
+    const int kvh = (int)(x - base) / lb;             // x - base < Hkv * S_max < 2^31
+    return Seg{bsel, kvh, lb, base + (long long)kvh * lb};
+  };
+  // Unit v starts at stream offset v*T/n_act, moved to the nearest whole
+  // tile of its sequence, or to the sequence's start or end if that leaves
+  // less than kMinPiece tokens on one side.
+  auto snap = [&](long long x) -> long long {
+    if (x <= 0) return 0;
+    if (x >= T) return T;
+    const Seg sg = find(x);
+    const int lx = (((int)(x - sg.start) + kTile / 2) / kTile) * kTile;
+    if (lx < kMinPiece) return sg.start;
+    if (sg.L - lx < kMinPiece) return sg.start + sg.L;
+    return sg.start + lx;
+  };
+  auto bnd = [&](int v) -> long long { return v <= 0 ? 0 : (v >= n_act ? T : snap(share(v, T, n_act))); };
+  // the unit whose range holds stream offset y (0 <= y < T)
+  auto unit_of = [&](long long y) -> int {
+    int v = (int)min((long long)n_act - 1, (long long)((double)y * (double)n_act / (double)T));
+    while (v > 0 && bnd(v) > y) --v;
+    while (v + 1 < n_act && bnd(v + 1) <= y) ++v;
+    return v;
+  };
+  // partial-result row r of slot sl: every unit has two slots, for its first
+  // and its last piece (the only ones that can cover part of a sequence)
+  auto part_row = [&](int sl, int r) -> size_t { return ((size_t)sl * n_mt + mt) * MT + r; };
+
+  if (u >= n_act) {
+    wait_vmcnt<0>();                                 // guessed tiles must land before the LDS is released
+    return;
+  }
+  const long long u_start = bnd(u);
+  const long long u_end = bnd(u + 1);
+  bool first_piece = true;
+  for (long long x = u_start; x < u_end;) {
+    const Seg sg = find(x);
+    const int b = sg.b, kvh = sg.kvh, L = sg.L;
+    const int P = L - N;
+    const int t_begin = (int)(x - sg.start);
+    const int t_end = (int)min((long long)L, u_end - sg.start);
+    const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+    const bool direct = (t_begin == 0 && t_end == L);   // the whole sequence is in this piece
+    x = sg.start + L;
+    const bool prefetched = first_piece && g_seg == b * Hkv + kvh && g_begin == t_begin && g_end == t_end;
+    if (first_piece && !prefetched && g_seg >= 0) wait_vmcnt<0>();   // discard the guessed tiles
+    first_piece = false;
+
+    __syncthreads();                                 // the previous piece is done with the LDS
+
+    // Thread indices from an opaque copy of threadIdx.x: without it the
+    // compiler hoists every per-lane LDS and global address of the tile loop
+    // out of the piece loop and keeps them live across it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM;
+    const int wt = wave / WM;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int row0 = mt * MT + wm * RB * 16;
+
+    float scale_log2 = sm_scale * kLog2e;
+    float out_scale = 1.0f;
+    if constexpr (KVF == SPEC_FP8_E4M3) {
+      scale_log2 *= k_scale[kvh];
+      out_scale = v_scale[kvh];
+    }
+
+    const size_t head_off = ((size_t)(b * Hkv + kvh) * S_max) * RBYTES;
+    const unsigned char* kbase = kc + head_off;
+    const unsigned char* vbase = vc + head_off;
+
+    auto issue = [&](int st, int i) { dma_tile(kbase, vbase, t_begin + i * kTile, t_end, st, wave, lane); };
+
+    // tiles 0 .. NSTAGE-2 go in flight first; everything up to the wait below
+    // runs in their shadow
+    if (!prefetched) {
+#pragma unroll
+      for (int i = 0; i < NSTAGE - 1; ++i)
+        if (i < ntiles) issue(i, i);
+      load_q(b, kvh, row0, l16, lg);
+    }
+
+    // merge bookkeeping for a piece that covers only part of its sequence:
+    // the units that hold its pieces, and this piece's partial-result slot
+    int u_first = u, npieces = 1, my_slot = 2 * u;
+    bool first_odd = false;
+    if (!direct) {
+      u_first = (u_start <= sg.start) ? u : unit_of(sg.start);
+      const int u_last = (u_end >= sg.start + L) ? u : unit_of(sg.start + L - 1);
+      npieces = u_last - u_first + 1;
+      first_odd = bnd(u_first) < sg.start;           // that unit's piece is its last one
+      my_slot = (u_start >= sg.start) ? 2 * u : 2 * u + 1;
+    }
+    // Complete the Q / mask loads here, once: the compiler cannot count the
+    // DMA instructions, so any wait it places for these loads drains the ring;
+    // inside the tile loop that would happen on every tile.  Here it only waits
+    // for the tiles issued above, which the loop needs first anyway.
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      asm volatile("" ::"v"(anc[rb]));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
+    }
+
+    wait_vmcnt<0>();   // usually already met by the wait above; a wave with no Q rows has none
+
+    f32x4_t oacc[RB][DB];
+    float m_run[RB], l_run[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m_run[rb] = -INFINITY;
+      l_run[rb] = 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+
+    // A operand of S^T = K . Q^T: lane (m = l16, lg) holds K[row][32c + 8lg .. +7]
+    auto read_k = [&](const unsigned char* st, int row, int c) -> bf16x8_t {
+      if constexpr (KVF == SPEC_BF16) {
+        return *reinterpret_cast<const bf16x8_t*>(st + row * RBYTES + (((4 * c + lg) ^ swz<UPR>(row)) << 4));
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(
+            st + row * RBYTES + (((2 * c + (lg >> 1)) ^ swz<UPR>(row)) << 4) + ((lg & 1) << 3));
+        return fp8x8_to_bf16(w.x, w.y);
+      }
+    };
+    // A operand of O^T = V^T . P^T: lane (l16, lg) holds V[32ch + 8lg + k][16db + l16],
+    // k = 0..7.  Transpose reads: a 16-lane group's 8-byte chunks form a vector
+    // E and lane j receives E[j + 16k]; so lanes 4k'..4k'+3 (bf16) or 2k, 2k+1
+    // (fp8) point at the 16 columns of token k.
+    auto read_v = [&](const unsigned char* st, int ch, int db) -> bf16x8_t {
+      if constexpr (KVF == SPEC_BF16) {
+        i16x4_t t[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 32 * ch + 8 * lg + 4 * r + (l16 >> 2);
+          const int u = 2 * db + ((l16 >> 1) & 1);
+          const int off = row * RBYTES + ((u ^ swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
+          t[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(st + off));
+        }
+        // whole-vector bit casts: assembling the operand element by element
+        // from bit-cast shorts is lowered wrongly (half-words get duplicated)
+        const i16x8_t both = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8_t, both);
+      } else {
+        const int row = 32 * ch + 8 * lg + (l16 >> 1);
+        const int off = row * RBYTES + ((db ^ swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
+        const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(st + off));
+        return fp8x8_to_bf16((uint32_t)t[0], (uint32_t)t[1]);
+      }
+    };
+
+    auto compute = [&](int st, int i) {
+      const unsigned char* ks = kst(st);
+      const unsigned char* vs = vst(st);
+      const int t0 = t_begin + i * kTile;
+      // ---- S^T = K . Q^T for this wave's chunks of the tile
+      f32x4_t sacc[RB][CPT][2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
-    }
-    // ---- O^T += V^T . P^T
+        for (int cp = 0; cp < CPT; ++cp)
 #pragma unroll
-    for (int cp = 0; cp < CPT; ++cp) {
+          for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8_t a = read_v(vs, wt * CPT + cp, db);
+      for (int cp = 0; cp < CPT; ++cp) {
+        const int ch = wt * CPT + cp;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][cp], oacc[rb][db], 0, 0, 0);
+        for (int c = 0; c < KC; ++c) {
+#pragma unroll
+          for (int G = 0; G < 2; ++G) {
+            const bf16x8_t a = read_k(ks, 32 * ch + chunk_token(G, l16), c);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
+          }
+        }
       }
-    }
-  };
-
-  // ring: wait for tile i (the tiles after it stay in flight), make it visible
-  // to all waves, refill the stage tile i-1 used, compute tile i
-  int st = 0;
-  for (int i = 0; i < ntiles; ++i) {
-    const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
-    switch (ahead) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1 * PT>(); break;
-      case 2: if constexpr (NSTAGE > 3) wait_vmcnt<2 * PT>(); break;
-      case 3: if constexpr (NSTAGE > 4) wait_vmcnt<3 * PT>(); break;
-      case 4: if constexpr (NSTAGE > 5) wait_vmcnt<4 * PT>(); break;
-      case 5: if constexpr (NSTAGE > 6) wait_vmcnt<5 * PT>(); break;
-      default: if constexpr (NSTAGE > 7) wait_vmcnt<6 * PT>(); break;
-    }
-    wg_barrier();
-    if (i + NSTAGE - 1 < ntiles) issue(st == 0 ? NSTAGE - 1 : st - 1, i + NSTAGE - 1);
-    compute(st, i);
-    st = (st + 1 == NSTAGE) ? 0 : st + 1;
-  }
-
-  // ---- waves that split the tile's tokens combine their states in LDS
-  if constexpr (WT == 2) {
-    // scratch in the ring: O blocks (1 KB per row block and column block)
-    // first, then (m, l) pairs (512 B per row block)
-    constexpr int OBYTES = WM * RB * DB * 1024;
-    static_assert(OBYTES + WM * RB * 512 <= NSTAGE * 2 * TB, "combine scratch");
-    __syncthreads();                                    // all DMA and LDS stage reads are done
-    auto scratch = [&](int off) -> unsigned char* { return smem + off; };
-    auto oslot = [&](int blk, int db) -> f32x4_t* {
-      return reinterpret_cast<f32x4_t*>(scratch((blk * DB + db) * 1024)) + lane;
-    };
-    auto mlslot = [&](int blk) -> float2* {
-      return reinterpret_cast<float2*>(scratch(OBYTES + blk * 512)) + lane;
-    };
-    if (wt == 1) {
+      // ---- mask, online softmax (base 2), P in bf16
+      const bool plain = (t0 + kTile <= min(P, t_end));   // all 64 tokens are prefix, all in the piece
+      bf16x8_t pb[RB][CPT];
+      float alpha[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        // this lane's 8 tokens of chunk cp sit at bits 32*ch + 8*lg .. +7
+        uint32_t vis8[CPT];
+        if (!plain) {
+          const uint64_t vis = tile_visibility(anc[rb], t0, P, t_end);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *oslot(wm * RB + rb, db) = oacc[rb][db];
-        *mlslot(wm * RB + rb) = make_float2(m_run[rb], l_run[rb]);
+          for (int cp = 0; cp < CPT; ++cp) vis8[cp] = (uint32_t)(vis >> (32 * (wt * CPT + cp) + 8 * lg)) & 0xFFu;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int cp = 0; cp < CPT; ++cp)
+#pragma unroll
+          for (int G = 0; G < 2; ++G)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float s = sacc[rb][cp][G][r] * scale_log2;
+              if (!plain) s = ((vis8[cp] >> (4 * G + r)) & 1u) ? s : -INFINITY;
+              sacc[rb][cp][G][r] = s;
+              mx = fmaxf(mx, s);
+            }
+        mx = row4_max(mx);
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        alpha[rb] = fast_exp2(m_run[rb] - m_use);
+        m_run[rb] = m_new;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int cp = 0; cp < CPT; ++cp)
+#pragma unroll
+          for (int G = 0; G < 2; ++G)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = fast_exp2(sacc[rb][cp][G][r] - m_use);
+              lsum += p;
+              pb[rb][cp][4 * G + r] = (__bf16)p;
+            }
+        l_run[rb] = l_run[rb] * alpha[rb] + lsum;
       }
+      // rescale O only when some row's running max moved (alpha != 1): after the
+      // first tiles that is rare, and skipping a multiply by exactly 1 changes
+      // nothing
+      bool moved = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) moved |= (alpha[rb] != 1.0f);
+      if (__any(moved)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
+      }
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int cp = 0; cp < CPT; ++cp) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8_t a = read_v(vs, wt * CPT + cp, db);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][cp], oacc[rb][db], 0, 0, 0);
+        }
+      }
+    };
+
+    // ring: wait for tile i (the tiles after it stay in flight), make it visible
+    // to all waves, refill the stage tile i-1 used, compute tile i
+    int st = 0;
+    for (int i = 0; i < ntiles; ++i) {
+      const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
+      switch (ahead) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1 * PT>(); break;
+        case 2: if constexpr (NSTAGE > 3) wait_vmcnt<2 * PT>(); break;
+        case 3: if constexpr (NSTAGE > 4) wait_vmcnt<3 * PT>(); break;
+        case 4: if constexpr (NSTAGE > 5) wait_vmcnt<4 * PT>(); break;
+        case 5: if constexpr (NSTAGE > 6) wait_vmcnt<5 * PT>(); break;
+        default: if constexpr (NSTAGE > 7) wait_vmcnt<6 * PT>(); break;
+      }
+      wg_barrier();
+      if (i + NSTAGE - 1 < ntiles) issue(st == 0 ? NSTAGE - 1 : st - 1, i + NSTAGE - 1);
+      compute(st, i);
+      st = (st + 1 == NSTAGE) ? 0 : st + 1;
+    }
+
+    // ---- waves that split the tile's tokens combine their states in LDS
+    if constexpr (WT == 2) {
+      // scratch in the ring: O blocks (1 KB per row block and column block)
+      // first, then (m, l) pairs (512 B per row block)
+      constexpr int OBYTES = WM * RB * DB * 1024;
+      static_assert(OBYTES + WM * RB * 512 <= NSTAGE * 2 * TB, "combine scratch");
+      __syncthreads();                                    // all DMA and LDS stage reads are done
+      auto scratch = [&](int off) -> unsigned char* { return smem + off; };
+      auto oslot = [&](int blk, int db) -> f32x4_t* {
+        return reinterpret_cast<f32x4_t*>(scratch((blk * DB + db) * 1024)) + lane;
+      };
+      auto mlslot = [&](int blk) -> float2* {
+        return reinterpret_cast<float2*>(scratch(OBYTES + blk * 512)) + lane;
+      };
+      if (wt == 1) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) *oslot(wm * RB + rb, db) = oacc[rb][db];
+          *mlslot(wm * RB + rb) = make_float2(m_run[rb], l_run[rb]);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (wt == 1) break;                              // combined state lives in the wt == 0 waves
+        const float2 o = *mlslot(wm * RB + rb);
+        const float m_new = fmaxf(m_run[rb], o.x);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float a0 = fast_exp2(m_run[rb] - m_use), a1 = fast_exp2(o.x - m_use);
+        m_run[rb] = m_new;
+        l_run[rb] = l_run[rb] * a0 + o.y * a1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] = oacc[rb][db] * a0 + *oslot(wm * RB + rb, db) * a1;
+      }
+    }
+
+
+    // ---- epilogue: lane holds O^T[16db + 4lg + r][row l16]
+    if (direct) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (wt != 0) break;                          // the token-split partner waves hold no result
+        const float l = row4_sum(l_run[rb]);
+        const int row = row0 + rb * 16 + l16;
+        if (row >= M) continue;
+        const int i = row / g, hl = row % g;
+        const float inv = out_scale / l;
+        __bf16* op = out + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D + 4 * lg;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          bf16x4_t v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)(oacc[rb][db][r] * inv);
+          *reinterpret_cast<bf16x4_t*>(op + 16 * db) = v;
+        }
+        if (lse && lg == 0) lse[(size_t)(b * N + i) * Hq + kvh * g + hl] = (m_run[rb] + log2f(l)) * kLn2;
+      }
+    } else if (wt == 0) {
+      // Partials go out in the lanes' own order (16 B per lane, 1 KB per wave
+      // store, fully coalesced): chunk ((wm*RB + rb)*DB + db)*64 + lane of the
+      // slot's O block, and (m, l) of row (wm*RB + rb)*16 + l16.  They are
+      // read by another workgroup of this launch, maybe on another XCD, so
+      // the stores are device scope.
+      const __amdgpu_buffer_rsrc_t ro = dev_rsrc(part_o + part_row(my_slot, 0) * D, MT * D * 4);
+      const __amdgpu_buffer_rsrc_t rm = dev_rsrc(part_ml + part_row(my_slot, 0), MT * 8);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l = row4_sum(l_run[rb]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          store_dev4(ro, (((wm * RB + rb) * DB + db) * kWave + lane) * 16, oacc[rb][db] * out_scale);
+        if (lg == 0) store_dev2(rm, ((wm * RB + rb) * 16 + l16) * 8, m_run[rb], l);
+      }
+    }
+    if (direct) continue;
+
+    // ---- merge, fused: the last workgroup to finish a piece of this
+    // (request, kv head, M-tile) combines every piece's partial in unit order,
+    // so the result does not depend on which workgroup that is.  The per-
+    // sequence counter lives in the workspace; it starts at zero and the
+    // merging workgroup resets it, leaving the workspace ready for the next
+    // call.
+    wait_vmcnt<0>();                                 // this lane's partial stores have completed
+    __syncthreads();                                 // ... for every lane
+    uint32_t* cnt = counters + (size_t)(b * Hkv + kvh) * n_mt + mt;
+    if (tid == 0) {
+      const uint32_t seen = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      s_last = (seen == (uint32_t)(npieces - 1)) ? 1u : 0u;
     }
     __syncthreads();
+    if (!s_last) continue;
+    // Every load of the merge is independent and each costs a trip to the
+    // device coherence point, so they are issued together: a thread owns IPT
+    // 16-byte chunks of the lane-ordered partial block and loads, per round,
+    // BATCH chunks x SG pieces plus each piece's (m, l) for the chunk's row;
+    // rounds over further pieces rescale the running sums (online softmax
+    // over the pieces).
+    constexpr int NT = NW * kWave;
+    constexpr int NCHUNK = MT * D / 4;                 // 16-byte chunks per block
+    static_assert(NCHUNK % NT == 0, "merge chunks split evenly over the threads");
+    constexpr int IPT = NCHUNK / NT;                   // chunks per thread
+    constexpr int BATCH = IPT < 8 ? IPT : 8;
+    constexpr int SG = 16 / BATCH;                     // pieces per load round
+    static_assert(IPT % BATCH == 0, "merge batches");
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (wt == 1) break;                              // combined state lives in the wt == 0 waves
-      const float2 o = *mlslot(wm * RB + rb);
-      const float m_new = fmaxf(m_run[rb], o.x);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float a0 = fast_exp2(m_run[rb] - m_use), a1 = fast_exp2(o.x - m_use);
-      m_run[rb] = m_new;
-      l_run[rb] = l_run[rb] * a0 + o.y * a1;
+    for (int k0 = 0; k0 < IPT; k0 += BATCH) {
+      float m[BATCH], den[BATCH];
+      f32x4_t acc[BATCH];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] = oacc[rb][db] * a0 + *oslot(wm * RB + rb, db) * a1;
-    }
-  }
-
-  // ---- epilogue: lane holds O^T[16db + 4lg + r][row l16]
-  const size_t unit_rows = (size_t)(b * Hkv + kvh) * n_splits * (size_t)(n_mt * MT);
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (wt != 0) break;                              // the token-split partner waves hold no result
-    const float l = row4_sum(l_run[rb]);
-    const int row = row0 + rb * 16 + l16;
-    if (row >= M) continue;
-    const int i = row / g, hl = row % g;
-    if (direct) {
-      const float inv = out_scale / l;
-      __bf16* op = out + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D + 4 * lg;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        bf16x4_t v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(oacc[rb][db][r] * inv);
-        *reinterpret_cast<bf16x4_t*>(op + 16 * db) = v;
+      for (int k = 0; k < BATCH; ++k) {
+        m[k] = -INFINITY;
+        den[k] = 0.f;
+        acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      if (lse && lg == 0) lse[(size_t)(b * N + i) * Hq + kvh * g + hl] = (m_run[rb] + log2f(l)) * kLn2;
-    } else {
-      // partials are read by another workgroup (maybe on another XCD) in this
-      // same launch: device-scope stores, written through past this XCD's L2
-      const size_t pidx = unit_rows + (size_t)split * (n_mt * MT) + row;
-      float* po = part_o + pidx * D + 4 * lg;
+      for (int s0 = 0; s0 < npieces; s0 += SG) {
+        float2 ml[SG][BATCH];
+        f32x4_t o[SG][BATCH];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4_t v = oacc[rb][db] * out_scale;
-        store_dev(po + 16 * db, v[0], v[1]);
-        store_dev(po + 16 * db + 2, v[2], v[3]);
-      }
-      if (lg == 0) store_dev(reinterpret_cast<float*>(part_ml + pidx), m_run[rb], l);
-    }
-  }
-  if (direct) return;
-
-  // ---- split merge, fused: the last workgroup of this (request, kv head,
-  // M-tile) to finish combines every split's partial, in split order, so the
-  // result does not depend on which workgroup that is.  The per-unit counter
-  // lives in the workspace; it starts at zero and the merging workgroup
-  // resets it, leaving the workspace ready for the next call.
-  wait_vmcnt<0>();                                   // this lane's partial stores have completed
-  __syncthreads();                                   // ... for every lane; every wave is done with the ring
-  uint32_t* s_last = reinterpret_cast<uint32_t*>(smem);
-  const int ns = (L + split_len - 1) / split_len;
-  uint32_t* cnt = counters + (size_t)(b * Hkv + kvh) * n_mt + mt;
-  if (tid == 0) {
-    const uint32_t seen = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    *s_last = (seen == (uint32_t)(ns - 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!*s_last) return;
-  // Every load of the merge is independent and each costs a trip to the
-  // device coherence point, so they are issued together: a thread owns IPT
-  // (row, column quad) items and loads, per round, BATCH items x SG splits of
-  // partial O plus each split's (m, l) for the item's row; rounds over further
-  // splits rescale the running sums (online softmax over the splits).
-  constexpr int NT = NW * kWave;
-  constexpr int QPR = D / 4;                         // column quads per row
-  static_assert((MT * QPR) % NT == 0, "merge items split evenly over the threads");
-  constexpr int IPT = MT * QPR / NT;                 // items per thread
-  constexpr int BATCH = IPT < 8 ? IPT : 8;
-  constexpr int SG = 16 / BATCH;                     // splits per load round
-  static_assert(IPT % BATCH == 0, "merge batches");
-  const size_t split_rows = (size_t)n_mt * MT;       // partial rows per split
-  const size_t tile_base = unit_rows + (size_t)mt * MT;
+        for (int j = 0; j < SG; ++j) {
+          const int sp = s0 + j;
+          const int sl = 2 * (u_first + sp) + ((sp == 0 && first_odd) ? 1 : 0);
+          const __amdgpu_buffer_rsrc_t ro = dev_rsrc(part_o + part_row(sl, 0) * D, MT * D * 4);
+          const __amdgpu_buffer_rsrc_t rm = dev_rsrc(part_ml + part_row(sl, 0), MT * 8);
 #pragma unroll
-  for (int k0 = 0; k0 < IPT; k0 += BATCH) {
-    float m[BATCH], den[BATCH];
-    f32x4_t acc[BATCH];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      m[k] = -INFINITY;
-      den[k] = 0.f;
-      acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int s0 = 0; s0 < ns; s0 += SG) {
-      float2 ml[SG][BATCH];
-      f32x4_t o[SG][BATCH];
-#pragma unroll
-      for (int j = 0; j < SG; ++j)
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
-          const int item = tid + (k0 + k) * NT;
-          const int r = item / QPR, qd = item % QPR;
-          ml[j][k] = make_float2(-INFINITY, 0.f);
-          o[j][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (s0 + j < ns && mt * MT + r < M) {
-            const size_t prow = tile_base + (size_t)(s0 + j) * split_rows + r;
-            ml[j][k] = load_dev(reinterpret_cast<const float*>(part_ml + prow));
-            const float2 lo = load_dev(part_o + prow * D + 4 * qd);
-            const float2 hi = load_dev(part_o + prow * D + 4 * qd + 2);
-            o[j][k] = f32x4_t{lo.x, lo.y, hi.x, hi.y};
+          for (int k = 0; k < BATCH; ++k) {
+            const int c = tid + (k0 + k) * NT;
+            const int rloc = (c / (DB * kWave)) * 16 + (c & 15);
+            ml[j][k] = make_float2(-INFINITY, 0.f);
+            o[j][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (sp < npieces) {
+              ml[j][k] = load_dev2(rm, rloc * 8);
+              o[j][k] = load_dev4(ro, c * 16);
+            }
           }
         }
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        float mc = m[k];
+        for (int k = 0; k < BATCH; ++k) {
+          float mc = m[k];
 #pragma unroll
-        for (int j = 0; j < SG; ++j) mc = fmaxf(mc, ml[j][k].x);
-        const float m_use = (mc == -INFINITY) ? 0.f : mc;
-        const float a = fast_exp2(m[k] - m_use);
-        den[k] *= a;
-        acc[k] *= a;
+          for (int j = 0; j < SG; ++j) mc = fmaxf(mc, ml[j][k].x);
+          const float m_use = (mc == -INFINITY) ? 0.f : mc;
+          const float a = fast_exp2(m[k] - m_use);
+          den[k] *= a;
+          acc[k] *= a;
 #pragma unroll
-        for (int j = 0; j < SG; ++j) {
-          const float w = fast_exp2(ml[j][k].x - m_use);
-          den[k] += w * ml[j][k].y;
-          acc[k] += w * o[j][k];
+          for (int j = 0; j < SG; ++j) {
+            const float w = fast_exp2(ml[j][k].x - m_use);
+            den[k] += w * ml[j][k].y;
+            acc[k] += w * o[j][k];
+          }
+          m[k] = mc;
         }
-        m[k] = mc;
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int c = tid + (k0 + k) * NT;
+        const int ln = c & 63;
+        const int db = (c / kWave) % DB;
+        const int row = mt * MT + (c / (DB * kWave)) * 16 + (ln & 15);
+        if (row >= M) continue;
+        const int i = row / g, hl = row % g;
+        const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
+        const float inv = 1.0f / den[k];
+        bf16x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[k][e] * inv);
+        *reinterpret_cast<bf16x4_t*>(out + orow * D + 16 * db + 4 * (ln >> 4)) = v;
+        if (lse && db == 0 && ln < 16) lse[orow] = (m[k] + log2f(den[k])) * kLn2;
       }
     }
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int item = tid + (k0 + k) * NT;
-      const int r = item / QPR, qd = item % QPR;
-      const int row = mt * MT + r;
-      if (row >= M) continue;
-      const int i = row / g, hl = row % g;
-      const size_t orow = (size_t)(b * N + i) * Hq + kvh * g + hl;
-      const float inv = 1.0f / den[k];
-      bf16x4_t v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[k][e] * inv);
-      *reinterpret_cast<bf16x4_t*>(out + orow * D + 4 * qd) = v;
-      if (lse && qd == 0) lse[orow] = (m[k] + log2f(den[k])) * kLn2;
-    }
+    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  wait_vmcnt<0>();   // a unit whose range came out empty still has its guessed tiles in flight
 }
 
 // fp32 Q/K/V: one wave per (request, node, head), exact fp32 arithmetic on the
@@ -744,29 +941,33 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
 
 struct AttnPlan {
   int rb, wm, wt, nstage, mt_rows, n_mt, M_pad;
-  int split_len, n_splits;
+  int n_units;
   size_t ws_bytes;
 };
+
+// Bytes of LDS a workgroup holds besides its K/V ring: the request-length
+// table and the merge flag.
+constexpr int kTableBytes = 4 * (1024 + 1) + 4;
 
 // Rows per workgroup follow the packed M = g*N.  Small M (<= 32) lets the
 // waves also split each tile's tokens (a 3-stage K/V ring, one workgroup per
 // CU); larger M splits rows over the waves (a 2-stage ring, two workgroups per
-// CU, so two waves share each SIMD).  KV splits are then added until the grid
-// has about one workgroup per resident slot (256 CUs), never below 256
-// tokens per split so the partial (O, m, l) traffic stays small against the
-// split's K/V bytes.  The split plan does not depend on the cached dtype, so
-// one workspace size serves every format.
-static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, int kv_bytes, AttnPlan* p) {
-  (void)kv_bytes;
-  if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < Hkv || Hq % Hkv) return false;
+// CU, so two waves share each SIMD).  The work stream is then cut into about
+// one unit per resident workgroup slot (256 CUs), each unit for all M-tiles.
+// The plan does not depend on the cached dtype, so one workspace size serves
+// every format: two partial-result slots per unit and M-tile, and one counter
+// per (request, kv head, M-tile).
+static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan* p) {
+  if (B < 1 || B > 1024 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < Hkv || Hq % Hkv) return false;
   if (D != 64 && D != 128) return false;
   if (S_max < N) return false;
+  if ((long long)B * S_max >= (1ll << 31) || (long long)Hkv * S_max >= (1ll << 31)) return false;
   const int M = (Hq / Hkv) * N;
   if (M <= 32) { p->rb = 1; p->wm = 2; p->wt = 2; p->nstage = 3; }
   else if (M <= 64) { p->rb = 2; p->wm = 2; p->wt = 1; p->nstage = 2; }
   else { p->rb = 2; p->wm = 4; p->wt = 1; p->nstage = 2; }
-  const int stage_bytes = 2 * kTile * D * 2;               // bf16 sizing for the split policy
-  const long long per_cu = std::max(1, std::min(2, (160 * 1024) / (p->nstage * stage_bytes)));
+  const int lds_bf16 = p->nstage * 2 * kTile * D * 2 + kTableBytes;
+  const long long per_cu = std::max(1, std::min(2, (160 * 1024) / lds_bf16));
   long long target_wgs = 256 * per_cu;
 #ifdef SPEC_PLAN_HOOK
   SPEC_PLAN_HOOK(p, M, target_wgs);
@@ -774,19 +975,10 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, int kv_by
   p->mt_rows = p->rb * p->wm * 16;
   p->n_mt = (M + p->mt_rows - 1) / p->mt_rows;
   p->M_pad = p->n_mt * p->mt_rows;
-  const long long units = (long long)B * Hkv * p->n_mt;
-  const int want = (int)std::max<long long>(1, (target_wgs + units - 1) / units);
-  int split_len = (S_max + want - 1) / want;
-  split_len = ((split_len + kTile - 1) / kTile) * kTile;
-  if (split_len < 256) split_len = 256;
-  p->split_len = split_len;
-  p->n_splits = (S_max + split_len - 1) / split_len;
-  p->ws_bytes = 0;
-  if (p->n_splits > 1) {
-    const size_t rows = (size_t)B * Hkv * p->n_splits * p->M_pad;
-    const size_t counters = (size_t)B * Hkv * p->n_mt;
-    p->ws_bytes = rows * (size_t)D * sizeof(float) + rows * sizeof(float2) + counters * sizeof(uint32_t);
-  }
+  p->n_units = (int)std::max<long long>(1, target_wgs / p->n_mt);
+  const size_t rows = (size_t)2 * p->n_units * p->M_pad;
+  const size_t counters = (size_t)B * Hkv * p->n_mt;
+  p->ws_bytes = rows * (size_t)D * sizeof(float) + rows * sizeof(float2) + counters * sizeof(uint32_t);
   return true;
 }
 
@@ -796,13 +988,12 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
                          float* lse, float* po, float2* pml, uint32_t* cnt, uint32_t* err,
                          hipStream_t st) {
-  const int units = B * Hkv * pl.n_splits;
-  const int units_pad = ((units + 7) / 8) * 8;
+  const int units_pad = ((pl.n_units + 7) / 8) * 8;
   const unsigned grid = (unsigned)units_pad * (unsigned)pl.n_mt;
   hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS>), dim3(grid), dim3(WM * WT * kWave),
                      0, st, static_cast<const __bf16*>(q), static_cast<const unsigned char*>(k),
                      static_cast<const unsigned char*>(v), ks, vs, pre, anc, B, N, Hq, Hkv, S_max,
-                     sm_scale, pl.split_len, pl.n_splits, pl.n_mt, static_cast<__bf16*>(out), lse,
+                     sm_scale, pl.n_units, pl.n_mt, static_cast<__bf16*>(out), lse,
                      po, pml, cnt, err);
 }
 
@@ -814,9 +1005,9 @@ constexpr bool split_fits() {
   constexpr int TB = kTile * D * ((KVF == SPEC_BF16) ? 2 : 1);
   constexpr int NW = WM * WT;
   constexpr int NLOAD = TB / 1024;
-  if (NS * 2 * TB > 160 * 1024) return false;
+  if (NS * 2 * TB + kTableBytes > 160 * 1024) return false;
   if (NLOAD % NW != 0) return false;
-  if ((NS - 2) * 2 * (NLOAD / NW) >= 64) return false;
+  if ((NS - 1) * 2 * (NLOAD / NW) >= 64) return false;   // a full ring start fits the vmcnt counter
   if (WT == 2 && WM * RB * (D / 16) * 1024 + WM * RB * 512 > NS * 2 * TB) return false;
   return true;
 }
@@ -851,7 +1042,7 @@ using namespace spectree;
 
 extern "C" size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max) {
   AttnPlan pl;
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, 2, &pl)) return 0;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return 0;
   return pl.ws_bytes;
 }
 
@@ -872,8 +1063,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   if (!f32 && !bf16 && !fp8) return SPEC_ERR_DTYPE;
   if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
   AttnPlan pl;
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, f32 ? 4 : (bf16 ? 2 : 1), &pl)) return SPEC_ERR_SHAPE;
-  if ((long long)B * Hkv * pl.n_splits * pl.n_mt >= (1ll << 31)) return SPEC_ERR_SHAPE;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return SPEC_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return SPEC_ERR_ALIGN;
 
@@ -899,7 +1089,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
     if (!workspace) return SPEC_ERR_WORKSPACE;
     if (workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
-    const size_t rows = (size_t)B * Hkv * pl.n_splits * pl.M_pad;
+    const size_t rows = (size_t)2 * pl.n_units * pl.M_pad;
     po = static_cast<float*>(workspace);
     pml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + rows * D * sizeof(float));
     cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + rows * D * sizeof(float) +
