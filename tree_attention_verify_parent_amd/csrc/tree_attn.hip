@@ -155,15 +155,18 @@ __device__ __forceinline__ uint64_t tile_visibility(uint64_t anc, int t0, int P,
 // Issued as inline assembly so the compiler's wait-count pass does not treat
 // every later LDS read as depending on every DMA in flight; the kernel orders
 // them itself with s_waitcnt vmcnt(N) before each barrier.
-__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds_ptr) {
-  const uint32_t lds_addr = (uint32_t)(size_t)(lds_void_t*)lds_ptr;
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
                : "memory", "m0");
 }
+// LDS byte address of a __shared__ object (the cast of the object itself
+// folds to a constant; callers add byte offsets to it)
+#define LDS_ADDR(obj) ((uint32_t)(size_t)(lds_void_t*)(obj))
 
 // The same for 4 bytes per lane: lane l's dword lands at lds_addr + 4*l.
-__device__ __forceinline__ void dma4(const void* gptr, const void* lds_ptr) {
-  const uint32_t lds_addr = (uint32_t)(size_t)(lds_void_t*)lds_ptr;
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr)
                : "memory", "m0");
 }
@@ -209,7 +212,7 @@ void tree_attn_split_kernel(
     const unsigned char* __restrict__ vc, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ prefix_lens,
     const uint64_t* __restrict__ anc_mask, int B, int N, int Hq, int Hkv, int S_max,
-    float sm_scale, int n_units, int n_mt, __bf16* __restrict__ out,
+    float sm_scale, int split_len, int n_splits, int n_units, int n_mt, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
     uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word) {
   static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
@@ -238,6 +241,11 @@ void tree_attn_split_kernel(
   auto kst = [&](int st) -> unsigned char* { return smem + (2 * st) * TB; };
   auto vst = [&](int st) -> unsigned char* { return smem + (2 * st + 1) * TB; };
 
+  // Every kernel argument at once: left to first use, each would be a scalar
+  // load with its own wait, and several of them stand before the first DMA.
+  asm volatile("" ::"s"(q), "s"(kc), "s"(vc), "s"(prefix_lens), "s"(anc_mask), "s"(B), "s"(N), "s"(Hq),
+               "s"(Hkv), "s"(S_max), "s"(split_len), "s"(n_splits), "s"(n_units), "s"(n_mt));
+
   // ---- work unit, XCD-aware: workgroups are dispatched round-robin over the
   // 8 XCDs, so the M-tiles of one unit get ids congruent mod 8 and share that
   // XCD's L2.
@@ -245,10 +253,10 @@ void tree_attn_split_kernel(
   const int per = 8 * n_mt;
   const int mt = (id % per) / 8;
   const int u = (id / per) * 8 + (id % 8);
-  if (u >= n_units) return;
+  const int n_fixed = B * Hkv * n_splits;
+  if (u >= max(n_fixed, n_units)) return;
   const int g = Hq / Hkv;
   const int M = g * N;
-
   const int lane0 = threadIdx.x & 63;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -265,8 +273,8 @@ void tree_attn_split_kernel(
       const int unit16 = (lane % UPR) ^ swz<UPR>(row);
       const size_t c = (size_t)min(t0 + row, t_end - 1);
       const size_t goff = c * RBYTES + unit16 * 16;
-      dma16(kbase + goff, kst(st) + j * 1024);
-      dma16(vbase + goff, vst(st) + j * 1024);
+      dma16(kbase + goff, LDS_ADDR(smem) + (2 * st) * TB + j * 1024);
+      dma16(vbase + goff, LDS_ADDR(smem) + (2 * st + 1) * TB + j * 1024);
     }
   };
 
@@ -292,77 +300,50 @@ void tree_attn_split_kernel(
     }
   };
 
-  // ---- Speculative start.  The lengths are not known until prefix_lens has
-  // been read and summed, which takes microseconds; in the common case where
-  // every request fills its cache (P_b = S_max - N) the unit's first piece is
-  // already known from the sizes alone, so its first tiles are fetched now.
-  // If the real lengths give another first piece, those tiles are drained and
-  // discarded (they only read in-bounds cache rows).
-  // Unit v's nominal start v*T/n (any deterministic monotone rule serves: all
-  // workgroups evaluate the same one), in fp64 rather than a slow 64-bit
-  // integer division.
-  auto share = [](int v, long long T, int n) -> long long { return (long long)((double)v * (double)T / (double)n); };
-  const long long Tg = (long long)B * Hkv * S_max;
-  const int n_actg = (int)max(1ll, min((long long)n_units, Tg / kMinPiece));
-  // sequence index of stream offset x when every sequence is S_max long
-  auto seg_g = [&](long long x) -> int {
-    int sgi = (int)((double)x / (double)S_max);
-    if ((long long)(sgi + 1) * S_max <= x) ++sgi;
-    if ((long long)sgi * S_max > x) --sgi;
-    return sgi;
-  };
-  auto bnd_g = [&](int v) -> long long {
-    if (v <= 0) return 0;
-    if (v >= n_actg) return Tg;
-    const long long x = share(v, Tg, n_actg);
-    const long long st = (long long)seg_g(x) * S_max;
-    const int lx = (((int)(x - st) + kTile / 2) / kTile) * kTile;
-    if (lx < kMinPiece) return st;
-    if (S_max - lx < kMinPiece) return st + S_max;
-    return st + lx;
-  };
-  // Wave 0 first fetches the prefix lengths into LDS (raw, in s_cum) with
-  // dword DMAs, ahead of its share of the guessed tiles, so it can wait for
-  // them alone below; a compiler-visible load would make it wait for the
-  // tiles too.
+  // ---- Two schedules.  Fixed: unit u < n_fixed is split u % n_splits
+  // (split_len tokens) of sequence u / n_splits.  When every request fills its
+  // cache (P_b = S_max - N) that divides the work evenly and needs nothing but
+  // the sizes, so the unit's first tiles and Q rows are fetched at once, before
+  // the prefix lengths are known.  Balanced (below): for ragged lengths the
+  // units instead take equal shares of the actual tokens.  Every workgroup
+  // reads all prefix lengths and so makes the same choice.
+  //
+  // Wave 0 fetches the prefix lengths into LDS (raw, in s_cum) with dword
+  // DMAs before anything else, so they land ahead of the tiles.
   if (wave0 == 0)
-    for (int c0 = 0; c0 < B; c0 += kWave) dma4(prefix_lens + min(c0 + lane0, B - 1), &s_cum[c0]);
-  int g_seg = -1, g_begin = 0, g_end = 0, g_tiles = 0;
-  if (u < n_actg) {
-    const long long xg = bnd_g(u), xge = bnd_g(u + 1);
-    if (xg < xge) {
-      g_seg = seg_g(xg);
-      g_begin = (int)(xg - (long long)g_seg * S_max);
-      g_end = (int)min((long long)S_max, xge - (long long)g_seg * S_max);
-      const size_t off = (size_t)g_seg * S_max * RBYTES;
-      g_tiles = min(NSTAGE - 1, (g_end - g_begin + kTile - 1) / kTile);
+    for (int c0 = 0; c0 < B; c0 += kWave) dma4(prefix_lens + min(c0 + lane0, B - 1), LDS_ADDR(s_cum) + 4 * c0);
+  int f_seg = -1, f_begin = 0, f_end = 0;
+  if (u < n_fixed) {
+    f_seg = u / n_splits;
+    f_begin = (u % n_splits) * split_len;
+    f_end = min(S_max, f_begin + split_len);
+    const size_t off = (size_t)f_seg * S_max * RBYTES;
+    const int nt = (f_end - f_begin + kTile - 1) / kTile;
 #pragma unroll
-      for (int i = 0; i < NSTAGE - 1; ++i)
-        if (i < g_tiles) dma_tile(kc + off, vc + off, g_begin + i * kTile, g_end, i, wave0, lane0);
-      load_q(g_seg / Hkv, g_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
-    }
+    for (int i = 0; i < NSTAGE - 1; ++i)
+      if (i < nt) dma_tile(kc + off, vc + off, f_begin + i * kTile, f_end, i, wave0, lane0);
+    load_q(f_seg / Hkv, f_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
   }
+  // whether every raw prefix length in s_cum is S_max - N (after a barrier
+  // that follows wave 0's wait for its DMAs)
+  auto uniform = [&]() -> bool {
+    bool bad = false;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const int bb = c0 + lane0;
+      bad = bad || (bb < B && s_cum[bb] != S_max - N);
+    }
+    return __ballot(bad) == 0;
+  };
 
   // ---- The work stream: the (request, kv head) sequences back to back, in
-  // request-major order; unit v of n_units owns stream tokens
-  // [bnd(v), bnd(v+1)), about an equal share, so ragged prefix lengths do not
-  // leave some workgroups with twice the work of others.  Every workgroup
-  // derives the same boundaries from a table of exclusive prefix sums of the
+  // request-major order; unit v of n_act owns stream tokens [bnd(v),
+  // bnd(v+1)), about an equal share, so ragged prefix lengths do not leave
+  // some workgroups with twice the work of others.  Every workgroup derives
+  // the same boundaries from a table of exclusive prefix sums of the
   // per-request token counts (0 for a request whose prefix length is
-  // invalid: it is flagged once and skipped).
-  if (wave0 == 0) {
-    // the prefix lengths have landed once only the guessed tiles are in flight
-    switch (g_tiles) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1 * PT>(); break;
-      case 2: if constexpr (NSTAGE > 2) wait_vmcnt<2 * PT>(); break;
-      case 3: if constexpr (NSTAGE > 3) wait_vmcnt<3 * PT>(); break;
-      case 4: if constexpr (NSTAGE > 4) wait_vmcnt<4 * PT>(); break;
-      case 5: if constexpr (NSTAGE > 5) wait_vmcnt<5 * PT>(); break;
-      case 6: if constexpr (NSTAGE > 6) wait_vmcnt<6 * PT>(); break;
-      default: if constexpr (NSTAGE > 7) wait_vmcnt<7 * PT>(); break;
-    }
-    asm volatile("" ::: "memory");
+  // invalid: it is flagged once and skipped).  Wave 0 builds the table in
+  // place from the raw prefix lengths in s_cum.
+  auto build_table = [&]() {
     int carry = 0;
     for (int c0 = 0; c0 < B; c0 += kWave) {
       const int bb = c0 + lane0;
@@ -382,11 +363,21 @@ void tree_attn_split_kernel(
       carry += __shfl(incl, kWave - 1);
     }
     if (lane0 == 0) s_cum[B] = carry;
-  }
-  __syncthreads();
-  const long long T = (long long)Hkv * __builtin_amdgcn_readfirstlane(s_cum[B]);
-  // units of at least kMinPiece tokens, fewer of them if the stream is short
-  const int n_act = (int)max(1ll, min((long long)n_units, T / kMinPiece));
+    __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the table is in LDS before the next barrier
+  };
+  // Unit v's nominal start, about v*T/n: any deterministic rule that is
+  // monotone in v serves (every workgroup evaluates the same one, and the
+  // result is snapped to a tile anyway), so it is computed in fp32, not with
+  // slow 64-bit integer or fp64 division.
+  auto share = [](int v, long long T, int n) -> long long {
+    return (long long)((float)v * ((float)T * __builtin_amdgcn_rcpf((float)n)));
+  };
+  long long T = 0;
+  int n_act = 1;
+  auto set_schedule = [&]() {
+    T = (long long)Hkv * __builtin_amdgcn_readfirstlane(s_cum[B]);
+    n_act = (int)max(1ll, min((long long)n_units, T / kMinPiece));   // units of >= kMinPiece tokens
+  };
 
   // The sequence holding stream offset x (0 <= x < T): the last request b with
   // Hkv * s_cum[b] <= x (searched 64 table entries at a time, first over
@@ -422,7 +413,7 @@ void tree_attn_split_kernel(
   auto bnd = [&](int v) -> long long { return v <= 0 ? 0 : (v >= n_act ? T : snap(share(v, T, n_act))); };
   // the unit whose range holds stream offset y (0 <= y < T)
   auto unit_of = [&](long long y) -> int {
-    int v = (int)min((long long)n_act - 1, (long long)((double)y * (double)n_act / (double)T));
+    int v = (int)min((long long)n_act - 1, (long long)((float)y * ((float)n_act * __builtin_amdgcn_rcpf((float)T))));
     while (v > 0 && bnd(v) > y) --v;
     while (v + 1 < n_act && bnd(v + 1) <= y) ++v;
     return v;
@@ -431,25 +422,49 @@ void tree_attn_split_kernel(
   // and its last piece (the only ones that can cover part of a sequence)
   auto part_row = [&](int sl, int r) -> size_t { return ((size_t)sl * n_mt + mt) * MT + r; };
 
-  if (u >= n_act) {
-    wait_vmcnt<0>();                                 // guessed tiles must land before the LDS is released
-    return;
+  long long u_start = 0, u_end = 0;
+  // leave the fixed schedule: the table, then this unit's balanced range
+  auto to_balanced = [&]() -> bool {
+    if (wave0 == 0) build_table();
+    __syncthreads();
+    set_schedule();
+    if (u >= n_act) return false;
+    u_start = bnd(u);
+    u_end = bnd(u + 1);
+    return true;
+  };
+
+  bool fixed = f_seg >= 0;                           // running a fixed split, not yet checked
+  if (!fixed) {
+    // no fixed split for this unit: it only has work under the balanced schedule
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (uniform() || !to_balanced()) return;
   }
-  const long long u_start = bnd(u);
-  const long long u_end = bnd(u + 1);
-  bool first_piece = true;
-  for (long long x = u_start; x < u_end;) {
-    const Seg sg = find(x);
-    const int b = sg.b, kvh = sg.kvh, L = sg.L;
+  for (long long x = fixed ? 0 : u_start; x < (fixed ? 1 : u_end);) {
+    int b, kvh, L, t_begin, t_end;
+    long long seg_start;
+    if (fixed) {
+      b = f_seg / Hkv;
+      kvh = f_seg % Hkv;
+      L = S_max;
+      seg_start = 0;
+      t_begin = f_begin;
+      t_end = f_end;
+      x = 1;
+    } else {
+      const Seg sg = find(x);
+      b = sg.b;
+      kvh = sg.kvh;
+      L = sg.L;
+      seg_start = sg.start;
+      t_begin = (int)(x - seg_start);
+      t_end = (int)min((long long)L, u_end - seg_start);
+      x = seg_start + L;
+    }
     const int P = L - N;
-    const int t_begin = (int)(x - sg.start);
-    const int t_end = (int)min((long long)L, u_end - sg.start);
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
     const bool direct = (t_begin == 0 && t_end == L);   // the whole sequence is in this piece
-    x = sg.start + L;
-    const bool prefetched = first_piece && g_seg == b * Hkv + kvh && g_begin == t_begin && g_end == t_end;
-    if (first_piece && !prefetched && g_seg >= 0) wait_vmcnt<0>();   // discard the guessed tiles
-    first_piece = false;
 
     __syncthreads();                                 // the previous piece is done with the LDS
 
@@ -481,7 +496,7 @@ void tree_attn_split_kernel(
 
     // tiles 0 .. NSTAGE-2 go in flight first; everything up to the wait below
     // runs in their shadow
-    if (!prefetched) {
+    if (!fixed) {                                    // a fixed split's first tiles are in flight already
 #pragma unroll
       for (int i = 0; i < NSTAGE - 1; ++i)
         if (i < ntiles) issue(i, i);
@@ -489,15 +504,22 @@ void tree_attn_split_kernel(
     }
 
     // merge bookkeeping for a piece that covers only part of its sequence:
-    // the units that hold its pieces, and this piece's partial-result slot
-    int u_first = u, npieces = 1, my_slot = 2 * u;
+    // this piece's partial-result slot, and the slots of all its sequence's
+    // pieces.  Fixed: piece sp of sequence f_seg has slot f_seg*n_splits + sp.
+    // Balanced: the units u_first .. u_first+npieces-1 hold the pieces, each
+    // unit has two slots (for its first and its last piece, the only ones that
+    // can cover part of a sequence), and the first unit's piece is its last
+    // one if it started in an earlier sequence.
+    int u_first = u, npieces = n_splits, my_slot = u;
     bool first_odd = false;
-    if (!direct) {
-      u_first = (u_start <= sg.start) ? u : unit_of(sg.start);
-      const int u_last = (u_end >= sg.start + L) ? u : unit_of(sg.start + L - 1);
+    if (fixed) {
+      u_first = f_seg * n_splits;
+    } else if (!direct) {
+      u_first = (u_start <= seg_start) ? u : unit_of(seg_start);
+      const int u_last = (u_end >= seg_start + L) ? u : unit_of(seg_start + L - 1);
       npieces = u_last - u_first + 1;
-      first_odd = bnd(u_first) < sg.start;           // that unit's piece is its last one
-      my_slot = (u_start >= sg.start) ? 2 * u : 2 * u + 1;
+      first_odd = bnd(u_first) < seg_start;
+      my_slot = (u_start >= seg_start) ? 2 * u : 2 * u + 1;
     }
     // Complete the Q / mask loads here, once: the compiler cannot count the
     // DMA instructions, so any wait it places for these loads drains the ring;
@@ -511,6 +533,17 @@ void tree_attn_split_kernel(
     }
 
     wait_vmcnt<0>();   // usually already met by the wait above; a wave with no Q rows has none
+    if (fixed) {
+      // wave 0's prefix lengths have landed (the wait above); once they are
+      // visible, check that the fixed schedule is the balanced one
+      __syncthreads();
+      if (!uniform()) {
+        fixed = false;
+        if (!to_balanced()) break;
+        x = u_start;
+        continue;
+      }
+    }
 
     f32x4_t oacc[RB][DB];
     float m_run[RB], l_run[RB];
@@ -672,7 +705,6 @@ void tree_attn_split_kernel(
       compute(st, i);
       st = (st + 1 == NSTAGE) ? 0 : st + 1;
     }
-
     // ---- waves that split the tile's tokens combine their states in LDS
     if constexpr (WT == 2) {
       // scratch in the ring: O blocks (1 KB per row block and column block)
@@ -794,7 +826,7 @@ void tree_attn_split_kernel(
 #pragma unroll
         for (int j = 0; j < SG; ++j) {
           const int sp = s0 + j;
-          const int sl = 2 * (u_first + sp) + ((sp == 0 && first_odd) ? 1 : 0);
+          const int sl = fixed ? u_first + sp : 2 * (u_first + sp) + ((sp == 0 && first_odd) ? 1 : 0);
           const __amdgpu_buffer_rsrc_t ro = dev_rsrc(part_o + part_row(sl, 0) * D, MT * D * 4);
           const __amdgpu_buffer_rsrc_t rm = dev_rsrc(part_ml + part_row(sl, 0), MT * 8);
 #pragma unroll
@@ -941,7 +973,7 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
 
 struct AttnPlan {
   int rb, wm, wt, nstage, mt_rows, n_mt, M_pad;
-  int n_units;
+  int split_len, n_splits, n_units;
   size_t ws_bytes;
 };
 
@@ -952,11 +984,14 @@ constexpr int kTableBytes = 4 * (1024 + 1) + 4;
 // Rows per workgroup follow the packed M = g*N.  Small M (<= 32) lets the
 // waves also split each tile's tokens (a 3-stage K/V ring, one workgroup per
 // CU); larger M splits rows over the waves (a 2-stage ring, two workgroups per
-// CU, so two waves share each SIMD).  The work stream is then cut into about
-// one unit per resident workgroup slot (256 CUs), each unit for all M-tiles.
-// The plan does not depend on the cached dtype, so one workspace size serves
-// every format: two partial-result slots per unit and M-tile, and one counter
-// per (request, kv head, M-tile).
+// CU, so two waves share each SIMD).  Work then comes in about one unit per
+// resident workgroup slot (256 CUs), each unit for all M-tiles, under one of
+// two schedules the kernel picks from the data: fixed splits of S_max
+// (split_len tokens, never under 256) when every request fills its cache, or
+// equal shares of the actual tokens otherwise.  The plan does not depend on
+// the cached dtype, so one workspace size serves every format: partial
+// results for the larger of the two slot counts (a fixed split each, or two
+// per balanced unit) and one counter per (request, kv head, M-tile).
 static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan* p) {
   if (B < 1 || B > 1024 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < Hkv || Hq % Hkv) return false;
   if (D != 64 && D != 128) return false;
@@ -976,8 +1011,17 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   p->n_mt = (M + p->mt_rows - 1) / p->mt_rows;
   p->M_pad = p->n_mt * p->mt_rows;
   p->n_units = (int)std::max<long long>(1, target_wgs / p->n_mt);
-  const size_t rows = (size_t)2 * p->n_units * p->M_pad;
-  const size_t counters = (size_t)B * Hkv * p->n_mt;
+  const long long seqs = (long long)B * Hkv;
+  const int want = (int)std::max<long long>(1, (p->n_units + seqs - 1) / seqs);
+  int split_len = (S_max + want - 1) / want;
+  split_len = ((split_len + kTile - 1) / kTile) * kTile;
+  if (split_len < 256) split_len = 256;
+  p->split_len = split_len;
+  p->n_splits = (S_max + split_len - 1) / split_len;
+  if (seqs * p->n_splits * p->n_mt >= (1ll << 31)) return false;
+  const size_t slots = (size_t)std::max<long long>(seqs * p->n_splits, 2ll * p->n_units);
+  const size_t rows = slots * p->M_pad;
+  const size_t counters = (size_t)seqs * p->n_mt;
   p->ws_bytes = rows * (size_t)D * sizeof(float) + rows * sizeof(float2) + counters * sizeof(uint32_t);
   return true;
 }
@@ -988,12 +1032,13 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
                          float* lse, float* po, float2* pml, uint32_t* cnt, uint32_t* err,
                          hipStream_t st) {
-  const int units_pad = ((pl.n_units + 7) / 8) * 8;
+  const int units = std::max(B * Hkv * pl.n_splits, pl.n_units);
+  const int units_pad = ((units + 7) / 8) * 8;
   const unsigned grid = (unsigned)units_pad * (unsigned)pl.n_mt;
   hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS>), dim3(grid), dim3(WM * WT * kWave),
                      0, st, static_cast<const __bf16*>(q), static_cast<const unsigned char*>(k),
                      static_cast<const unsigned char*>(v), ks, vs, pre, anc, B, N, Hq, Hkv, S_max,
-                     sm_scale, pl.n_units, pl.n_mt, static_cast<__bf16*>(out), lse,
+                     sm_scale, pl.split_len, pl.n_splits, pl.n_units, pl.n_mt, static_cast<__bf16*>(out), lse,
                      po, pml, cnt, err);
 }
 
@@ -1089,7 +1134,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
     if (!workspace) return SPEC_ERR_WORKSPACE;
     if (workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
-    const size_t rows = (size_t)2 * pl.n_units * pl.M_pad;
+    const size_t rows = (size_t)std::max<long long>((long long)B * Hkv * pl.n_splits, 2ll * pl.n_units) * pl.M_pad;
     po = static_cast<float*>(workspace);
     pml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + rows * D * sizeof(float));
     cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + rows * D * sizeof(float) +
