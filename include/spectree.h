@@ -89,8 +89,9 @@ spec_status spec_tree_mask_build(const int32_t* parents, int B, int N,
 
 /*
  * spec_tree_attn_workspace_bytes -- scratch needed by spec_tree_attn_verify
- * for these sizes (0 when the launch needs none).  Pure function of its
- * arguments; returns 0 for sizes spec_tree_attn_verify would reject.
+ * for these sizes (any cache dtype).  Pure function of its arguments; returns
+ * 0 for sizes spec_tree_attn_verify would reject.  The fp32 path uses none of
+ * it.
  */
 size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max);
 
@@ -110,6 +111,7 @@ size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int 
  *     lse[b][i][h] = log sum_c exp(s_c)
  * Cache rows >= P + N are never read.
  *
+ *   B          1..1024 requests, with B*S_max and Hkv*S_max below 2^31
  *   q          [B][N][Hq][D] of q_dtype (SPEC_F32 or SPEC_BF16), 16-B aligned
  *   k_cache,
  *   v_cache    [B][Hkv][S_max][D] of kv_dtype, 16-B aligned; tree node j of
@@ -132,8 +134,11 @@ size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int 
  *   err_word   nullable: SPEC_DERR_PREFIX
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Results are deterministic: the split-K merge runs in a fixed order.
- * Long requests are split over several workgroups; the last one of a
- * request to finish merges the partial results in the same launch.
+ * Work is cut into about one unit per resident workgroup: fixed splits of
+ * S_max when every request fills its cache (prefix_lens[b] == S_max - N),
+ * otherwise equal shares of the actual tokens; the kernel picks from the data.
+ * A request spread over several workgroups is merged, in the same launch, by
+ * the last of them to finish.
  */
 spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype,
                                   const void* k_cache, const void* v_cache, spec_dtype kv_dtype,

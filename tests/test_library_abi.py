@@ -101,6 +101,8 @@ def test_attention_host_checks(L):
     assert _attn(L, shape=(8, 6, 30, 8, 128, 2054)) == SPEC_ERR_SHAPE    # Hq % Hkv
     assert _attn(L, shape=(8, 6, 32, 8, 96, 2054)) == SPEC_ERR_SHAPE     # D
     assert _attn(L, shape=(8, 65, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE   # N
+    assert _attn(L, shape=(1025, 6, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE  # B beyond the length table
+    assert _attn(L, shape=(1024, 6, 32, 8, 128, 2 ** 21)) == SPEC_ERR_SHAPE  # B * S_max reaches 2^31
     assert _attn(L, shape=(8, 6, 32, 8, 128, 5)) == SPEC_ERR_SHAPE       # S_max < N
     assert _attn(L, q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
     assert _attn(L) == SPEC_ERR_WORKSPACE                            # split path needs scratch
