@@ -236,6 +236,37 @@ def test_attention_many_splits_short_requests():
     _attn_case(w, "many_splits", prefix_lens=x["prefix_lens"])
 
 
+def test_attention_balanced_many_requests():
+    """More than 64 requests with ragged lengths: the per-request length table
+    spans several 64-entry blocks (two-level search), units cross many short
+    sequences (several whole sequences and partial pieces per unit)."""
+    w = W[2].replace(B=150, N=5, Hq=8, Hkv=2, D=64, prefix_lo=0, prefix_hi=700, V=10, seed=41,
+                     max_depth=3, max_children=2)
+    log(f"[balanced] B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} P=[{w.prefix_lo},{w.prefix_hi}]")
+    _attn_case(w, "balanced_many_requests")
+
+
+def test_attention_ragged_with_one_bad_prefix():
+    """A ragged batch where one request's prefix length is out of range: it is
+    flagged and skipped, the others are balanced and correct."""
+    w = W[2].replace(B=6, prefix_lo=100, prefix_hi=2500, V=10, seed=42)
+    x = synth.make_inputs(w, with_logits=False)
+    d = to_device(x)
+    pre = x["prefix_lens"].copy()
+    pre[3] = w.S_max                                 # P + N > S_max
+    d["prefix_lens"] = torch.from_numpy(pre).cuda()
+    anc, _, _ = st.tree_mask_build(d["parents"])
+    out, lse, err = st.tree_attn_verify(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc,
+                                        x["sm_scale"])
+    torch.cuda.synchronize()
+    assert int(err[0]) & st.DERR_PREFIX
+    qo, ko, vo = oracle_views(x)
+    keep = [b for b in range(w.B) if b != 3]
+    ro, rl = oracle.tree_attention(qo[keep], ko[keep], vo[keep], x["prefix_lens"][keep], x["parents"][keep],
+                                   x["sm_scale"], q_fmt=w.q_dtype, kv_fmt=w.kv_dtype)
+    check_attention(out.float().cpu().numpy()[keep], ro, w.kv_dtype, "ragged_bad_prefix")
+
+
 def test_attention_is_deterministic():
     w = SMALL["tree16_ragged_bf16"]
     x = synth.make_inputs(w, with_logits=False)
