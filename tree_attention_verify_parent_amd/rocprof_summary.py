@@ -66,10 +66,15 @@ def pmc(d):
     return agg
 
 
+ATTENTION_SOURCES = ("common.h", "tree_attn.hip")
+
+
 def source_sha(root):
+    """Digest of the attention kernel's sources: counter runs stay valid while
+    these are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(root, "tree_attention_verify_parent_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ATTENTION_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
