@@ -122,7 +122,7 @@ size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int 
  *   prefix_lens int32[B]
  *   anc_mask   uint64[B][N] from spec_tree_mask_build
  *   D          64 or 128
- *   sm_scale   softmax scale (typically 1/sqrt(D))
+ *   sm_scale   softmax scale, finite and > 0 (typically 1/sqrt(D))
  *   out        [B][N][Hq][D] of q_dtype, 16-B aligned
  *   lse        float[B][N][Hq], nullable
  *   workspace  >= spec_tree_attn_workspace_bytes(...) bytes, 16-B aligned;

@@ -87,8 +87,8 @@ def test_argmax_host_checks(L):
 
 
 def _attn(L, q=FAKE, qd=1, k=FAKE, v=FAKE, kvd=1, ks=None, vs=None, shape=(8, 6, 32, 8, 128, 2054),
-          out=FAKE, ws=None, wsb=0):
-    return L.spec_tree_attn_verify(q, qd, k, v, kvd, ks, vs, FAKE, FAKE, *shape, 0.088, out, None, ws,
+          out=FAKE, ws=None, wsb=0, scale=0.088):
+    return L.spec_tree_attn_verify(q, qd, k, v, kvd, ks, vs, FAKE, FAKE, *shape, scale, out, None, ws,
                                    wsb, None, None)
 
 
@@ -102,6 +102,8 @@ def test_attention_host_checks(L):
     assert _attn(L, shape=(8, 6, 32, 8, 96, 2054)) == SPEC_ERR_SHAPE     # D
     assert _attn(L, shape=(8, 65, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE   # N
     assert _attn(L, shape=(1025, 6, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE  # B beyond the length table
+    assert _attn(L, scale=0.0) == SPEC_ERR_SHAPE                    # the softmax scale must be positive
+    assert _attn(L, scale=float("nan")) == SPEC_ERR_SHAPE
     assert _attn(L, shape=(1024, 6, 32, 8, 128, 2 ** 21)) == SPEC_ERR_SHAPE  # B * S_max reaches 2^31
     assert _attn(L, shape=(8, 6, 32, 8, 128, 5)) == SPEC_ERR_SHAPE       # S_max < N
     assert _attn(L, q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN

@@ -23,6 +23,7 @@
 // A request whose tokens fit one split writes its output directly; otherwise
 // each split writes (O, m, l) partials and the last split to finish combines
 // them in split order (deterministic), in the same launch.
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -631,6 +632,8 @@ void tree_attn_split_kernel(
 #pragma unroll
           for (int cp = 0; cp < CPT; ++cp) vis8[cp] = (uint32_t)(vis >> (32 * (wt * CPT + cp) + 8 * lg)) & 0xFFu;
         }
+        // max over the raw scores (the scale is positive, so it keeps the order
+        // and commutes with the max exactly), masked tokens to -inf
         float mx = -INFINITY;
 #pragma unroll
         for (int cp = 0; cp < CPT; ++cp)
@@ -638,16 +641,18 @@ void tree_attn_split_kernel(
           for (int G = 0; G < 2; ++G)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              float s = sacc[rb][cp][G][r] * scale_log2;
+              float s = sacc[rb][cp][G][r];
               if (!plain) s = ((vis8[cp] >> (4 * G + r)) & 1u) ? s : -INFINITY;
               sacc[rb][cp][G][r] = s;
               mx = fmaxf(mx, s);
             }
-        mx = row4_max(mx);
+        mx = row4_max(mx) * scale_log2;
         const float m_new = fmaxf(m_run[rb], mx);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         alpha[rb] = fast_exp2(m_run[rb] - m_use);
         m_run[rb] = m_new;
+        // p = 2^(s*scale - m) with one fma; the row sum (for the output's
+        // normalisation and the exact log-sum-exp) is over the fp32 p
         float lsum = 0.0f;
 #pragma unroll
         for (int cp = 0; cp < CPT; ++cp)
@@ -655,7 +660,7 @@ void tree_attn_split_kernel(
           for (int G = 0; G < 2; ++G)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float p = fast_exp2(sacc[rb][cp][G][r] - m_use);
+              const float p = fast_exp2(__builtin_fmaf(sacc[rb][cp][G][r], scale_log2, -m_use));
               lsum += p;
               pb[rb][cp][4 * G + r] = (__bf16)p;
             }
@@ -1109,6 +1114,7 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
   AttnPlan pl;
   if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return SPEC_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return SPEC_ERR_ALIGN;
 
