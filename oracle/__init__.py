@@ -16,6 +16,9 @@ What is computed, and where the pages say so:
     section 2, closing paragraph on tree attention).
   * Acceptance length is the number of draft tokens the target accepts in one
     verification step (Runtime Draft Model Training, "Evaluation").
+  * The accepted and rejected outcomes of each verification are what the
+    serving engine streams on (Aurora, section 2): the commit step keeps the
+    accepted path's K/V rows and labels every node.
 
 Everything is plain: explicit parent-pointer walks, a dense boolean mask,
 naive softmax in float64, a linear argmax, a recursive accept walk.
@@ -31,9 +34,11 @@ from .attention import (bf16_bits_to_f64, e4m3_decode_table, decode_e4m3, dense_
                         tree_attention_bh, tree_attention)
 from .argmax import vocab_argmax
 from .step import verify_step
+from .commit import commit_accepted, LABEL_ACCEPTED, LABEL_REJECTED, LABEL_ROOT
 
 __all__ = [
     "ancestors", "build_masks", "accept_walk", "children_of",
     "bf16_bits_to_f64", "e4m3_decode_table", "decode_e4m3", "dense_tree_mask",
     "tree_attention_bh", "tree_attention", "vocab_argmax", "verify_step",
+    "commit_accepted", "LABEL_ACCEPTED", "LABEL_REJECTED", "LABEL_ROOT",
 ]

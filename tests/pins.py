@@ -352,3 +352,70 @@ def check_attention_ignores_rows_past_tree(tree_attention, seed: int = 7):
         v2[b, :, int(prefix[b]) + 5:] = np.nan
     out2, _ = tree_attention(q, k2, v2, prefix, parents, 0.7, q_fmt="f32", kv_fmt="f32")
     np.testing.assert_array_equal(out, out2)
+
+
+# ------------------------------------------------------------------ commit
+
+def _row_tagged_cache(B, Hkv, S, width=3):
+    """K/V whose every element says which (request, head, row) it came from."""
+    b, h, r, c = np.meshgrid(np.arange(B), np.arange(Hkv), np.arange(S), np.arange(width), indexing="ij")
+    k = (b * 1_000_000 + h * 10_000 + r * 10 + c).astype(np.int64)
+    return k, -k
+
+
+def check_commit_golden(commit_accepted):
+    for name, par, P, L, path, stored, labels in read_golden("commit_hand_examples.txt"):
+        par, P, L, path, stored, labels = ints(par), int(P), int(L), ints(path), ints(stored), ints(labels)
+        N = len(par)
+        k, v = _row_tagged_cache(1, 2, P + N + 2)
+        pn = np.full((1, N), -1, dtype=np.int32)
+        pn[0, :L + 1] = path
+        k2, v2, newp, lab = commit_accepted(k, v, np.array([P]), np.array([L]), pn, N)
+        assert int(newp[0]) == P + 1 + L, name
+        assert list(lab[0]) == labels, (name, list(lab[0]))
+        for j, node in enumerate(stored):
+            assert np.array_equal(k2[0, :, P + j], k[0, :, P + node]), (name, j)
+            assert np.array_equal(v2[0, :, P + j], v[0, :, P + node]), (name, j)
+        rest = [r for r in range(k.shape[2]) if not P + 1 <= r <= P + L]
+        assert np.array_equal(k2[0, :, rest], k[0, :, rest]) and np.array_equal(v2[0, :, rest], v[0, :, rest]), name
+
+
+def check_commit_against_parent_chase(commit_accepted, accept_walk, seed: int = 8):
+    """Random trees and tokens: the committed rows P+1..P+L hold, in order, the
+    nodes met walking parent links up from the accepted path's end node (found
+    here independently of the walk's own path output), labels mark exactly
+    those nodes, every other row and request is untouched."""
+    rng = np.random.default_rng(seed)
+    for trial in range(60):
+        B, N, Hkv = 3, int(rng.integers(1, 12)), 2
+        parents = np.zeros((B, N), dtype=np.int32)
+        for b in range(B):
+            parents[b, 0] = -1
+            for i in range(1, N):
+                parents[b, i] = rng.integers(0, i)
+        d = rng.integers(0, 3, size=(B, N)).astype(np.int32)
+        t = rng.integers(0, 3, size=(B, N)).astype(np.int32)
+        L, path, _ = accept_walk(parents, d, t, V=3)
+        prefix = rng.integers(0, 6, size=B)
+        S = int(prefix.max()) + N + 1
+        k, v = _row_tagged_cache(B, Hkv, S)
+        k2, v2, newp, lab = commit_accepted(k, v, prefix, L, path, N)
+        for b in range(B):
+            P, Lb = int(prefix[b]), int(L[b])
+            chain, n = [], int(path[b][Lb])
+            while n != -1:
+                chain.append(n)
+                n = int(parents[b, n])
+            chain.reverse()
+            assert len(chain) == Lb + 1 and chain[0] == 0
+            for j, node in enumerate(chain):
+                assert np.array_equal(k2[b, :, P + j], k[b, :, P + node])
+                assert np.array_equal(v2[b, :, P + j], v[b, :, P + node])
+            others = [r for r in range(S) if not P + 1 <= r <= P + Lb]
+            assert np.array_equal(k2[b, :, others], k[b, :, others])
+            assert int(newp[b]) == P + 1 + Lb
+            want = [0] * N
+            want[0] = 2
+            for node in chain[1:]:
+                want[node] = 1
+            assert list(lab[b]) == want

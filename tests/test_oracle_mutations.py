@@ -22,7 +22,7 @@ def load_mutant(edits):
     pkg.__path__ = []
     sys.modules[name] = pkg
     try:
-        for mod in ("tree", "attention", "argmax", "step"):
+        for mod in ("tree", "attention", "argmax", "step", "commit"):
             with open(os.path.join(ORACLE_DIR, mod + ".py")) as f:
                 src = f.read()
             for (fname, old, new) in edits:
@@ -92,6 +92,17 @@ MUTANTS = {
                     lambda o: _check_e4m3(o)),
     "e4m3_subnormal_dropped": ([("attention", "tab[code] = s * (m / 8.0) * 2.0 ** -6", "tab[code] = 0.0")],
                                lambda o: _check_e4m3(o)),
+    # commit step
+    "commit_dst_off_by_one": ([("commit", "k_new[b, :, P + k] = k_cache[b, :, src]", "k_new[b, :, P + k - 1] = k_cache[b, :, src]")],
+                              lambda o: pins.check_commit_golden(o.commit.commit_accepted)),
+    "commit_prefix_drops_root": ([("commit", "new_prefix[b] = P + 1 + L", "new_prefix[b] = P + L")],
+                                 lambda o: pins.check_commit_golden(o.commit.commit_accepted)),
+    "commit_root_labelled_accepted": ([("commit", "labels[b, 0] = LABEL_ROOT", "labels[b, 0] = LABEL_ACCEPTED")],
+                                      lambda o: pins.check_commit_against_parent_chase(o.commit.commit_accepted,
+                                                                                       o.tree.accept_walk)),
+    "commit_source_by_depth": ([("commit", "src = P + path[k]", "src = P + k")],
+                               lambda o: pins.check_commit_against_parent_chase(o.commit.commit_accepted,
+                                                                                o.tree.accept_walk)),
 }
 
 
