@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--attn-calls", type=int, default=200, help="calls in the attention timing graph")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-commit", action="store_true", help="skip timing the commit step")
     ap.add_argument("--copy-calibration", type=float, default=0,
                     help="only run a plain float32 elementwise copy that reads and writes this many "
                          "bytes (5 launches) and exit: the reference point that scales the HBM byte "
@@ -333,6 +334,34 @@ def main():
     roof["launch_us"] = round(attn_us, 3)
     roof["bytes_per_launch"] = bytes_["attention"]
 
+    # ---- the commit step after verification (keep the accepted path's K/V,
+    # label outcomes): a graph of back-to-back calls on the accepted paths of
+    # the warm-up step, in place on the cache replicas (the rows it moves do
+    # not change its cost)
+    commit = None
+    if not args.no_commit:
+        newp = torch.empty(B, dtype=torch.int32, device=dev)
+        labels = torch.empty((B, N), dtype=torch.int8, device=dev)
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            for c in range(calls):
+                st.commit_accepted(kcs[c % R], vcs[c % R], prefix, acc_len, path, new_prefix_lens=newp,
+                                   labels=labels, err=err)
+        torch.cuda.synchronize()
+        cg.replay()
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(reps):
+            cg.replay()
+        c1.record()
+        torch.cuda.synchronize()
+        commit_us = c0.elapsed_time(c1) * 1e3 / (reps * calls)
+        kv_elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+        moved = int(acc_len.sum().item()) * w.Hkv * w.D * kv_elem * 2 * 2      # K and V rows, read + write
+        commit = dict(launch_us=round(commit_us, 3), bytes_per_launch=moved + B * N + 12 * B,
+                      accept_len_sum=int(acc_len.sum().item()))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, args.cpu_baseline_seconds)
@@ -361,6 +390,7 @@ def main():
         "accept_len_mean": round(float(acc_len.float().mean().item()), 3),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "commit_step": commit,
     }
     print(json.dumps(line), flush=True)
 

@@ -11,6 +11,7 @@
  *   spec_tree_attn_verify  tree-masked split-KV attention over the KV cache
  *   spec_vocab_argmax      per-node argmax of the target logits
  *   spec_accept_walk       longest matched root-to-node path -> accepted tokens
+ *   spec_commit_accepted   (after the step) keep the accepted path's K/V, label outcomes
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -64,6 +65,8 @@ typedef enum {
 #define SPEC_DERR_PARENT 2u  /* parents[b][i] not in [0, i) for some i >= 1   */
 #define SPEC_DERR_PREFIX 4u  /* prefix_lens[b] < 0 or prefix_lens[b]+N > S_max */
 #define SPEC_DERR_TOKEN  8u  /* a draft token or target argmax not in [0, V)  */
+#define SPEC_DERR_PATH  16u  /* accept_len not in [0, N-1], or the accepted
+                                path is not root-first, increasing, in [0, N) */
 
 #define SPEC_MAX_NODES 64
 
@@ -189,6 +192,37 @@ spec_status spec_accept_walk(const int32_t* parents, const uint64_t* anc_mask,
                              int B, int N, int V,
                              int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
                              uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_commit_accepted -- keep the accepted path in the cache, label outcomes.
+ *
+ * The step after verification: the accepted and rejected outcomes of every
+ * proposed token are the record the serving engine streams on (Aurora,
+ * section 2, the inference server, and the mapping of accepted tokens and
+ * rejected proposals to positive and negative feedback).  A reading of it
+ * for the cache: it keeps the prefix, the root (node 0, row P) and the
+ * accepted draft nodes in path order, so the node at depth k of the accepted
+ * path moves to row P + k (k = 1..L); rows past P + L are left as they were
+ * and are free for the next tree.  The bonus token has no K/V yet.
+ *
+ *   k_cache,
+ *   v_cache         [B][Hkv][S_max][D] of kv_dtype (any of the three), 16-B
+ *                   aligned; updated in place
+ *   prefix_lens     int32[B]   P of each request before this step
+ *   accept_len      int32[B]   L from spec_accept_walk
+ *   path_nodes      int32[B][N] from spec_accept_walk (entries 0..L read)
+ *   D               64 or 128
+ *   new_prefix_lens int32[B]   out: P + 1 + L (prefix, root, accepted tokens)
+ *   node_labels     int8[B][N] out, nullable: 2 root, 1 accepted draft node,
+ *                   0 rejected draft node
+ *   err_word        nullable: SPEC_DERR_PREFIX / SPEC_DERR_PATH; a flagged
+ *                   request's cache rows and outputs are left unchanged
+ */
+spec_status spec_commit_accepted(void* k_cache, void* v_cache, spec_dtype kv_dtype,
+                                 const int32_t* prefix_lens, const int32_t* accept_len,
+                                 const int32_t* path_nodes, int B, int N, int Hkv, int D, int S_max,
+                                 int32_t* new_prefix_lens, int8_t* node_labels,
+                                 uint32_t* err_word, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* spec_status_string(spec_status status);

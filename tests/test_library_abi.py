@@ -116,3 +116,15 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(st.SpecError):
         st.tree_mask_build(torch.zeros((1, 6), dtype=torch.int32))
+
+
+def test_commit_host_checks(L):
+    def commit(k=FAKE, v=FAKE, dt=1, shape=(4, 6, 8, 128, 2054), newp=FAKE):
+        return L.spec_commit_accepted(k, v, dt, FAKE, FAKE, FAKE, *shape, newp, None, None, None)
+    assert commit(k=None) == SPEC_ERR_NULL
+    assert commit(newp=None) == SPEC_ERR_NULL
+    assert commit(dt=7) == SPEC_ERR_DTYPE
+    assert commit(shape=(4, 65, 8, 128, 2054)) == SPEC_ERR_SHAPE
+    assert commit(shape=(4, 6, 8, 96, 2054)) == SPEC_ERR_SHAPE
+    assert commit(shape=(0, 6, 8, 128, 2054)) == SPEC_ERR_SHAPE
+    assert commit(shape=(4, 6, 8, 128, 5)) == SPEC_ERR_SHAPE

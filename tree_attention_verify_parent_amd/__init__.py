@@ -16,21 +16,21 @@ import torch
 
 __all__ = [
     "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify",
-    "vocab_argmax", "accept_walk", "verify_step", "DERR_ROOT", "DERR_PARENT", "DERR_PREFIX",
-    "DERR_TOKEN", "library_path",
+    "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "DERR_ROOT", "DERR_PARENT",
+    "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "library_path",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspectree.so")
 
 SPEC_F32, SPEC_BF16, SPEC_FP8_E4M3 = 0, 1, 2
-DERR_ROOT, DERR_PARENT, DERR_PREFIX, DERR_TOKEN = 1, 2, 4, 8
+DERR_ROOT, DERR_PARENT, DERR_PREFIX, DERR_TOKEN, DERR_PATH = 1, 2, 4, 8, 16
 MAX_NODES = 64
 
 _DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3fn: SPEC_FP8_E4M3}
 
 EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
-           "spec_vocab_argmax", "spec_accept_walk", "spec_status_string"]
+           "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted", "spec_status_string"]
 
 
 class SpecError(RuntimeError):
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.spec_vocab_argmax.restype = c_i
     L.spec_accept_walk.argtypes = [c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p]
     L.spec_accept_walk.restype = c_i
+    L.spec_commit_accepted.argtypes = [c_p, c_p, c_i, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p]
+    L.spec_commit_accepted.restype = c_i
     L.spec_status_string.argtypes = [c_i]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -164,6 +166,26 @@ def accept_walk(parents, anc_mask, draft_tokens, target_argmax, V, *, accept_len
                                   B, N, int(V), _ptr(accept_len), _ptr(path_nodes), _ptr(out_tokens),
                                   _ptr(err), _stream(stream)))
     return accept_len, path_nodes, out_tokens, err
+
+
+def commit_accepted(k_cache, v_cache, prefix_lens, accept_len, path_nodes, *, new_prefix_lens=None,
+                    labels=None, want_labels=True, err=None, stream=None):
+    """In place: request b's accepted path node at depth k moves to cache row
+    prefix_lens[b] + k.  Returns (new_prefix_lens int32[B], labels int8[B][N]
+    or None, err)."""
+    B, Hkv, S_max, D = k_cache.shape
+    N = path_nodes.shape[1]
+    if k_cache.dtype not in _DTYPE or v_cache.dtype != k_cache.dtype or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise SpecError("k_cache / v_cache must be matching [B][Hkv][S_max][D] tensors of a supported dtype")
+    dev = k_cache.device
+    new_prefix_lens = torch.empty(B, dtype=torch.int32, device=dev) if new_prefix_lens is None else new_prefix_lens
+    if labels is None and want_labels:
+        labels = torch.empty((B, N), dtype=torch.int8, device=dev)
+    err = _err_word(err, dev)
+    _check(lib().spec_commit_accepted(_ptr(k_cache), _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(prefix_lens),
+                                      _ptr(accept_len), _ptr(path_nodes), B, N, Hkv, D, S_max,
+                                      _ptr(new_prefix_lens), _ptr(labels), _ptr(err), _stream(stream)))
+    return new_prefix_lens, labels, err
 
 
 def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *,
