@@ -51,6 +51,8 @@ def test_commit_matches_oracle(name):
     assert int(err[0]) == 0
     Lc, pc = L.cpu().numpy(), path.cpu().numpy()
     log(f"  accept_len {list(Lc)}")
+    if w.tree == "random":     # the case must exercise real moves, not only paths already in place
+        assert any(pc[b][k] != k for b in range(w.B) for k in range(1, int(Lc[b]) + 1)), list(Lc)
     ko, vo, po, lo = oracle.commit_accepted(kb, vb, x["prefix_lens"], Lc, pc, w.N)
     assert np.array_equal(_bytes(d["k_cache"]), ko)
     assert np.array_equal(_bytes(d["v_cache"]), vo)
