@@ -35,10 +35,11 @@ from .attention import (bf16_bits_to_f64, e4m3_decode_table, decode_e4m3, dense_
 from .argmax import vocab_argmax
 from .step import verify_step
 from .commit import commit_accepted, LABEL_ACCEPTED, LABEL_REJECTED, LABEL_ROOT
+from .paged import gather_pages
 
 __all__ = [
     "ancestors", "build_masks", "accept_walk", "children_of",
     "bf16_bits_to_f64", "e4m3_decode_table", "decode_e4m3", "dense_tree_mask",
     "tree_attention_bh", "tree_attention", "vocab_argmax", "verify_step",
-    "commit_accepted", "LABEL_ACCEPTED", "LABEL_REJECTED", "LABEL_ROOT",
+    "commit_accepted", "LABEL_ACCEPTED", "LABEL_REJECTED", "LABEL_ROOT", "gather_pages",
 ]

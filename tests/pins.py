@@ -419,3 +419,32 @@ def check_commit_against_parent_chase(commit_accepted, accept_walk, seed: int = 
             for node in chain[1:]:
                 want[node] = 1
             assert list(lab[b]) == want
+
+
+# ------------------------------------------------------------------- paged
+
+def check_gather_pages_round_trip(gather_pages, seed: int = 9):
+    """Scatter a tagged contiguous cache into shuffled pages (written here
+    token by token), gather it back: identical, including a request whose
+    pages are shared with nobody and a partially filled last page."""
+    rng = np.random.default_rng(seed)
+    for B, Hkv, S_max, ps in [(3, 2, 40, 8), (2, 1, 64, 16), (1, 3, 7, 4)]:
+        maxp = -(-S_max // ps)
+        contig = _row_tagged_cache(B, Hkv, S_max)[0]
+        num_pages = B * maxp + 3
+        perm = rng.permutation(num_pages)[: B * maxp].reshape(B, maxp)
+        pages = np.full((num_pages, ps, Hkv, contig.shape[-1]), -7, dtype=contig.dtype)
+        for b in range(B):
+            for t in range(S_max):
+                pages[perm[b, t // ps], t % ps] = contig[b, :, t]
+        back = gather_pages(pages, perm, ps, S_max)
+        assert np.array_equal(back, contig)
+
+
+def check_gather_pages_identity(gather_pages):
+    """Pages laid out request after request in order: the gather is a reshape."""
+    B, Hkv, ps, maxp = 2, 2, 4, 3
+    pages = np.arange(B * maxp * ps * Hkv * 5).reshape(B * maxp, ps, Hkv, 5)
+    table = np.arange(B * maxp).reshape(B, maxp)
+    want = pages.reshape(B, maxp * ps, Hkv, 5).transpose(0, 2, 1, 3)
+    assert np.array_equal(gather_pages(pages, table, ps, maxp * ps), want)
