@@ -67,6 +67,8 @@ typedef enum {
 #define SPEC_DERR_TOKEN  8u  /* a draft token or target argmax not in [0, V)  */
 #define SPEC_DERR_PATH  16u  /* accept_len not in [0, N-1], or the accepted
                                 path is not root-first, increasing, in [0, N) */
+#define SPEC_DERR_PAGE  32u  /* a block-table entry a request uses is not in
+                                [0, num_pages)                                 */
 
 #define SPEC_MAX_NODES 64
 
@@ -151,6 +153,36 @@ spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype,
                                   float sm_scale, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes,
                                   uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_tree_attn_verify_paged -- spec_tree_attn_verify over a paged cache.
+ *
+ * The verify pass runs inside a serving engine (SGLang or vLLM: Aurora,
+ * section 2, the inference server) whose K/V caches are paged.  A reading of
+ * that layout: a pool of pages of page_size tokens, token-major (each token a
+ * [Hkv][D] block); request b's logical token t is in page
+ * block_table[b][t / page_size], slot t % page_size.  Everything else --
+ * tree layout (node j at logical token prefix_lens[b] + j), mask, outputs,
+ * dtypes, workspace (query spec_tree_attn_workspace_bytes with
+ * S_max = max_pages * page_size) and errors -- is as in spec_tree_attn_verify.
+ *
+ *   k_pages,
+ *   v_pages      [num_pages][page_size][Hkv][D] of kv_dtype (SPEC_BF16 or
+ *                SPEC_FP8_E4M3; q_dtype SPEC_BF16), 16-B aligned
+ *   block_table  int32[B][max_pages], 1 <= max_pages <= 2048
+ *   page_size    a power of two, 1..4096
+ *   err_word     nullable: SPEC_DERR_PREFIX; SPEC_DERR_PAGE for an entry a
+ *                request uses outside [0, num_pages) (it reads page 0 instead)
+ */
+spec_status spec_tree_attn_verify_paged(const void* q, spec_dtype q_dtype,
+                                        const void* k_pages, const void* v_pages, spec_dtype kv_dtype,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                        const int32_t* block_table, int max_pages, int page_size,
+                                        int num_pages, int B, int N, int Hq, int Hkv, int D,
+                                        float sm_scale, void* out, float* lse,
+                                        void* workspace, size_t workspace_bytes,
+                                        uint32_t* err_word, hipStream_t stream);
 
 /*
  * spec_vocab_argmax -- per-row argmax of float32 logits.

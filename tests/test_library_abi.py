@@ -128,3 +128,19 @@ def test_commit_host_checks(L):
     assert commit(shape=(4, 6, 8, 96, 2054)) == SPEC_ERR_SHAPE
     assert commit(shape=(0, 6, 8, 128, 2054)) == SPEC_ERR_SHAPE
     assert commit(shape=(4, 6, 8, 128, 5)) == SPEC_ERR_SHAPE
+
+
+def test_paged_attention_host_checks(L):
+    def paged(table=FAKE, qd=1, kvd=1, max_pages=40, page_size=16, num_pages=100, shape=(4, 6, 32, 8, 128),
+              scale=0.088):
+        return L.spec_tree_attn_verify_paged(FAKE, qd, FAKE, FAKE, kvd, None, None, FAKE, FAKE, table, max_pages,
+                                             page_size, num_pages, *shape, scale, FAKE, None, None, 0, None, None)
+    assert paged(table=None) == SPEC_ERR_NULL
+    assert paged(qd=0, kvd=0) == SPEC_ERR_DTYPE                     # no fp32 paged path
+    assert paged(kvd=2) == SPEC_ERR_NULL                            # fp8 pages need scales
+    assert paged(page_size=24) == SPEC_ERR_SHAPE                    # not a power of two
+    assert paged(max_pages=2049) == SPEC_ERR_SHAPE
+    assert paged(num_pages=0) == SPEC_ERR_SHAPE
+    assert paged(shape=(4, 65, 32, 8, 128)) == SPEC_ERR_SHAPE
+    assert paged(scale=-1.0) == SPEC_ERR_SHAPE
+    assert paged() == SPEC_ERR_WORKSPACE                            # every check passed but the workspace

@@ -15,21 +15,22 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify",
+    "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify", "tree_attn_verify_paged",
     "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "DERR_ROOT", "DERR_PARENT",
-    "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "library_path",
+    "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "DERR_PAGE", "library_path",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libspectree.so")
 
 SPEC_F32, SPEC_BF16, SPEC_FP8_E4M3 = 0, 1, 2
-DERR_ROOT, DERR_PARENT, DERR_PREFIX, DERR_TOKEN, DERR_PATH = 1, 2, 4, 8, 16
+DERR_ROOT, DERR_PARENT, DERR_PREFIX, DERR_TOKEN, DERR_PATH, DERR_PAGE = 1, 2, 4, 8, 16, 32
 MAX_NODES = 64
 
 _DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3fn: SPEC_FP8_E4M3}
 
 EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
+           "spec_tree_attn_verify_paged",
            "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted", "spec_status_string"]
 
 
@@ -58,6 +59,9 @@ def lib() -> ctypes.CDLL:
                                         c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_sz,
                                         c_p, c_p]
     L.spec_tree_attn_verify.restype = c_i
+    L.spec_tree_attn_verify_paged.argtypes = [c_p, c_i, c_p, c_p, c_i, c_p, c_p, c_p, c_p, c_p, c_i, c_i, c_i,
+                                              c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_sz, c_p, c_p]
+    L.spec_tree_attn_verify_paged.restype = c_i
     L.spec_vocab_argmax.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_p]
     L.spec_vocab_argmax.restype = c_i
     L.spec_accept_walk.argtypes = [c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p]
@@ -139,6 +143,36 @@ def tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc_mask, sm_scale, *, k_
         _ptr(k_scale), _ptr(v_scale), _ptr(prefix_lens), _ptr(anc_mask),
         B, N, Hq, Hkv, D, S_max, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _ptr(err), _stream(stream)))
+    return out, lse, err
+
+
+def tree_attn_verify_paged(q, k_pages, v_pages, prefix_lens, anc_mask, block_table, sm_scale, *,
+                           k_scale=None, v_scale=None, out=None, lse=None, want_lse=True, workspace=None,
+                           err=None, stream=None):
+    """Tree-masked attention over a paged cache: q [B][N][Hq][D] bf16; pages
+    [num_pages][page_size][Hkv][D] (bf16 or float8_e4m3fn); block_table
+    int32[B][max_pages]; returns (out, lse, err)."""
+    B, N, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_pages = block_table.shape[1]
+    dev = q.device
+    if q.dtype not in _DTYPE or k_pages.dtype not in _DTYPE or v_pages.dtype != k_pages.dtype:
+        raise SpecError(f"unsupported dtypes q={q.dtype} kv={k_pages.dtype}/{v_pages.dtype}")
+    if tuple(k_pages.shape) != (num_pages, page_size, Hkv, D) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise SpecError("k_pages / v_pages must be [num_pages][page_size][Hkv][D] matching q")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    ws_need = attn_workspace_bytes(B, N, Hq, Hkv, D, max_pages * page_size)
+    if workspace is None and ws_need:
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, dev)
+    _check(lib().spec_tree_attn_verify_paged(
+        _ptr(q), _DTYPE[q.dtype], _ptr(k_pages), _ptr(v_pages), _DTYPE[k_pages.dtype], _ptr(k_scale),
+        _ptr(v_scale), _ptr(prefix_lens), _ptr(anc_mask), _ptr(block_table), max_pages, page_size, num_pages,
+        B, N, Hq, Hkv, D, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _ptr(err),
+        _stream(stream)))
     return out, lse, err
 
 

@@ -197,6 +197,8 @@ struct SplitOccupancy {
 constexpr int kMinPiece = 128;
 // Requests per launch: every workgroup keeps a table of their lengths in LDS.
 constexpr int kMaxBatch = 1024;
+// Paged caches: a workgroup stages the page ids of its current piece in LDS.
+constexpr int kMaxPages = 2048;
 
 // One (request, kv head) token sequence of the concatenated work stream:
 // request b, kv head kvh, L = P_b + N tokens, starting at stream offset start.
@@ -205,7 +207,7 @@ struct Seg {
   long long start;
 };
 
-template <int D, int KVF, int RB, int WM, int WT, int NSTAGE>
+template <int D, int KVF, int RB, int WM, int WT, int NSTAGE, bool PAGED>
 __global__ __launch_bounds__(WM * WT * kWave)
 __attribute__((amdgpu_waves_per_eu(SplitOccupancy<D, RB, WM, WT, NSTAGE>::value)))
 void tree_attn_split_kernel(
@@ -215,7 +217,8 @@ void tree_attn_split_kernel(
     const uint64_t* __restrict__ anc_mask, int B, int N, int Hq, int Hkv, int S_max,
     float sm_scale, int split_len, int n_splits, int n_units, int n_mt, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word) {
+    uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word,
+    const int32_t* __restrict__ block_table, int max_pages, int ps_log2, int num_pages) {
   static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
   static_assert(NSTAGE >= 2 && NSTAGE <= 8, "ring depth");
   constexpr int NW = WM * WT;
@@ -239,6 +242,7 @@ void tree_attn_split_kernel(
   __shared__ __align__(1024) unsigned char smem[NSTAGE * 2 * TB];
   __shared__ int s_cum[kMaxBatch + 1];
   __shared__ uint32_t s_last;
+  __shared__ int s_pages[PAGED ? kMaxPages : 1];
   auto kst = [&](int st) -> unsigned char* { return smem + (2 * st) * TB; };
   auto vst = [&](int st) -> unsigned char* { return smem + (2 * st + 1) * TB; };
 
@@ -265,18 +269,52 @@ void tree_attn_split_kernel(
   // kbase / vbase; rows at or past t_end repeat row t_end - 1) into stage st:
   // wave w issues instructions w, w+NW, ...; lane l of instruction j fills LDS
   // bytes j*1024 + 16l, i.e. row j*RPI + l/UPR at swizzled unit l%UPR.
+  // Paged caches: kbase / vbase point at the kv head's row in the pool's first
+  // token, and token c of the sequence sits in page s_pages[c/page - pg0]
+  // (the page ids of the current piece, staged by stage_pages), with rows of
+  // Hkv * RBYTES bytes per token.
   auto dma_tile = [&](const unsigned char* kbase, const unsigned char* vbase, int t0, int t_end, int st,
-                      int wave, int lane) {
+                      int wave, int lane, int pg0) {
 #pragma unroll
     for (int qd = 0; qd < KPW; ++qd) {
       const int j = wave + qd * NW;
       const int row = j * RPI + lane / UPR;
       const int unit16 = (lane % UPR) ^ swz<UPR>(row);
-      const size_t c = (size_t)min(t0 + row, t_end - 1);
-      const size_t goff = c * RBYTES + unit16 * 16;
+      const int c = min(t0 + row, t_end - 1);
+      size_t goff;
+      if constexpr (PAGED) {
+        const size_t page = (size_t)s_pages[(c >> ps_log2) - pg0];
+        goff = ((page << ps_log2) | (size_t)(c & ((1 << ps_log2) - 1))) * ((size_t)Hkv * RBYTES) + unit16 * 16;
+      } else {
+        goff = (size_t)c * RBYTES + unit16 * 16;
+      }
       dma16(kbase + goff, LDS_ADDR(smem) + (2 * st) * TB + j * 1024);
       dma16(vbase + goff, LDS_ADDR(smem) + (2 * st + 1) * TB + j * 1024);
     }
+  };
+
+  // Paged caches: the page ids of tokens [t0, t1) of request b into s_pages
+  // (an id outside the pool is flagged and replaced by page 0, so no access
+  // leaves the pool), then a barrier.  Every wave of the workgroup calls it.
+  auto stage_pages = [&](int b, int t0, int t1) {
+    if constexpr (PAGED) {
+      const int pg0 = t0 >> ps_log2;
+      const int np = ((t1 - 1) >> ps_log2) - pg0 + 1;
+      for (int i = threadIdx.x; i < np; i += NW * kWave) {
+        int id = block_table[(size_t)b * max_pages + pg0 + i];
+        if (id < 0 || id >= num_pages) {
+          flag_error(err_word, SPEC_DERR_PAGE);
+          id = 0;
+        }
+        s_pages[i] = id;
+      }
+      __syncthreads();
+    }
+  };
+  // the kv head's K / V row base of sequence (b, kvh)
+  auto seq_base = [&](const unsigned char* pool, int b, int kvh) -> const unsigned char* {
+    if constexpr (PAGED) return pool + (size_t)kvh * RBYTES;
+    else return pool + ((size_t)(b * Hkv + kvh) * S_max) * RBYTES;
   };
 
   // ---- Q rows of a wave as MFMA B operands (K-slots 32c + 8lg .. +7) and
@@ -318,11 +356,13 @@ void tree_attn_split_kernel(
     f_seg = u / n_splits;
     f_begin = (u % n_splits) * split_len;
     f_end = min(S_max, f_begin + split_len);
-    const size_t off = (size_t)f_seg * S_max * RBYTES;
+    stage_pages(f_seg / Hkv, f_begin, f_end);
+    const unsigned char* kb = seq_base(kc, f_seg / Hkv, f_seg % Hkv);
+    const unsigned char* vb = seq_base(vc, f_seg / Hkv, f_seg % Hkv);
     const int nt = (f_end - f_begin + kTile - 1) / kTile;
 #pragma unroll
     for (int i = 0; i < NSTAGE - 1; ++i)
-      if (i < nt) dma_tile(kc + off, vc + off, f_begin + i * kTile, f_end, i, wave0, lane0);
+      if (i < nt) dma_tile(kb, vb, f_begin + i * kTile, f_end, i, wave0, lane0, f_begin >> ps_log2);
     load_q(f_seg / Hkv, f_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
   }
   // whether every raw prefix length in s_cum is S_max - N (after a barrier
@@ -489,15 +529,16 @@ void tree_attn_split_kernel(
       out_scale = v_scale[kvh];
     }
 
-    const size_t head_off = ((size_t)(b * Hkv + kvh) * S_max) * RBYTES;
-    const unsigned char* kbase = kc + head_off;
-    const unsigned char* vbase = vc + head_off;
+    const unsigned char* kbase = seq_base(kc, b, kvh);
+    const unsigned char* vbase = seq_base(vc, b, kvh);
+    const int pg0 = t_begin >> ps_log2;
 
-    auto issue = [&](int st, int i) { dma_tile(kbase, vbase, t_begin + i * kTile, t_end, st, wave, lane); };
+    auto issue = [&](int st, int i) { dma_tile(kbase, vbase, t_begin + i * kTile, t_end, st, wave, lane, pg0); };
 
     // tiles 0 .. NSTAGE-2 go in flight first; everything up to the wait below
     // runs in their shadow
     if (!fixed) {                                    // a fixed split's first tiles are in flight already
+      stage_pages(b, t_begin, t_end);
 #pragma unroll
       for (int i = 0; i < NSTAGE - 1; ++i)
         if (i < ntiles) issue(i, i);
@@ -1031,31 +1072,39 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   return true;
 }
 
-template <int D, int KVF, int RB, int WM, int WT, int NS>
+// Paged cache description (null table: contiguous caches).
+struct PagedArgs {
+  const int32_t* table;
+  int max_pages, ps_log2, num_pages;
+};
+
+template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED>
 static void launch_split(const AttnPlan& pl, const void* q, const void* k, const void* v,
                          const float* ks, const float* vs, const int32_t* pre, const uint64_t* anc,
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
                          float* lse, float* po, float2* pml, uint32_t* cnt, uint32_t* err,
-                         hipStream_t st) {
+                         const PagedArgs& pg, hipStream_t st) {
   const int units = std::max(B * Hkv * pl.n_splits, pl.n_units);
   const int units_pad = ((units + 7) / 8) * 8;
   const unsigned grid = (unsigned)units_pad * (unsigned)pl.n_mt;
-  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS>), dim3(grid), dim3(WM * WT * kWave),
-                     0, st, static_cast<const __bf16*>(q), static_cast<const unsigned char*>(k),
-                     static_cast<const unsigned char*>(v), ks, vs, pre, anc, B, N, Hq, Hkv, S_max,
-                     sm_scale, pl.split_len, pl.n_splits, pl.n_units, pl.n_mt, static_cast<__bf16*>(out), lse,
-                     po, pml, cnt, err);
+  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS, PAGED>), dim3(grid),
+                     dim3(WM * WT * kWave), 0, st, static_cast<const __bf16*>(q),
+                     static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), ks, vs, pre,
+                     anc, B, N, Hq, Hkv, S_max, sm_scale, pl.split_len, pl.n_splits, pl.n_units, pl.n_mt,
+                     static_cast<__bf16*>(out), lse, po, pml, cnt, err, pg.table, pg.max_pages, pg.ps_log2,
+                     pg.num_pages);
 }
 
-// Whether an instantiation is buildable: the ring fits the LDS, the tiles in
-// flight fit the vmcnt counter, the DMA splits evenly over the waves and the
-// token-split combine has scratch room.
-template <int D, int KVF, int RB, int WM, int WT, int NS>
+// Whether an instantiation is buildable: the ring (plus the length table and,
+// for paged caches, the page ids) fits the LDS, the tiles in flight fit the
+// vmcnt counter, the DMA splits evenly over the waves and the token-split
+// combine has scratch room.
+template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED>
 constexpr bool split_fits() {
   constexpr int TB = kTile * D * ((KVF == SPEC_BF16) ? 2 : 1);
   constexpr int NW = WM * WT;
   constexpr int NLOAD = TB / 1024;
-  if (NS * 2 * TB + kTableBytes > 160 * 1024) return false;
+  if (NS * 2 * TB + kTableBytes + (PAGED ? 4 * kMaxPages : 0) > 160 * 1024) return false;
   if (NLOAD % NW != 0) return false;
   if ((NS - 1) * 2 * (NLOAD / NW) >= 64) return false;   // a full ring start fits the vmcnt counter
   if (WT == 2 && WM * RB * (D / 16) * 1024 + WM * RB * 512 > NS * 2 * TB) return false;
@@ -1067,19 +1116,19 @@ constexpr bool split_fits() {
 #define SPEC_SPLIT_PLANS(X) X(1, 2, 2, 3) X(2, 2, 1, 2) X(2, 4, 1, 2)
 #endif
 
-template <int D, int KVF>
+template <int D, int KVF, bool PAGED>
 static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, const void* v,
                            const float* ks, const float* vs, const int32_t* pre,
                            const uint64_t* anc, int B, int N, int Hq, int Hkv, int S_max,
                            float sm_scale, void* out, float* lse, float* po, float2* pml,
-                           uint32_t* cnt, uint32_t* err, hipStream_t st) {
-#define SPEC_TRY(RB_, WM_, WT_, NS_)                                                               \
-  if constexpr (split_fits<D, KVF, RB_, WM_, WT_, NS_>()) {                                        \
-    if (pl.rb == RB_ && pl.wm == WM_ && pl.wt == WT_ && pl.nstage == NS_) {                        \
-      launch_split<D, KVF, RB_, WM_, WT_, NS_>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, \
-                                               sm_scale, out, lse, po, pml, cnt, err, st);        \
-      return true;                                                                                 \
-    }                                                                                              \
+                           uint32_t* cnt, uint32_t* err, const PagedArgs& pg, hipStream_t st) {
+#define SPEC_TRY(RB_, WM_, WT_, NS_)                                                                  \
+  if constexpr (split_fits<D, KVF, RB_, WM_, WT_, NS_, PAGED>()) {                                    \
+    if (pl.rb == RB_ && pl.wm == WM_ && pl.wt == WT_ && pl.nstage == NS_) {                           \
+      launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, \
+                                                      sm_scale, out, lse, po, pml, cnt, err, pg, st);   \
+      return true;                                                                                    \
+    }                                                                                                 \
   }
   SPEC_SPLIT_PLANS(SPEC_TRY)
 #undef SPEC_TRY
@@ -1097,6 +1146,42 @@ extern "C" size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, 
 }
 
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The bf16 / e4m3 split kernel for either cache layout (pg.table set: paged).
+static spec_status run_split(const AttnPlan& pl, bool bf16, const void* q, const void* k, const void* v,
+                             const float* k_scale, const float* v_scale, const int32_t* prefix_lens,
+                             const uint64_t* anc_mask, int B, int N, int Hq, int Hkv, int D, int S_max,
+                             float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             uint32_t* err_word, const PagedArgs& pg, hipStream_t stream) {
+  float* po = nullptr;
+  float2* pml = nullptr;
+  uint32_t* cnt = nullptr;
+  if (pl.ws_bytes) {
+    if (!workspace) return SPEC_ERR_WORKSPACE;
+    if (workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
+    const size_t rows = (size_t)std::max<long long>((long long)B * Hkv * pl.n_splits, 2ll * pl.n_units) * pl.M_pad;
+    po = static_cast<float*>(workspace);
+    pml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + rows * D * sizeof(float));
+    cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + rows * D * sizeof(float) +
+                                      rows * sizeof(float2));
+  }
+
+  const bool paged = pg.table != nullptr;
+#define SPEC_DISPATCH(D_, KVF_)                                                                           \
+  (paged ? dispatch_shape<D_, KVF_, true>(pl, q, k, v, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, \
+                                          S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, stream)     \
+         : dispatch_shape<D_, KVF_, false>(pl, q, k, v, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq,    \
+                                           Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, stream))
+  bool launched;
+  if (bf16) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_BF16) : SPEC_DISPATCH(128, SPEC_BF16);
+  else launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_FP8_E4M3) : SPEC_DISPATCH(128, SPEC_FP8_E4M3);
+#undef SPEC_DISPATCH
+  if (!launched) return SPEC_ERR_SHAPE;
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+
+  return SPEC_OK;
+}
 
 extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, const void* k_cache,
                                              const void* v_cache, spec_dtype kv_dtype,
@@ -1133,30 +1218,36 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
   }
 
-  float* po = nullptr;
-  float2* pml = nullptr;
-  uint32_t* cnt = nullptr;
-  if (pl.ws_bytes) {
-    if (!workspace) return SPEC_ERR_WORKSPACE;
-    if (workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
-    const size_t rows = (size_t)std::max<long long>((long long)B * Hkv * pl.n_splits, 2ll * pl.n_units) * pl.M_pad;
-    po = static_cast<float*>(workspace);
-    pml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + rows * D * sizeof(float));
-    cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + rows * D * sizeof(float) +
-                                      rows * sizeof(float2));
-  }
+  return run_split(pl, bf16, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
+                   S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word, PagedArgs{nullptr, 0, 0, 0},
+                   stream);
+}
 
-  bool launched;
-  if (bf16) {
-    if (D == 64) launched = dispatch_shape<64, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
-    else launched = dispatch_shape<128, SPEC_BF16>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
-  } else {
-    if (D == 64) launched = dispatch_shape<64, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
-    else launched = dispatch_shape<128, SPEC_FP8_E4M3>(pl, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, stream);
-  }
-  if (!launched) return SPEC_ERR_SHAPE;
-  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-
-  return SPEC_OK;
+extern "C" spec_status spec_tree_attn_verify_paged(const void* q, spec_dtype q_dtype, const void* k_pages,
+                                                   const void* v_pages, spec_dtype kv_dtype,
+                                                   const float* k_scale, const float* v_scale,
+                                                   const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                                   const int32_t* block_table, int max_pages, int page_size,
+                                                   int num_pages, int B, int N, int Hq, int Hkv, int D,
+                                                   float sm_scale, void* out, float* lse, void* workspace,
+                                                   size_t workspace_bytes, uint32_t* err_word,
+                                                   hipStream_t stream) {
+  if (!q || !k_pages || !v_pages || !prefix_lens || !anc_mask || !block_table || !out) return SPEC_ERR_NULL;
+  const bool bf16 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_BF16);
+  const bool fp8 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_FP8_E4M3);
+  if (!bf16 && !fp8) return SPEC_ERR_DTYPE;
+  if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
+  if (page_size < 1 || (page_size & (page_size - 1)) || page_size > 4096) return SPEC_ERR_SHAPE;
+  if (max_pages < 1 || max_pages > kMaxPages || num_pages < 1) return SPEC_ERR_SHAPE;
+  const int S_max = max_pages * page_size;
+  AttnPlan pl;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return SPEC_ERR_SHAPE;
+  if ((long long)num_pages * page_size * Hkv * D >= (1ll << 40)) return SPEC_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out)) return SPEC_ERR_ALIGN;
+  int ps_log2 = 0;
+  while ((1 << ps_log2) < page_size) ++ps_log2;
+  return run_split(pl, bf16, q, k_pages, v_pages, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
+                   S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
+                   PagedArgs{block_table, max_pages, ps_log2, num_pages}, stream);
 }
