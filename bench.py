@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="skip timing the commit step")
+    ap.add_argument("--page-size", type=int, default=16,
+                    help="also time the attention over a paged copy of the cache with this page size (0: skip)")
     ap.add_argument("--copy-calibration", type=float, default=0,
                     help="only run a plain float32 elementwise copy that reads and writes this many "
                          "bytes (5 launches) and exit: the reference point that scales the HBM byte "
@@ -362,6 +364,50 @@ def main():
         commit = dict(launch_us=round(commit_us, 3), bytes_per_launch=moved + B * N + 12 * B,
                       accept_len_sum=int(acc_len.sum().item()))
 
+    # ---- the same attention over a paged cache: every replica's K/V scattered
+    # into a shuffled pool of token-major pages, read through a block table
+    paged = None
+    if args.page_size:
+        ps = args.page_size
+        maxp = -(-w.S_max // ps)
+        num_pages = B * maxp
+        g = torch.Generator().manual_seed(11)
+        perm = torch.randperm(num_pages, generator=g).view(B, maxp).to(torch.int32)
+        table = perm.to(dev)
+        flat = perm.view(-1).long().to(dev)
+
+        def paginate(c):
+            pad = torch.zeros(B, w.Hkv, maxp * ps, w.D, dtype=c.dtype, device=dev)
+            pad[:, :, : w.S_max] = c
+            blocks = pad.view(B, w.Hkv, maxp, ps, w.D).permute(0, 2, 3, 1, 4).reshape(B * maxp, ps, w.Hkv, w.D)
+            pages = torch.empty_like(blocks)
+            pages[flat] = blocks
+            return pages
+
+        kps = [paginate(kcs[r]) for r in range(R)]
+        vps = [paginate(vcs[r]) for r in range(R)]
+        ws_p = torch.zeros(max(st.attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, maxp * ps), 16),
+                           dtype=torch.uint8, device=dev)
+        pg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pg):
+            for c in range(calls):
+                st.tree_attn_verify_paged(qs[c % R], kps[c % R], vps[c % R], prefix, anc, table, x["sm_scale"],
+                                          k_scale=ks, v_scale=vs, out=out, lse=lse, workspace=ws_p, err=err)
+        torch.cuda.synchronize()
+        pg.replay()
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for _ in range(reps):
+            pg.replay()
+        p1.record()
+        torch.cuda.synchronize()
+        paged_us = p0.elapsed_time(p1) * 1e3 / (reps * calls)
+        pbytes = bytes_["attention"] + B * maxp * 4
+        paged = dict(page_size=ps, launch_us=round(paged_us, 3), achieved_gbs=round(pbytes / paged_us / 1e3, 1),
+                     frac=round(pbytes / paged_us / 1e3 / PEAK_HBM_GBS, 4))
+        del kps, vps
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, args.cpu_baseline_seconds)
@@ -391,6 +437,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "commit_step": commit,
+        "paged_attention": paged,
     }
     print(json.dumps(line), flush=True)
 
