@@ -21,18 +21,35 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 
 SHORT = ("tree_attn_split_kernel", "tree_attn_f32_kernel", "vocab_argmax_kernel", "accept_walk_kernel",
-         "tree_mask_build_kernel")
+         "tree_mask_build_kernel", "commit_accepted_kernel")
+
+
+def _mangled_args(tail: str) -> str:
+    """Template arguments of an Itanium-mangled name made of integer and bool
+    literals only (``ILi128ELb0EE`` -> ``<128,false>``); '' otherwise."""
+    m = re.match(r"I((?:L[a-z]-?\d+E)+)E", tail)
+    if not m:
+        return ""
+    vals = []
+    for kind, v in re.findall(r"L([a-z])(-?\d+)E", m.group(1)):
+        vals.append(("true" if v != "0" else "false") if kind == "b" else v)
+    return "<" + ",".join(vals) + ">"
 
 
 def short_name(name: str) -> str:
+    """Kernel name without namespace and argument list, template arguments kept
+    (demangled names from the trace, or mangled ones from the counter runs)."""
     for k in SHORT:
         if k in name:
             tpl = name.split(k, 1)[1]
-            return k + (tpl[:tpl.find("(")] if tpl.startswith("<") else "")
+            if tpl.startswith("<"):
+                return k + tpl[:tpl.find("(")]
+            return k + _mangled_args(tpl)
     if "elementwise" in name.lower():
         return "elementwise:" + name[:56]
     return name[:70]
@@ -109,11 +126,14 @@ def main(argv=None):
         fetch, write, cfetch, cwrite = (pmc(d) for d in a.dirs)
 
         def avg(agg, kern, ctr):
-            for k, ctrs in agg.items():
-                if k.startswith(kern) and ctr in ctrs:
-                    v = ctrs[ctr]
-                    return sum(v) / len(v)
-            raise SystemExit(f"no {ctr} for {kern}")
+            # the exact name (template arguments included), else the one kernel it prefixes
+            hits = [k for k, ctrs in agg.items() if ctr in ctrs and (k == kern or k.startswith(kern + "<"))]
+            if kern in hits:
+                hits = [kern]
+            if len(hits) != 1:
+                raise SystemExit(f"{ctr} for {kern}: {'none' if not hits else 'ambiguous: ' + ', '.join(hits)}")
+            v = agg[hits[0]][ctr]
+            return sum(v) / len(v)
 
         def copy_avg(agg, ctr):
             best = None
