@@ -83,7 +83,7 @@ def pmc(d):
     return agg
 
 
-ATTENTION_SOURCES = ("common.h", "tree_attn.hip")
+ATTENTION_SOURCES = ("common.h", "gfx950.h", "tree_attn.hip")
 
 
 def source_sha(root):
