@@ -19,6 +19,9 @@ What is computed, and where the pages say so:
   * The accepted and rejected outcomes of each verification are what the
     serving engine streams on (Aurora, section 2): the commit step keeps the
     accepted path's K/V rows and labels every node.
+  * The draft model is trained on all accepted and rejected branches in one
+    batched forward and backward pass under the same tree mask (Aurora,
+    section 2, closing paragraph): the attention's backward pass.
 
 Everything is plain: explicit parent-pointer walks, a dense boolean mask,
 naive softmax in float64, a linear argmax, a recursive accept walk.
@@ -36,10 +39,12 @@ from .argmax import vocab_argmax
 from .step import verify_step
 from .commit import commit_accepted, LABEL_ACCEPTED, LABEL_REJECTED, LABEL_ROOT
 from .paged import gather_pages
+from .attention_bwd import tree_attention_backward
 
 __all__ = [
     "ancestors", "build_masks", "accept_walk", "children_of",
     "bf16_bits_to_f64", "e4m3_decode_table", "decode_e4m3", "dense_tree_mask",
     "tree_attention_bh", "tree_attention", "vocab_argmax", "verify_step",
     "commit_accepted", "LABEL_ACCEPTED", "LABEL_REJECTED", "LABEL_ROOT", "gather_pages",
+    "tree_attention_backward",
 ]

@@ -448,3 +448,145 @@ def check_gather_pages_identity(gather_pages):
     table = np.arange(B * maxp).reshape(B, maxp)
     want = pages.reshape(B, maxp * ps, Hkv, 5).transpose(0, 2, 1, 3)
     assert np.array_equal(gather_pages(pages, table, ps, maxp * ps), want)
+
+
+# ---------------------------------------------------------------- backward
+
+def _backward_case(rng, B, N, Hq, Hkv, D, P, tree="random"):
+    parents, prefix, q, k, v = rand_case(rng, B, N, Hq, Hkv, D, P, tree=tree)
+    d_out = rng.standard_normal(q.shape).astype(np.float32)
+    return parents, prefix, q, k, v, d_out
+
+
+def _dense_mask_by_walk(parents_b, P):
+    """bool[N][P+N] by parent-pointer chase, written here so the pin does not
+    lean on the oracle's own mask."""
+    N = len(parents_b)
+    A = np.zeros((N, P + N), dtype=bool)
+    A[:, :P] = True
+    for i in range(N):
+        j = i
+        while j != -1:
+            A[i, P + j] = True
+            j = int(parents_b[j])
+    return A
+
+
+def _torch_loss(q, k, v, d_out, parents, prefix, scale, Hq, Hkv):
+    """sum <dO, out> through torch's float64 SDPA (math path), GQA by
+    repeat_interleave; q, k, v are float64 leaf tensors."""
+    g = Hq // Hkv
+    B, N = q.shape[0], q.shape[1]
+    total = torch.zeros((), dtype=torch.float64)
+    for b in range(B):
+        Pb = int(prefix[b])
+        L = Pb + N
+        A = torch.from_numpy(_dense_mask_by_walk(parents[b], Pb))
+        kk = k[b, :, :L].repeat_interleave(g, dim=0)                  # [Hq][L][D]
+        vv = v[b, :, :L].repeat_interleave(g, dim=0)
+        qq = q[b].transpose(0, 1)                                      # [Hq][N][D]
+        o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=A, scale=scale)
+        total = total + (o.transpose(0, 1) * torch.from_numpy(d_out[b].astype(np.float64))).sum()
+    return total
+
+
+def check_backward_autograd(tree_attention_backward, seed: int = 10):
+    """Gradients equal torch autograd through float64 SDPA with the dense tree
+    mask, for random trees, ragged prefixes and GQA."""
+    rng = np.random.default_rng(seed)
+    for (B, N, Hq, Hkv, D, P) in [(2, 7, 4, 2, 8, [5, 0]), (1, 9, 6, 3, 4, 11), (2, 5, 2, 2, 16, [2, 9])]:
+        parents, prefix, q, k, v, d_out = _backward_case(rng, B, N, Hq, Hkv, D, P)
+        sc = 0.4
+        dq, dk, dv = tree_attention_backward(q, k, v, prefix, parents, d_out, sc, q_fmt="f32", kv_fmt="f32")
+        tq, tk, tv = (torch.from_numpy(x.astype(np.float64)).requires_grad_(True) for x in (q, k, v))
+        _torch_loss(tq, tk, tv, d_out, parents, prefix, sc, Hq, Hkv).backward()
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def check_backward_finite_differences(tree_attention_backward, seed: int = 11):
+    """Central differences of sum <dO, out> (out from torch's float64 SDPA)
+    at a sample of q, K and V entries agree with the gradients."""
+    rng = np.random.default_rng(seed)
+    B, N, Hq, Hkv, D = 1, 6, 4, 2, 4
+    parents, prefix, q, k, v, d_out = _backward_case(rng, B, N, Hq, Hkv, D, [3])
+    sc, h = 0.6, 1e-6
+    dq, dk, dv = tree_attention_backward(q, k, v, prefix, parents, d_out, sc, q_fmt="f32", kv_fmt="f32")
+    base = [torch.from_numpy(x.astype(np.float64)) for x in (q, k, v)]
+
+    def loss(which, idx, delta):
+        xs = [t.clone() for t in base]
+        xs[which][idx] += delta
+        return float(_torch_loss(*xs, d_out, parents, prefix, sc, Hq, Hkv))
+
+    L = int(prefix[0]) + N
+    picks = [(0, (0, i, hh, d)) for i in range(N) for hh in (0, 3) for d in (0, 2)]
+    picks += [(w, (0, kvh, c, d)) for w in (1, 2) for kvh in (0, 1) for c in range(L) for d in (1, 3)]
+    picks += [(1, (0, 0, L, 0)), (2, (0, 1, L + 1, 2))]                 # rows past the tree
+    grads = (dq, dk, dv)
+    for which, idx in picks:
+        fd = (loss(which, idx, h) - loss(which, idx, -h)) / (2 * h)
+        assert abs(grads[which][idx] - fd) <= 1e-7 + 1e-6 * abs(fd), (which, idx, grads[which][idx], fd)
+
+
+def check_backward_invariants(tree_attention_backward, seed: int = 12):
+    """Sum over keys of dK is zero (each row's softmax gradient sums to zero);
+    sum over keys of dV is the sum of dO over the rows sharing the kv head
+    (each row's weights sum to one); rows past the tree get nothing."""
+    rng = np.random.default_rng(seed)
+    B, N, Hq, Hkv, D = 3, 8, 6, 2, 5
+    parents, prefix, q, k, v, d_out = _backward_case(rng, B, N, Hq, Hkv, D, [0, 4, 13])
+    dq, dk, dv = tree_attention_backward(q, k, v, prefix, parents, d_out, 0.8, q_fmt="f32", kv_fmt="f32")
+    g = Hq // Hkv
+    for b in range(B):
+        L = int(prefix[b]) + N
+        for kvh in range(Hkv):
+            np.testing.assert_allclose(dk[b, kvh, :L].sum(axis=0), 0.0, atol=1e-12)
+            want = d_out[b, :, kvh * g:(kvh + 1) * g].astype(np.float64).sum(axis=(0, 1))
+            np.testing.assert_allclose(dv[b, kvh, :L].sum(axis=0), want, rtol=1e-12, atol=1e-12)
+            assert not dk[b, kvh, L:].any() and not dv[b, kvh, L:].any()
+
+
+def check_backward_subtree_locality(tree_attention_backward, seed: int = 13):
+    """With dO non-zero for one node i only, the tree rows that receive K/V
+    gradient are exactly i's ancestors-or-self (the prefix rows all do)."""
+    rng = np.random.default_rng(seed)
+    B, N, Hq, Hkv, D, P = 1, 10, 2, 1, 4, 3
+    parents, prefix, q, k, v, d_out = _backward_case(rng, B, N, Hq, Hkv, D, [P])
+    for i in range(N):
+        d1 = np.zeros_like(d_out)
+        d1[0, i] = d_out[0, i]
+        _, dk, dv = tree_attention_backward(q, k, v, prefix, parents, d1, 0.5, q_fmt="f32", kv_fmt="f32")
+        chain, j = set(), i
+        while j != -1:
+            chain.add(j)
+            j = int(parents[0][j])
+        for jj in range(N):
+            hit = bool(np.abs(dv[0, 0, P + jj]).sum() > 0)
+            assert hit == (jj in chain), (i, jj)
+            if jj not in chain:
+                assert not dk[0, 0, P + jj].any()
+        assert np.abs(dv[0, 0, :P]).sum(axis=1).min() > 0
+
+
+def check_backward_closed_form(tree_attention_backward):
+    """P = 0, root and one child, D = 1, sm_scale = 1.  The root sees only its
+    own key: dq_root = 0 and its dO goes to v_0 whole.  The child has weights
+    w0, w1 = softmax(q1 k0, q1 k1): d out1/d q1 = w0 w1 (k1 - k0)(v1 - v0),
+    d out1/d k1 = -d out1/d k0 = q1 w0 w1 (v1 - v0), d out1/d v_c = w_c."""
+    q0, q1, k0, k1, v0, v1, a, c = 0.5, 1.5, 2.0, -1.0, 3.0, 7.0, 0.25, -2.0
+    q = np.array([[[[q0]], [[q1]]]], dtype=np.float32)
+    k = np.array([[[[k0], [k1]]]], dtype=np.float32)
+    v = np.array([[[[v0], [v1]]]], dtype=np.float32)
+    dO = np.array([[[[a]], [[c]]]], dtype=np.float32)
+    dq, dk, dv = tree_attention_backward(q, k, v, np.array([0]), np.array([[-1, 0]]), dO, 1.0,
+                                         q_fmt="f32", kv_fmt="f32")
+    e0, e1 = math.exp(q1 * k0), math.exp(q1 * k1)
+    w0, w1 = e0 / (e0 + e1), e1 / (e0 + e1)
+    assert dq[0, 0, 0, 0] == 0.0
+    assert abs(dq[0, 1, 0, 0] - c * w0 * w1 * (k1 - k0) * (v1 - v0)) < 1e-14
+    assert abs(dk[0, 0, 1, 0] - c * q1 * w0 * w1 * (v1 - v0)) < 1e-14
+    assert abs(dk[0, 0, 0, 0] + c * q1 * w0 * w1 * (v1 - v0)) < 1e-14
+    assert abs(dv[0, 0, 0, 0] - (a + c * w0)) < 1e-14
+    assert abs(dv[0, 0, 1, 0] - c * w1) < 1e-14

@@ -22,7 +22,7 @@ def load_mutant(edits):
     pkg.__path__ = []
     sys.modules[name] = pkg
     try:
-        for mod in ("tree", "attention", "argmax", "step", "commit"):
+        for mod in ("tree", "attention", "argmax", "step", "commit", "attention_bwd"):
             with open(os.path.join(ORACLE_DIR, mod + ".py")) as f:
                 src = f.read()
             for (fname, old, new) in edits:
@@ -103,6 +103,19 @@ MUTANTS = {
     "commit_source_by_depth": ([("commit", "src = P + path[k]", "src = P + k")],
                                lambda o: pins.check_commit_against_parent_chase(o.commit.commit_accepted,
                                                                                 o.tree.accept_walk)),
+    # backward pass
+    "bwd_no_softmax_mean": ([("attention_bwd", "ds = w * (dw - (w * dw).sum(axis=1, keepdims=True))", "ds = w * dw")],
+                            lambda o: pins.check_backward_invariants(o.attention_bwd.tree_attention_backward)),
+    "bwd_dw_from_k": ([("attention_bwd", "dw = dO @ Vf.T", "dw = dO @ Kf.T")],
+                      lambda o: pins.check_backward_autograd(o.attention_bwd.tree_attention_backward)),
+    "bwd_dq_unscaled": ([("attention_bwd", "dQ = float(sm_scale) * (ds @ Kf)", "dQ = ds @ Kf")],
+                        lambda o: pins.check_backward_finite_differences(o.attention_bwd.tree_attention_backward)),
+    "bwd_dk_from_weights": ([("attention_bwd", "dK = float(sm_scale) * (ds.T @ Q)", "dK = float(sm_scale) * (w.T @ Q)")],
+                            lambda o: pins.check_backward_invariants(o.attention_bwd.tree_attention_backward)),
+    "bwd_unmasked_weights": ([("attention_bwd", "    s = np.where(A, s, -np.inf)\n", "")],
+                             lambda o: pins.check_backward_subtree_locality(o.attention_bwd.tree_attention_backward)),
+    "bwd_dv_last_head_only": ([("attention_bwd", "dv[b, kvh, :L] += dVh", "dv[b, kvh, :L] = dVh")],
+                              lambda o: pins.check_backward_invariants(o.attention_bwd.tree_attention_backward)),
 }
 
 
