@@ -12,6 +12,7 @@
  *   spec_vocab_argmax      per-node argmax of the target logits
  *   spec_accept_walk       longest matched root-to-node path -> accepted tokens
  *   spec_commit_accepted   (after the step) keep the accepted path's K/V, label outcomes
+ *   spec_tree_attn_backward (training) gradients of the tree-masked attention
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -255,6 +256,54 @@ spec_status spec_commit_accepted(void* k_cache, void* v_cache, spec_dtype kv_dty
                                  const int32_t* path_nodes, int B, int N, int Hkv, int D, int S_max,
                                  int32_t* new_prefix_lens, int8_t* node_labels,
                                  uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_tree_attn_backward_workspace_bytes -- scratch needed by
+ * spec_tree_attn_backward for these sizes.  Pure function of its arguments;
+ * 0 when the sizes need none or would be rejected.
+ */
+size_t spec_tree_attn_backward_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max);
+
+/*
+ * spec_tree_attn_backward -- gradients of spec_tree_attn_verify's attention.
+ *
+ * The draft model is trained on all accepted and rejected branches of a
+ * verification in one batched forward and backward pass under the same tree
+ * mask (Aurora, section 2, closing paragraph).  With the notation of
+ * spec_tree_attn_verify (keys c < L = P + N of request b, kv head kvh, the
+ * mask, sm_scale) and the upstream gradient dO of every output row, this
+ * returns the gradients of  sum_{b,i,h} <dO[b][i][h], out[b][i][h]>:
+ *     p_c   = exp(s_c - lse[b][i][h]) on visible keys, 0 elsewhere
+ *     ds_c  = sm_scale * p_c * (<dO[b][i][h], V[c]> - <dO[b][i][h], out[b][i][h]>)
+ *     dq[b][i][h]  = sum_c ds_c K[c]
+ *     dk[b][kvh][c] = sum over (i, h in kvh's group) of ds_c q[b][i][h]
+ *     dv[b][kvh][c] = sum over (i, h in kvh's group) of p_c dO[b][i][h]
+ *
+ *   q, out, d_out [B][N][Hq][D] of dtype, 16-B aligned; out and lse are the
+ *                 forward pass's results for the same inputs
+ *   k_cache,
+ *   v_cache       [B][Hkv][S_max][D] of dtype, 16-B aligned
+ *   dtype         SPEC_F32 (all fp32) or SPEC_BF16 (all bf16)
+ *   lse           float[B][N][Hq], required
+ *   D             64 or 128
+ *   Hq/Hkv * N    at most 128
+ *   dq            out: [B][N][Hq][D] of dtype
+ *   dk, dv        out: [B][Hkv][S_max][D] of dtype; rows c < P_b + N are
+ *                 written, later rows are left as they are
+ *   workspace     >= spec_tree_attn_backward_workspace_bytes(...) bytes,
+ *                 16-B aligned, zero-filled before its first use and left
+ *                 zeroed by every call (the same rules as the forward pass's)
+ *   err_word      nullable: SPEC_DERR_PREFIX
+ * Accumulation is fp32; bf16 results are rounded to nearest even.  The sum
+ * over a request's keys is taken in a fixed order, so results are
+ * deterministic.
+ */
+spec_status spec_tree_attn_backward(const void* q, const void* k_cache, const void* v_cache, spec_dtype dtype,
+                                    const int32_t* prefix_lens, const uint64_t* anc_mask, const void* out,
+                                    const float* lse, const void* d_out, int B, int N, int Hq, int Hkv,
+                                    int D, int S_max, float sm_scale, void* dq, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                    hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* spec_status_string(spec_status status);

@@ -218,6 +218,21 @@ def make_inputs(w: Workload, seed: Optional[int] = None, with_logits: bool = Tru
     )
 
 
+def make_backward_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """The verify-step inputs of ``w`` (without logits) plus an upstream
+    gradient d_out [B][N][Hq][D] ~ N(0, 1) in q's dtype, drawn from a stream
+    of its own, for the attention's backward pass.  fp8 caches are not
+    differentiated: ``w`` must use f32 or bf16 K/V."""
+    if w.kv_dtype not in ("f32", "bf16"):
+        raise ValueError("the backward pass takes f32 or bf16 caches")
+    x = make_inputs(w, seed, with_logits=False)
+    seed = w.seed if seed is None else seed
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xB0]).generate_state(2)))
+    g = r.standard_normal((w.B, w.N, w.Hq, w.D), dtype=np.float32)
+    x["d_out"] = _to_storage(g, w.q_dtype)
+    return x
+
+
 def _kv_storage(x: np.ndarray, w: Workload):
     if w.kv_dtype == "e4m3":
         return quantize_e4m3_per_head(x)

@@ -103,3 +103,44 @@ def check_integers(got: dict, want: dict, what: str = "") -> None:
     assert np.array_equal(got["accept_len"], want["accept_len"]), f"{what}: accept_len"
     assert np.array_equal(got["path_nodes"], want["path_nodes"]), f"{what}: path_nodes"
     assert np.array_equal(got["out_tokens"], want["out_tokens"]), f"{what}: out_tokens"
+
+
+# Backward-pass gradients: |gpu - oracle| <= a * max_b|oracle| + r * |oracle|
+# elementwise per request b, relative L2 <= 1e-2 over the tensor and over the
+# tree rows of dK / dV (the reasoning is in tests/test_gpu_backward.py).
+GRAD_TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
+
+
+def check_grad(got, want, what, fmt):
+    """got / want: lists with one array per request (that request's rows)."""
+    a, r = GRAD_TOL[fmt]
+    worst, num, den, max_abs = 0.0, 0.0, 0.0, 0.0
+    for gb, wb in zip(got, want):
+        gb = np.asarray(gb, dtype=np.float64)
+        wb = np.asarray(wb, dtype=np.float64)
+        assert np.isfinite(gb).all(), f"{what}: non-finite"
+        scale = float(np.abs(wb).max())
+        err = np.abs(gb - wb)
+        worst = max(worst, float((err / (a * scale + r * np.abs(wb))).max()))
+        max_abs = max(max_abs, float(err.max()))
+        num += float(np.sum((gb - wb) ** 2))
+        den += float(np.sum(wb ** 2))
+    rel = (num / max(den, 1e-300)) ** 0.5
+    log(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst/bound={worst:.3f}")
+    assert worst <= 1.0 and rel <= 1e-2, (what, worst, rel)
+
+
+def per_request(dq, dk, dv, prefix, N):
+    """Each request's dq, and its dk / dv rows below P_b + N."""
+    L = [int(p) + N for p in prefix]
+    return ([dq[b] for b in range(len(L))], [dk[b][:, :L[b]] for b in range(len(L))],
+            [dv[b][:, :L[b]] for b in range(len(L))])
+
+
+def check_tree_rows(dk, dv, rk, rv, prefix, N):
+    for gname, G, R in (("dk", dk, rk), ("dv", dv, rv)):
+        g = np.concatenate([G[b][:, int(p):int(p) + N].ravel() for b, p in enumerate(prefix)]).astype(np.float64)
+        r = np.concatenate([R[b][:, int(p):int(p) + N].ravel() for b, p in enumerate(prefix)])
+        rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+        log(f"  {gname} tree rows: rel_l2={rel:.3e}")
+        assert rel <= 1e-2, (gname, rel)

@@ -144,3 +144,32 @@ def test_paged_attention_host_checks(L):
     assert paged(shape=(4, 65, 32, 8, 128)) == SPEC_ERR_SHAPE
     assert paged(scale=-1.0) == SPEC_ERR_SHAPE
     assert paged() == SPEC_ERR_WORKSPACE                            # every check passed but the workspace
+
+
+def test_backward_workspace_bytes(L):
+    f = L.spec_tree_attn_backward_workspace_bytes
+    # M = 24 rows padded to 32; 33 tiles of 64 keys in runs of 3 -> 11 runs per (request, kv head):
+    # one fp32 partial of 32 x 128 per run, one counter per (request, kv head)
+    assert f(8, 6, 32, 8, 128, 2054) == 64 * 11 * 32 * 128 * 4 + 64 * 4
+    assert f(1, 6, 4, 1, 64, 134) == 2 * 32 * 64 * 4 + 4             # 3 tiles in runs of 2: 2 runs
+    assert f(64, 16, 64, 8, 128, 64) == 0                            # one tile: dq is written directly
+    for bad in [(8, 6, 32, 8, 96, 2054), (8, 17, 64, 8, 128, 2054), (8, 6, 30, 8, 128, 2054),
+                (0, 6, 32, 8, 128, 2054), (8, 6, 32, 8, 128, 5)]:
+        assert f(*bad) == 0, bad
+
+
+def test_backward_host_checks(L):
+    def bwd(q=FAKE, dt=1, lse=FAKE, dq=FAKE, shape=(8, 6, 32, 8, 128, 2054), scale=0.088, ws=None, wsb=0):
+        return L.spec_tree_attn_backward(q, FAKE, FAKE, dt, FAKE, FAKE, FAKE, lse, FAKE, *shape, scale, dq,
+                                         FAKE, FAKE, ws, wsb, None, None)
+    assert bwd(q=None) == SPEC_ERR_NULL
+    assert bwd(lse=None) == SPEC_ERR_NULL                         # the forward pass's lse is required
+    assert bwd(dq=None) == SPEC_ERR_NULL
+    assert bwd(dt=2) == SPEC_ERR_DTYPE                            # no fp8 gradients
+    assert bwd(shape=(8, 17, 64, 8, 128, 2054)) == SPEC_ERR_SHAPE  # 8 x 17 rows > 128
+    assert bwd(shape=(8, 6, 32, 8, 96, 2054)) == SPEC_ERR_SHAPE
+    assert bwd(scale=0.0) == SPEC_ERR_SHAPE
+    assert bwd(q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
+    assert bwd() == SPEC_ERR_WORKSPACE
+    need = L.spec_tree_attn_backward_workspace_bytes(8, 6, 32, 8, 128, 2054)
+    assert bwd(ws=FAKE, wsb=need - 1) == SPEC_ERR_WORKSPACE

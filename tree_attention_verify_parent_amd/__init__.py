@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify", "tree_attn_verify_paged",
-    "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "DERR_ROOT", "DERR_PARENT",
+    "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "attn_backward_workspace_bytes",
+    "tree_attn_backward", "DERR_ROOT", "DERR_PARENT",
     "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "DERR_PAGE", "library_path",
 ]
 
@@ -31,7 +32,8 @@ _DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3f
 
 EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
            "spec_tree_attn_verify_paged",
-           "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted", "spec_status_string"]
+           "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted",
+           "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_status_string"]
 
 
 class SpecError(RuntimeError):
@@ -68,6 +70,11 @@ def lib() -> ctypes.CDLL:
     L.spec_accept_walk.restype = c_i
     L.spec_commit_accepted.argtypes = [c_p, c_p, c_i, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p]
     L.spec_commit_accepted.restype = c_i
+    L.spec_tree_attn_backward_workspace_bytes.argtypes = [c_i] * 6
+    L.spec_tree_attn_backward_workspace_bytes.restype = c_sz
+    L.spec_tree_attn_backward.argtypes = [c_p, c_p, c_p, c_i, c_p, c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_i,
+                                          c_f, c_p, c_p, c_p, c_p, c_sz, c_p, c_p]
+    L.spec_tree_attn_backward.restype = c_i
     L.spec_status_string.argtypes = [c_i]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -220,6 +227,41 @@ def commit_accepted(k_cache, v_cache, prefix_lens, accept_len, path_nodes, *, ne
                                       _ptr(accept_len), _ptr(path_nodes), B, N, Hkv, D, S_max,
                                       _ptr(new_prefix_lens), _ptr(labels), _ptr(err), _stream(stream)))
     return new_prefix_lens, labels, err
+
+
+def attn_backward_workspace_bytes(B, N, Hq, Hkv, D, S_max) -> int:
+    return int(lib().spec_tree_attn_backward_workspace_bytes(B, N, Hq, Hkv, D, S_max))
+
+
+def tree_attn_backward(q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, sm_scale, *, dq=None,
+                       dk=None, dv=None, workspace=None, err=None, stream=None):
+    """Backward pass of tree_attn_verify: q, out, d_out [B][N][Hq][D] and
+    caches [B][Hkv][S_max][D], all float32 or all bf16; lse float32[B][N][Hq]
+    from the forward pass.  Returns (dq, dk, dv, err).  Rows of dk / dv at or
+    past prefix_lens[b] + N are not written (zero when allocated here)."""
+    B, N, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    dts = {q.dtype, k_cache.dtype, v_cache.dtype, out.dtype, d_out.dtype}
+    if len(dts) != 1 or q.dtype not in (torch.float32, torch.bfloat16):
+        raise SpecError(f"q, caches, out and d_out must share one dtype, float32 or bfloat16: {dts}")
+    if tuple(k_cache.shape) != (B, Hkv, S_max, D) or tuple(v_cache.shape) != (B, Hkv, S_max, D):
+        raise SpecError("k_cache / v_cache must be [B][Hkv][S_max][D] matching q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(d_out.shape) != tuple(q.shape):
+        raise SpecError("out and d_out must have q's shape")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.zeros_like(k_cache) if dk is None else dk
+    dv = torch.zeros_like(v_cache) if dv is None else dv
+    ws_need = attn_backward_workspace_bytes(B, N, Hq, Hkv, D, S_max)
+    if workspace is None and ws_need:
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, dev)
+    _check(lib().spec_tree_attn_backward(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _DTYPE[q.dtype], _ptr(prefix_lens), _ptr(anc_mask), _ptr(out),
+        _ptr(lse), _ptr(d_out), B, N, Hq, Hkv, D, S_max, float(sm_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), ws_bytes, _ptr(err), _stream(stream)))
+    return dq, dk, dv, err
 
 
 def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *,
