@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="skip timing the commit step")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the attention's backward pass")
     ap.add_argument("--page-size", type=int, default=16,
                     help="also time the attention over a paged copy of the cache with this page size (0: skip)")
     ap.add_argument("--copy-calibration", type=float, default=0,
@@ -408,6 +409,43 @@ def main():
                      frac=round(pbytes / paged_us / 1e3 / PEAK_HBM_GBS, 4))
         del kps, vps
 
+    # ---- the attention's backward pass (training on the verified tree):
+    # back-to-back calls over the replicas, each writing its own dK / dV
+    backward = None
+    if not args.no_backward and w.kv_dtype in ("f32", "bf16") and w.group * N <= 128:
+        gd = torch.Generator().manual_seed(12)
+        d_out = torch.randn(q0.shape, generator=gd).to(q0.dtype).to(dev)
+        out_b = out.clone()
+        lse_b = lse.clone()
+        dq_b = torch.empty_like(q0)
+        dks = [torch.empty_like(k0) for _ in range(R)]
+        dvs = [torch.empty_like(v0) for _ in range(R)]
+        ws_b = torch.zeros(max(st.attn_backward_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, w.S_max), 16),
+                           dtype=torch.uint8, device=dev)
+        bg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bg):
+            for c in range(calls):
+                st.tree_attn_backward(qs[c % R], kcs[c % R], vcs[c % R], prefix, anc, out_b, lse_b, d_out,
+                                      x["sm_scale"], dq=dq_b, dk=dks[c % R], dv=dvs[c % R], workspace=ws_b,
+                                      err=err)
+        torch.cuda.synchronize()
+        bg.replay()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(reps):
+            bg.replay()
+        b1.record()
+        torch.cuda.synchronize()
+        bwd_us = b0.elapsed_time(b1) * 1e3 / (reps * calls)
+        q_bytes = q0.numel() * q0.element_size()
+        # K, V read and dK, dV written once; q, out, dO read and dq written once
+        bbytes = 2 * bytes_["kv"] + 4 * q_bytes + 4 * B * N * w.Hq + 8 * B * N + 4 * B
+        backward = dict(kernel="tree_attn_bwd_kernel", launch_us=round(bwd_us, 3), bytes_per_launch=bbytes,
+                        achieved_gbs=round(bbytes / bwd_us / 1e3, 1),
+                        frac=round(bbytes / bwd_us / 1e3 / PEAK_HBM_GBS, 4))
+        del dks, dvs
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, args.cpu_baseline_seconds)
@@ -438,6 +476,7 @@ def main():
         "cpu_baseline": cpu,
         "commit_step": commit,
         "paged_attention": paged,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 

@@ -148,10 +148,13 @@ def test_paged_attention_host_checks(L):
 
 def test_backward_workspace_bytes(L):
     f = L.spec_tree_attn_backward_workspace_bytes
-    # M = 24 rows padded to 32; 33 tiles of 64 keys in runs of 3 -> 11 runs per (request, kv head):
-    # one fp32 partial of 32 x 128 per run, one counter per (request, kv head)
-    assert f(8, 6, 32, 8, 128, 2054) == 64 * 11 * 32 * 128 * 4 + 64 * 4
-    assert f(1, 6, 4, 1, 64, 134) == 2 * 32 * 64 * 4 + 4             # 3 tiles in runs of 2: 2 runs
+    # M = 24 rows padded to 32; 64 (request, kv head) sequences of 33 tiles of 64 keys, 4 runs each to
+    # give the 256 CUs a workgroup each (runs of 9 tiles): one fp32 partial of 32 x 128 per run, one
+    # counter per sequence
+    assert f(8, 6, 32, 8, 128, 2054) == 64 * 4 * 32 * 128 * 4 + 64 * 4
+    assert f(1, 6, 4, 1, 64, 134) == 3 * 32 * 64 * 4 + 4             # 3 tiles: runs of one tile
+    # no run longer than 64 tiles: 512 sequences of 129 tiles -> 3 runs of 43
+    assert f(64, 16, 64, 8, 128, 8208) == 512 * 3 * 128 * 128 * 4 + 512 * 4
     assert f(64, 16, 64, 8, 128, 64) == 0                            # one tile: dq is written directly
     for bad in [(8, 6, 32, 8, 96, 2054), (8, 17, 64, 8, 128, 2054), (8, 6, 30, 8, 128, 2054),
                 (0, 6, 32, 8, 128, 2054), (8, 6, 32, 8, 128, 5)]:

@@ -15,12 +15,13 @@
 //
 // bf16 kernel: workgroup = one (request, kv head, run of 64-key tiles), four
 // waves.  K/V tiles stream HBM -> LDS by direct DMA into a ring, as in the
-// forward pass; Q and dO of all M rows sit in LDS for the whole run.  Wave w
+// forward pass; Q and dO of all M rows sit in LDS (and, for M <= 32, in
+// registers) for the whole run.  Wave w
 // owns keys 16w .. 16w+15 of a tile:
 //   S  = Q . K^T,  dP = dO . V^T                     (M x 16, lane = key)
 //   dV^T = dO^T . P,  dK^T = Q^T . dS                (D x 16, lane = key)
-// so dK and dV of a key are finished inside one wave and go straight to HBM,
-// 4 consecutive columns per lane.  dS^T goes through LDS, and wave w then
+// so dK and dV of a key are finished inside one wave; they go to HBM as
+// whole rows, turned around through the wave's own rows of the V stage.  dS^T goes through LDS, and wave w then
 // accumulates dq^T = K^T . dS^T for its quarter of the D columns over the
 // whole run.  A run that covers its whole sequence writes dq directly;
 // otherwise each run writes an fp32 partial and the last run of the sequence
@@ -54,6 +55,15 @@ template <int UPR>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (UPR == 16) return ((row & 7) << 1) | ((row >> 3) & 1);
   else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
+// XOR swizzle of the 16-byte units of the 16-row staging area that turns
+// dK / dV from the MFMA C layout into whole rows: the writes put 16 rows x 2
+// halves of one unit pair on distinct banks, the row reads touch one row.
+template <int UPR>
+__device__ __forceinline__ int sws(int row) {
+  if constexpr (UPR == 16) return row & 15;
+  else return (row >> 1) & 7;
 }
 
 // s_waitcnt lgkmcnt(0) with vmcnt / expcnt unconstrained: LDS writes done,
@@ -96,7 +106,7 @@ struct Shape {
   static constexpr int MB = MP / 16;               // 16-row blocks of M
   static constexpr int KS = MP / 32;               // MFMA k-steps over M
   static constexpr int DN = DB / kWaves;           // dq column blocks per wave
-  static constexpr int SPT = 2 * DB;               // dK + dV stores per wave per tile
+  static constexpr int SPT = 2 * (16 * RBYTES / 1024);   // dK + dV row stores per wave per tile
   static constexpr int DS_STRIDE = MP * 2 + 8;     // bytes per dS^T row (padded)
   static constexpr int LDS = NSTAGE * 2 * TB + 2 * MP * RBYTES + kTile * DS_STRIDE + MP * 16 + 16;
   // every wave's DMAs and stores in flight fit the 6-bit vmcnt counter
@@ -172,50 +182,66 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
       dma16(vbase + goff, LDS_ADDR(ring) + (2 * st + 1) * TB + j * 1024);
     }
   };
+  // ---- prologue, by DMA ahead of the first K/V tiles: Q and dO rows into
+  // LDS (swizzled like the tiles), O rows into the last ring stage (not used
+  // before the loop starts), the forward pass's lse and each row's ancestor
+  // mask.  Rows m >= M repeat row M-1; their lse becomes +inf, so p = 0.
+  {
+    auto row_of = [&](int m) -> size_t {
+      const int mm = min(m, M - 1);
+      return (size_t)(b * N + mm / g) * Hq + kvh * g + mm % g;
+    };
+    constexpr int QI = MP * RBYTES / 1024;         // 1-KB DMA instructions per tensor
+    for (int j = w; j < QI; j += kWaves) {
+      const int m = j * RPI + lane / UPR;
+      const size_t e = row_of(m) * D + 8 * ((lane % UPR) ^ swz<UPR>(m));
+      dma16(q + e, LDS_ADDR(sq) + j * 1024);
+      dma16(dout + e, LDS_ADDR(sdo) + j * 1024);
+      dma16(out + e, LDS_ADDR(ring) + (2 * (NSTAGE - 1)) * TB + j * 1024);
+    }
+    if (w == 0) {
+#pragma unroll
+      for (int j = 0; j < (MP + 63) / 64; ++j)
+        if (64 * j + lane < MP) dma4(lse + row_of(64 * j + lane), LDS_ADDR(s_lse2) + 256 * j);
+#pragma unroll
+      for (int j = 0; j < (2 * MP + 63) / 64; ++j) {
+        const int idx = 64 * j + lane;             // dword idx of the per-row masks
+        const int m = min(idx >> 1, M - 1);
+        if ((idx >> 1) < MP)
+          dma4(reinterpret_cast<const uint32_t*>(anc_mask) + 2 * ((size_t)b * N + m / g) + (idx & 1),
+               LDS_ADDR(s_anc) + 256 * j);
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
     if (i < ntiles) dma_tile(i, i);
-
-  // ---- Q and dO of every row into LDS (swizzled like the tiles), with
-  // D[m] = <dO[m], O[m]>, the forward pass's lse in base 2 and each row's
-  // ancestor mask.  Rows m >= M are zero with lse = +inf, so p = 0 there.
+  // the prologue's DMAs have landed once at most the K/V tiles' are in flight
+  wait_ring<PT, 0, NSTAGE - 1, 0>(min(NSTAGE - 1, ntiles), 0);
+  wg_barrier();
   {
-    constexpr int NCH = MP * UPR;                  // 16-byte chunks per tensor
+    // D[m] = <dO[m], O[m]>: the UPR chunks of a row sit in UPR consecutive lanes
+    constexpr int NCH = MP * UPR;
     static_assert(NCH % kThreads == 0, "chunks split evenly over the threads");
+    const unsigned char* otmp = ring + (2 * (NSTAGE - 1)) * TB;
 #pragma unroll
     for (int k = 0; k < NCH / kThreads; ++k) {
       const int c = tid + k * kThreads;
       const int m = c / UPR, u = c % UPR;
-      bf16x8_t qv = {}, dov = {}, ov = {};
-      if (m < M) {
-        const size_t r = ((size_t)(b * N + m / g) * Hq + kvh * g + m % g) * D + 8 * u;
-        qv = *reinterpret_cast<const bf16x8_t*>(q + r);
-        dov = *reinterpret_cast<const bf16x8_t*>(dout + r);
-        ov = *reinterpret_cast<const bf16x8_t*>(out + r);
-      }
+      const int off = m * RBYTES + ((u ^ swz<UPR>(m)) << 4);
+      const bf16x8_t dov = *reinterpret_cast<const bf16x8_t*>(sdo + off);
+      const bf16x8_t ov = *reinterpret_cast<const bf16x8_t*>(otmp + off);
       float dm = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dm = fmaf((float)dov[e], (float)ov[e], dm);
-      // the UPR chunks of a row sit in UPR consecutive lanes
 #pragma unroll
       for (int o = UPR / 2; o > 0; o >>= 1) dm += __shfl_xor(dm, o, kWave);
-      const int off = m * RBYTES + ((u ^ swz<UPR>(m)) << 4);
-      *reinterpret_cast<bf16x8_t*>(sq + off) = qv;
-      *reinterpret_cast<bf16x8_t*>(sdo + off) = dov;
       if (u == 0) s_dm[m] = dm;
     }
-    for (int m = tid; m < MP; m += kThreads) {
-      float l2 = INFINITY;
-      uint64_t a = 0;
-      if (m < M) {
-        l2 = lse[(size_t)(b * N + m / g) * Hq + kvh * g + m % g] * kLog2e;
-        a = anc_mask[(size_t)b * N + m / g];
-      }
-      s_lse2[m] = l2;
-      s_anc[m] = a;
-    }
+    for (int m = tid; m < MP; m += kThreads) s_lse2[m] = (m < M) ? s_lse2[m] * kLog2e : INFINITY;
   }
   wait_lgkm0();
+  wg_barrier();
 
   const float scale_log2 = sm_scale * kLog2e;
 
@@ -238,6 +264,45 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
     }
     const i16x8_t both = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, both);
+  };
+
+  // With 32 packed rows the Q and dO operands of every tile (natural and
+  // transposed, 128 registers) stay in registers; larger M reads them from LDS.
+  constexpr bool CACHE = (MP == 32);
+  bf16x8_t qn[CACHE ? MB : 1][CACHE ? KC : 1], don[CACHE ? MB : 1][CACHE ? KC : 1];
+  bf16x8_t qt[CACHE ? KS : 1][CACHE ? DB : 1], dot[CACHE ? KS : 1][CACHE ? DB : 1];
+  if constexpr (CACHE) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        qn[mb][c] = read_row(sq, 16 * mb + l16, 4 * c + lg);
+        don[mb][c] = read_row(sdo, 16 * mb + l16, 4 * c + lg);
+      }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        qt[s][db] = read_tr(sq, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db);
+        dot[s][db] = read_tr(sdo, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db);
+      }
+  }
+  // A operands: Q / dO rows 16mb.. at d-step c; Q^T / dO^T columns 16db.. at row step s
+  auto q_nat = [&](int mb, int c) -> bf16x8_t {
+    if constexpr (CACHE) return qn[mb][c];
+    else return read_row(sq, 16 * mb + l16, 4 * c + lg);
+  };
+  auto do_nat = [&](int mb, int c) -> bf16x8_t {
+    if constexpr (CACHE) return don[mb][c];
+    else return read_row(sdo, 16 * mb + l16, 4 * c + lg);
+  };
+  auto q_tr = [&](int s, int db) -> bf16x8_t {
+    if constexpr (CACHE) return qt[s][db];
+    else return read_tr(sq, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db);
+  };
+  auto do_tr = [&](int s, int db) -> bf16x8_t {
+    if constexpr (CACHE) return dot[s][db];
+    else return read_tr(sdo, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db);
   };
 
   // dq^T accumulators: rows d = 16*(w*DN + dn) + 4lg + r, column m = 16mb + l16
@@ -285,10 +350,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
       const bf16x8_t vf = read_row(vs, key, 4 * c + lg);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row(sq, 16 * mb + l16, 4 * c + lg), kf,
-                                                           sacc[mb], 0, 0, 0);
-        pacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row(sdo, 16 * mb + l16, 4 * c + lg), vf,
-                                                           pacc[mb], 0, 0, 0);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q_nat(mb, c), kf, sacc[mb], 0, 0, 0);
+        pacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do_nat(mb, c), vf, pacc[mb], 0, 0, 0);
       }
     }
 
@@ -331,25 +394,35 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8_t a_do = read_tr(sdo, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db);
-        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_do, pb[s], dvacc[db], 0, 0, 0);
-        const bf16x8_t a_q = read_tr(sq, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_q, dsb[s], dkacc[db], 0, 0, 0);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do_tr(s, db), pb[s], dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q_tr(s, db), dsb[s], dkacc[db], 0, 0, 0);
       }
     }
-    // lane holds columns 16db + 4lg .. +3 of key row tk: 8-byte stores
+    // ---- dV and dK of the wave's 16 keys leave through the wave's own 16
+    // rows of the V stage (free once its dP is done, and read by no other
+    // wave): 8-byte LDS writes from the C layout, then contiguous 16-byte-
+    // per-lane stores of whole rows.  Keys at or past L fall outside the
+    // buffer bounds and are dropped.
+    unsigned char* stg = ring + (2 * st + 1) * TB + 16 * w * RBYTES;
+    auto stage_out = [&](const f32x4_t* acc, __amdgpu_buffer_rsrc_t rsrc) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      bf16x4_t v4, k4;
+      for (int db = 0; db < DB; ++db) {
+        bf16x4_t v4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v4[r] = (__bf16)dvacc[db][r];
-        k4[r] = (__bf16)dkacc[db][r];
+        for (int r = 0; r < 4; ++r) v4[r] = (__bf16)acc[db][r];
+        *reinterpret_cast<bf16x4_t*>(stg + l16 * RBYTES + (((2 * db + (lg >> 1)) ^ sws<UPR>(l16)) << 4) +
+                                     ((lg & 1) << 3)) = v4;
       }
-      const int off = tk * RBYTES + (16 * db + 4 * lg) * 2;
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v4), rdv, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, k4), rdk, off, 0, 0);
-    }
+#pragma unroll
+      for (int k = 0; k < SPT / 2; ++k) {
+        const int row = k * RPI + lane / UPR;
+        const int u = lane % UPR;
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(stg + row * RBYTES + ((u ^ sws<UPR>(row)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (t0 + 16 * w + row) * RBYTES + u * 16, 0, 0);
+      }
+    };
+    stage_out(dvacc, rdv);
+    stage_out(dkacc, rdk);
 
     // ---- dq^T += K^T . dS^T over the tile's 64 keys, this wave's columns
     wait_lgkm0();
@@ -587,10 +660,12 @@ struct BwdPlan {
   size_t ws_bytes;
 };
 
-// Runs of tiles: about kTargetRuns workgroups over the launch, each at least
-// kMinRun tiles long, from the largest possible sequence (S_max keys).
-constexpr int kTargetRuns = 1024;
-constexpr int kMinRun = 2;
+// Runs of tiles, sized from the largest possible sequence (S_max keys): at
+// least one workgroup per CU (a workgroup fills a CU's LDS), and no run
+// longer than kMaxRun tiles, which bounds the imbalance when prefix lengths
+// differ.  Longer runs pay the prologue and the dq merge less often.
+constexpr int kCUs = 256;
+constexpr int kMaxRun = 64;
 
 static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPlan* p) {
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < 1 || Hq % Hkv) return false;
@@ -601,11 +676,13 @@ static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPl
   if (M > 128) return false;
   p->mp = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
   p->nstage = (D == 128 && p->mp == 128) ? 2 : 3;
+#ifdef SPEC_BWD_NSTAGE_HOOK
+  SPEC_BWD_NSTAGE_HOOK(p->nstage);
+#endif
   const long long seqs = (long long)B * Hkv;
   const int n_tiles = (S_max + kTile - 1) / kTile;
-  int want = (int)std::max<long long>(1, (kTargetRuns + seqs - 1) / seqs);
-  int split_len = std::max(kMinRun, (n_tiles + want - 1) / want);
-  split_len = std::min(split_len, n_tiles);
+  const long long want = std::max<long long>((kCUs + seqs - 1) / seqs, (n_tiles + kMaxRun - 1) / kMaxRun);
+  int split_len = (int)((n_tiles + want - 1) / want);
 #ifdef SPEC_BWD_SPLIT_HOOK
   SPEC_BWD_SPLIT_HOOK(split_len, n_tiles);
 #endif
@@ -695,6 +772,11 @@ extern "C" spec_status spec_tree_attn_backward(const void* q, const void* k_cach
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;                                            \
   }
   SPEC_BWD(128, 32, 3)
+#ifdef SPEC_BWD_NSTAGE_HOOK
+  SPEC_BWD(128, 32, 4)
+  SPEC_BWD(128, 64, 2)
+  SPEC_BWD(64, 32, 4)
+#endif
   SPEC_BWD(128, 64, 3)
   SPEC_BWD(128, 128, 2)
   SPEC_BWD(64, 32, 3)
