@@ -22,6 +22,9 @@ What is computed, and where the pages say so:
   * The draft model is trained on all accepted and rejected branches in one
     batched forward and backward pass under the same tree mask (Aurora,
     section 2, closing paragraph): the attention's backward pass.
+  * Numeric precision (FP8 / FP4) is part of what decides serving speed
+    (Aurora, section 1): the fp8-arithmetic attention quantizes each query
+    row to e4m3 (``fp8.py``).
 
 Everything is plain: explicit parent-pointer walks, a dense boolean mask,
 naive softmax in float64, a linear argmax, a recursive accept walk.
@@ -40,11 +43,12 @@ from .step import verify_step
 from .commit import commit_accepted, LABEL_ACCEPTED, LABEL_REJECTED, LABEL_ROOT
 from .paged import gather_pages
 from .attention_bwd import tree_attention_backward
+from .fp8 import encode_e4m3, quantize_rows_e4m3, dequantize_rows_e4m3
 
 __all__ = [
     "ancestors", "build_masks", "accept_walk", "children_of",
     "bf16_bits_to_f64", "e4m3_decode_table", "decode_e4m3", "dense_tree_mask",
     "tree_attention_bh", "tree_attention", "vocab_argmax", "verify_step",
     "commit_accepted", "LABEL_ACCEPTED", "LABEL_REJECTED", "LABEL_ROOT", "gather_pages",
-    "tree_attention_backward",
+    "tree_attention_backward", "encode_e4m3", "quantize_rows_e4m3", "dequantize_rows_e4m3",
 ]

@@ -65,6 +65,8 @@ def decode_e4m3(codes, scale: float) -> np.ndarray:
 
 
 def _as_f64(x, fmt: str) -> np.ndarray:
+    if fmt == "f64":                 # values already exact in float64 (e.g. a dequantized e4m3 q)
+        return np.asarray(x, dtype=np.float64)
     if fmt == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if fmt == "bf16":

@@ -590,3 +590,57 @@ def check_backward_closed_form(tree_attention_backward):
     assert abs(dk[0, 0, 0, 0] + c * q1 * w0 * w1 * (v1 - v0)) < 1e-14
     assert abs(dv[0, 0, 0, 0] - (a + c * w0)) < 1e-14
     assert abs(dv[0, 0, 1, 0] - c * w1) < 1e-14
+
+
+# -------------------------------------------------------------------- fp8
+
+def check_e4m3_encode_against_torch(encode_e4m3, seed: int = 15):
+    """Round-to-nearest-even e4m3 encoding equals torch's float8_e4m3fn
+    conversion: random magnitudes over the whole range (subnormals included),
+    every finite code's own value, and the midpoints between neighbours."""
+    rng = np.random.default_rng(seed)
+    from oracle import e4m3_decode_table
+    tab = e4m3_decode_table()
+    finite = np.array([c for c in range(256) if not np.isnan(tab[c])])
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-0.02, 0.02, 2000),
+                        tab[finite], rng.standard_normal(2000) * 30])
+    pos = np.sort(np.unique(tab[finite][tab[finite] >= 0]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([x, mids, -mids]).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = encode_e4m3(x)
+    # -0.0 and +0.0 both decode to zero; compare values for zeros, codes otherwise
+    same = (got == ref) | ((tab[got] == 0) & (tab[ref] == 0))
+    assert same.all(), (x[~same][:5], got[~same][:5], ref[~same][:5])
+
+
+def check_e4m3_ties_go_to_even(encode_e4m3):
+    """Midpoints between consecutive codes round to the code with an even
+    mantissa: 1.0625 (between 1.0 = 0x38 and 1.125 = 0x39) -> 0x38, 1.1875
+    (between 0x39 and 1.25 = 0x3A) -> 0x3A."""
+    assert encode_e4m3(np.array([1.0625]))[0] == 0x38
+    assert encode_e4m3(np.array([1.1875]))[0] == 0x3A
+    assert encode_e4m3(np.array([-1.1875]))[0] == 0xBA
+
+
+def check_row_quantization(quantize_rows_e4m3, dequantize_rows_e4m3, seed: int = 16):
+    """Each row's largest magnitude becomes exactly +-448; a row of zeros keeps
+    scale 1 and zero codes; every element is within half an e4m3 step
+    (relative 2^-4) of its value, or within the subnormal step."""
+    rng = np.random.default_rng(seed)
+    q = (rng.standard_normal((7, 5, 128)) * rng.uniform(0.01, 30, (7, 5, 1))).astype(np.float32)
+    q[3, 2] = 0.0
+    codes, scale = quantize_rows_e4m3(q)
+    assert codes.shape == q.shape and scale.shape == q.shape[:-1]
+    assert scale[3, 2] == 1.0 and not codes[3, 2].any()
+    from oracle import e4m3_decode_table
+    tab = e4m3_decode_table()
+    for idx in np.ndindex(q.shape[:-1]):
+        if not q[idx].any():
+            continue
+        j = int(np.argmax(np.abs(q[idx])))
+        assert abs(tab[codes[idx][j]]) == 448.0
+    qh = dequantize_rows_e4m3(codes, scale)
+    amax = np.abs(q).max(axis=-1, keepdims=True)
+    step = np.maximum(np.abs(q) * 2.0 ** -4, amax / 448 * 2.0 ** -10)
+    assert (np.abs(qh - q) <= step * (1 + 1e-6)).all()
