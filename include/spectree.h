@@ -13,6 +13,7 @@
  *   spec_accept_walk       longest matched root-to-node path -> accepted tokens
  *   spec_commit_accepted   (after the step) keep the accepted path's K/V, label outcomes
  *   spec_tree_attn_backward (training) gradients of the tree-masked attention
+ *   spec_tree_attn_verify_f8 the attention in fp8 arithmetic over an e4m3 cache
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -256,6 +257,35 @@ spec_status spec_commit_accepted(void* k_cache, void* v_cache, spec_dtype kv_dty
                                  const int32_t* path_nodes, int B, int N, int Hkv, int D, int S_max,
                                  int32_t* new_prefix_lens, int8_t* node_labels,
                                  uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_tree_attn_verify_f8 -- the same attention in fp8 arithmetic, for e4m3
+ * caches.
+ *
+ * The pages count numeric precision (FP8 / FP4) among what decides real
+ * serving speed (Aurora, section 1, on acceptance rate versus speed-up).
+ * This variant computes spec_tree_attn_verify's result for an e4m3 cache
+ * with both products on the fp8 matrix cores:
+ *     K, V        the cache's e4m3 codes as they are (no decode)
+ *     q           each (node, head) row quantized to e4m3 with its own scale
+ *                 amax(|row|) / 448 (round to nearest even)
+ *     p           exp(s - running row max) quantized as e4m3(p * 2^8)
+ *     sums        fp32; the softmax denominator sums the unquantized p
+ * The e4m3 roundings of q and p (3 mantissa bits) make the result differ
+ * from the exact attention by a few percent (relative L2), well inside the
+ * fp8 bound of 6e-2 absolute / 1e-2 relative per element.
+ *
+ *   Arguments as spec_tree_attn_verify with q_dtype = SPEC_BF16 and
+ *   kv_dtype = SPEC_FP8_E4M3 (k_scale, v_scale required), D = 128 only; the
+ *   same workspace size (spec_tree_attn_workspace_bytes) and rules.
+ */
+spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                     int B, int N, int Hq, int Hkv, int D, int S_max,
+                                     float sm_scale, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint32_t* err_word, hipStream_t stream);
 
 /*
  * spec_tree_attn_backward_workspace_bytes -- scratch needed by

@@ -1,0 +1,110 @@
+"""GPU parity of the fp8-arithmetic attention (spec_tree_attn_verify_f8).
+
+Reference: the oracle's exact attention of the e4m3-quantized query
+(``oracle.quantize_rows_e4m3``: the same per-row recipe the kernel follows,
+so the kernel and the reference see the same q codes) over the same e4m3
+cache.  What remains is the kernel's rounding of every probability to
+e4m3(p * 2^8): each weight is off by at most 2^-4 relative (half a step of
+3 mantissa bits), in the numerator only (the denominator sums the exact p),
+so each output element is off by at most
+    2^-4 * max over the row's visible keys c of |V[c][d]|
+plus the bf16 rounding of the output (2^-9 |r|, taken as 2^-8) and 1e-3 of
+fp32 and exp2 slack.  Relative L2 error must stay within 5e-2 (about 2^-4 /
+sqrt 3 is expected) and the log-sum-exp, which sums the exact p, within the
+forward pass's bound.  The distance to the exact attention of the
+unquantized q (both roundings, a few percent) is logged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tree_attention_verify_parent_amd as st
+from tests.gpu_util import bits16, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+REL_L2 = 5e-2
+
+CASES = {
+    "tree16_g8_fp8": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=8, seed=61),
+    "tree16_g8_fp8_ragged": W[4].replace(B=5, prefix_lo=0, prefix_hi=1700, V=8, seed=62),
+    "chain6_g4_fp8": W[1].replace(B=3, kv_dtype="e4m3", prefix_lo=700, prefix_hi=700, V=8, seed=63),
+    "tree8_g8_fp8_m64": W[4].replace(B=3, N=8, max_depth=3, prefix_lo=250, prefix_hi=600, V=8, seed=64),
+    "tree64_g2_fp8_deep": W[4].replace(B=2, N=64, Hq=4, Hkv=2, max_depth=30, max_children=2, prefix_lo=0,
+                                       prefix_hi=130, V=8, seed=65),
+    "one_node_fp8": W[4].replace(B=3, N=1, tree="chain", prefix_lo=1, prefix_hi=200, V=8, seed=66),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    st.lib()
+
+
+def max_visible_v(vdec, prefix, parents, N):
+    """max over the keys each node sees of |V[c][d]|: [B][N][Hkv][D]."""
+    B, Hkv, _, D = vdec.shape
+    out = np.zeros((B, N, Hkv, D))
+    for b in range(B):
+        A = oracle.dense_tree_mask(parents[b], int(prefix[b]))
+        av = np.abs(vdec[b][:, :A.shape[1]])                        # [Hkv][L][D]
+        for i in range(N):
+            out[b, i] = av[:, A[i]].max(axis=1)
+    return out
+
+
+def run_case(w):
+    x = synth.make_inputs(w, with_logits=False)
+    d = to_device(x)
+    anc, _, err = st.tree_mask_build(d["parents"])
+    out, lse, err = st.tree_attn_verify_f8(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc,
+                                           x["sm_scale"], d["k_scale"], d["v_scale"], err=err)
+    torch.cuda.synchronize()
+    qb = bits16(x["q"])
+    kc, vc = x["k_cache"].view(torch.uint8).numpy(), x["v_cache"].view(torch.uint8).numpy()
+    codes, scale = oracle.quantize_rows_e4m3(oracle.bf16_bits_to_f64(qb).astype(np.float32))
+    qh = oracle.dequantize_rows_e4m3(codes, scale)
+    ro, rl = oracle.tree_attention(qh, kc, vc, x["prefix_lens"], x["parents"], x["sm_scale"], q_fmt="f64",
+                                   kv_fmt="e4m3", k_scale=x["k_scale"], v_scale=x["v_scale"])
+    ex, _ = oracle.tree_attention(qb, kc, vc, x["prefix_lens"], x["parents"], x["sm_scale"], q_fmt="bf16",
+                                  kv_fmt="e4m3", k_scale=x["k_scale"], v_scale=x["v_scale"])
+    vdec = oracle.decode_e4m3(vc, 1.0) * x["v_scale"][None, :, None, None]
+    vmax = np.repeat(max_visible_v(vdec, x["prefix_lens"], x["parents"], w.N), w.Hq // w.Hkv, axis=2)
+    return out.float().cpu().numpy(), lse.cpu().numpy(), int(err[0]), ro, rl, ex, vmax
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_f8_attention_matches_oracle(name):
+    w = CASES[name]
+    log(f"[f8] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P=[{w.prefix_lo},{w.prefix_hi}] seed={w.seed}")
+    out, lse, err, ro, rl, ex, vmax = run_case(w)
+    assert err == 0
+    assert np.isfinite(out).all()
+    e = np.abs(out - ro)
+    bound = 2.0 ** -4 * vmax + 2.0 ** -8 * np.abs(ro) + 1e-3
+    worst = float((e / bound).max())
+    rel = float(np.linalg.norm(out - ro) / np.linalg.norm(ro))
+    lerr = np.abs(lse - rl)
+    rel_exact = float(np.linalg.norm(out - ex) / np.linalg.norm(ex))
+    log(f"  vs quantized-q reference: max_abs={e.max():.3e} rel_l2={rel:.3e} worst/bound={worst:.3f} "
+        f"lse max_abs={lerr.max():.3e}; vs exact attention rel_l2={rel_exact:.3e}")
+    assert worst <= 1.0 and rel <= REL_L2, (worst, rel)
+    np.testing.assert_allclose(lse, rl, rtol=1e-4, atol=1e-3)
+
+
+def test_f8_rejects_what_it_does_not_cover():
+    w = CASES["tree16_g8_fp8"]
+    x = synth.make_inputs(w, with_logits=False)
+    d = to_device(x)
+    anc, _, _ = st.tree_mask_build(d["parents"])
+    with pytest.raises(st.SpecError):          # bf16 caches go to spec_tree_attn_verify
+        st.tree_attn_verify_f8(d["q"], d["k_cache"].to(torch.bfloat16), d["v_cache"].to(torch.bfloat16),
+                               d["prefix_lens"], anc, x["sm_scale"], d["k_scale"], d["v_scale"])
+    lib = st.lib()
+    assert lib.spec_tree_attn_verify_f8(None, None, None, None, None, None, None, 1, 1, 1, 1, 128, 8, 0.1,
+                                        None, None, None, 0, None, None) == 1

@@ -55,6 +55,31 @@ __device__ __forceinline__ int swz(int row) {
 template <int I>
 using Int = std::integral_constant<int, I>;
 
+// Internal K/V format id: e4m3 caches read by fp8 arithmetic.  The codes go
+// to v_mfma_f32_16x16x128_f8f6f4 as they are (no decode), and the kernel
+// quantizes Q (per row) and the probabilities P to e4m3 itself.
+constexpr int kKvF8Mma = 16 + SPEC_FP8_E4M3;
+
+// LDS swizzle of that path (128-byte rows, 8 units): its K operand reads 16
+// consecutive rows at one unit, and its V transpose reads rows 4g..4g+3 and
+// 16+4g..19+4g (+32h) at one unit; this XOR map of row bits (found by an
+// exhaustive search over linear maps) gives both distinct banks.
+__device__ __forceinline__ int swz_f8(int row) { return ((row >> 1) & 3) | ((((row >> 3) ^ (row >> 4)) & 1) << 2); }
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// 16x16x128 e4m3 x e4m3 MFMA, fp32 accumulate (the zero scale operands select
+// the unscaled instruction)
+__device__ __forceinline__ f32x4_t mfma_f8(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// four floats -> four e4m3 codes (round to nearest even) in one dword, first in the low byte
+__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
 // Visibility of the 64 tokens t0 .. t0+63 of a tile to one query row: bit k
 // is set iff token t0+k is in the row's prefix, or is a tree node on the
 // row's ancestor-or-self path, and lies before the split end t_end.
@@ -118,6 +143,8 @@ void tree_attn_split_kernel(
   static_assert(NSTAGE >= 2 && NSTAGE <= 8, "ring depth");
   constexpr int NW = WM * WT;
   constexpr int EB = (KVF == SPEC_BF16) ? 2 : 1;     // bytes per cached element
+  constexpr bool F8 = (KVF == kKvF8Mma);             // fp8 arithmetic on an e4m3 cache
+  static_assert(!F8 || (WT == 1 && D == 128), "the fp8 path covers whole tiles per wave, D = 128");
   constexpr int CPT = 2 / WT;                        // 32-token chunks per wave per tile
   constexpr int RBYTES = D * EB;                     // bytes per K/V row
   constexpr int UPR = RBYTES / 16;                   // 16-byte units per row
@@ -174,7 +201,10 @@ void tree_attn_split_kernel(
     for (int qd = 0; qd < KPW; ++qd) {
       const int j = wave + qd * NW;
       const int row = j * RPI + lane / UPR;
-      const int unit16 = (lane % UPR) ^ swz<UPR>(row);
+      int sw;
+      if constexpr (F8) sw = swz_f8(row);
+      else sw = swz<UPR>(row);
+      const int unit16 = (lane % UPR) ^ sw;
       const int c = min(t0 + row, t_end - 1);
       size_t goff;
       if constexpr (PAGED) {
@@ -222,9 +252,12 @@ void tree_attn_split_kernel(
       const int row = row0 + rb * 16 + l16;
       if (row < M) {
         const int i = row / g, hl = row % g;
-        const __bf16* qp = q + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D + 8 * lg;
+        const __bf16* qp = q + ((size_t)(b * N + i) * Hq + kvh * g + hl) * D;
+        // bf16: the B operand's K-slots 32c + 8lg .. +7; fp8: the 32 columns
+        // 32lg .. 32lg+31 the lane quantizes for its 16x16x128 B operand
 #pragma unroll
-        for (int c = 0; c < KC; ++c) qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * c);
+        for (int c = 0; c < KC; ++c)
+          qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + (F8 ? 32 * lg + 8 * c : 32 * c + 8 * lg));
         anc[rb] = anc_mask[(size_t)b * N + i];
       } else {
 #pragma unroll
@@ -419,10 +452,13 @@ void tree_attn_split_kernel(
 
     float scale_log2 = sm_scale * kLog2e;
     float out_scale = 1.0f;
-    if constexpr (KVF == SPEC_FP8_E4M3) {
+    if constexpr (KVF != SPEC_BF16) {
       scale_log2 *= k_scale[kvh];
       out_scale = v_scale[kvh];
     }
+    // fp8 arithmetic: P goes to the MFMA as e4m3(p * 2^8), which keeps weights
+    // down to 2^-17 of the row maximum representable (p <= 1 < 448 / 2^8)
+    if constexpr (F8) out_scale *= 1.0f / 256.0f;
 
     const unsigned char* kbase = seq_base(kc, b, kvh);
     const unsigned char* vbase = seq_base(vc, b, kvh);
@@ -467,6 +503,36 @@ void tree_attn_split_kernel(
       asm volatile("" ::"v"(anc[rb]));
 #pragma unroll
       for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
+    }
+    // fp8 arithmetic: each (node, head) row of Q as e4m3 codes with its own
+    // scale amax / 448 (rows of zeros get scale 1); the four lanes of a row
+    // hold a quarter each.  srow is the row's score scale in base 2.
+    i32x8_t qf8[F8 ? RB : 1];
+    float srow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      srow[rb] = scale_log2;
+      if constexpr (F8) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qreg[rb][c][e]));
+        amax = row4_max(amax);
+        const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+        srow[rb] = scale_log2 * (amax > 0.0f ? amax * (1.0f / 448.0f) : 1.0f);
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            // q * (448 / amax) can exceed 448 by an ulp in fp32: clamp (the
+            // value it rounds to anyway)
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf((float)qreg[rb][c][4 * h + e] * inv, -448.0f), 448.0f);
+            qf8[rb][2 * c + h] = pack_e4m3x4(v[0], v[1], v[2], v[3]);
+          }
+      }
     }
 
     wait_vmcnt<0>();   // usually already met by the wait above; a wave with no Q rows has none
@@ -529,6 +595,92 @@ void tree_attn_split_kernel(
       }
     };
 
+    // fp8 arithmetic operands.  K: lane (m = l16, lg) holds K[row][32lg ..
+    // 32lg+31], the A operand of S^T = K . Q^T over all of D = 128.  V^T: lane
+    // (l16, lg) holds V[16b + 4lg + r][16db + l16] at K-slot 4b + r (b, r =
+    // 0..3), the tokens its S^T accumulators hold; K-slots 16..31 are zero.
+    auto read_k8 = [&](const unsigned char* st, int row) -> i32x8_t {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + row * RBYTES + (((2 * lg) ^ swz_f8(row)) << 4));
+      const u32x4_t c = *reinterpret_cast<const u32x4_t*>(st + row * RBYTES + (((2 * lg + 1) ^ swz_f8(row)) << 4));
+      return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    };
+    auto read_v8 = [&](const unsigned char* st, int db) -> i32x8_t {
+      i32x2_t t[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = l16 >> 1;                     // lanes 2k, 2k+1 point at token k
+        const int row = 16 * (2 * h + (kk >> 2)) + 4 * lg + (kk & 3);
+        const int off = row * RBYTES + ((db ^ swz_f8(row)) << 4) + ((l16 & 1) << 3);
+        t[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(st + off));
+      }
+      return i32x8_t{t[0][0], t[0][1], t[1][0], t[1][1], 0, 0, 0, 0};
+    };
+
+    auto compute_f8 = [&](int st, int i) {
+      const unsigned char* ks = kst(st);
+      const unsigned char* vs = vst(st);
+      const int t0 = t_begin + i * kTile;
+      // ---- S^T = K . Q^T: four 16-token blocks, lane holds tokens 16b + 4lg + r
+      f32x4_t sacc[RB][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const i32x8_t a = read_k8(ks, 16 * kb + l16);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+      const bool plain = (t0 + kTile <= min(P, t_end));
+      i32x8_t pb8[RB];
+      float alpha[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint64_t vis = plain ? ~0ull : tile_visibility(anc[rb], t0, P, t_end);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float s = sacc[rb][kb][r];
+            if (!plain) s = ((vis >> (16 * kb + 4 * lg + r)) & 1ull) ? s : -INFINITY;
+            sacc[rb][kb][r] = s;
+            mx = fmaxf(mx, s);
+          }
+        mx = row4_max(mx) * srow[rb];
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        alpha[rb] = fast_exp2(m_run[rb] - m_use);
+        m_run[rb] = m_new;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = fast_exp2(__builtin_fmaf(sacc[rb][kb][r], srow[rb], -m_use));
+            lsum += p[r];
+          }
+          pb8[rb][kb] = pack_e4m3x4(p[0] * 256.0f, p[1] * 256.0f, p[2] * 256.0f, p[3] * 256.0f);
+          pb8[rb][4 + kb] = 0;
+        }
+        l_run[rb] = l_run[rb] * alpha[rb] + lsum;
+      }
+      bool moved = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) moved |= (alpha[rb] != 1.0f);
+      if (__any(moved)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
+      }
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i32x8_t a = read_v8(vs, db);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma_f8(a, pb8[rb], oacc[rb][db]);
+      }
+    };
+
     auto compute = [&](int st, int i) {
       const unsigned char* ks = kst(st);
       const unsigned char* vs = vst(st);
@@ -582,7 +734,7 @@ void tree_attn_split_kernel(
               sacc[rb][cp][G][r] = s;
               mx = fmaxf(mx, s);
             }
-        mx = row4_max(mx) * scale_log2;
+        mx = row4_max(mx) * srow[rb];
         const float m_new = fmaxf(m_run[rb], mx);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         alpha[rb] = fast_exp2(m_run[rb] - m_use);
@@ -596,7 +748,7 @@ void tree_attn_split_kernel(
           for (int G = 0; G < 2; ++G)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float p = fast_exp2(__builtin_fmaf(sacc[rb][cp][G][r], scale_log2, -m_use));
+              const float p = fast_exp2(__builtin_fmaf(sacc[rb][cp][G][r], srow[rb], -m_use));
               lsum += p;
               pb[rb][cp][4 * G + r] = (__bf16)p;
             }
@@ -643,7 +795,8 @@ void tree_attn_split_kernel(
       }
       wg_barrier();
       if (i + NSTAGE - 1 < ntiles) issue(st == 0 ? NSTAGE - 1 : st - 1, i + NSTAGE - 1);
-      compute(st, i);
+      if constexpr (F8) compute_f8(st, i);
+      else compute(st, i);
       st = (st + 1 == NSTAGE) ? 0 : st + 1;
     }
     // ---- waves that split the tile's tokens combine their states in LDS
@@ -1002,6 +1155,7 @@ constexpr bool split_fits() {
   if (NS * 2 * TB + kTableBytes + (PAGED ? 4 * kMaxPages : 0) > 160 * 1024) return false;
   if (NLOAD % NW != 0) return false;
   if ((NS - 1) * 2 * (NLOAD / NW) >= 64) return false;   // a full ring start fits the vmcnt counter
+  if (KVF == kKvF8Mma && (WT != 1 || D != 128 || PAGED)) return false;
   if (WT == 2 && WM * RB * (D / 16) * 1024 + WM * RB * 512 > NS * 2 * TB) return false;
   return true;
 }
@@ -1009,6 +1163,11 @@ constexpr bool split_fits() {
 // (RB, WM, WT, NSTAGE) instantiations the planner may pick.
 #ifndef SPEC_SPLIT_PLANS
 #define SPEC_SPLIT_PLANS(X) X(1, 2, 2, 3) X(2, 2, 1, 2) X(2, 4, 1, 2)
+#endif
+// The fp8-arithmetic path: every wave covers whole tiles (WT = 1); for M <= 32
+// the plan keeps the 32-row tile of the bf16 plan, so the workspace is the same.
+#ifndef SPEC_F8_PLANS
+#define SPEC_F8_PLANS(X) X(1, 2, 1, 3) X(2, 2, 1, 2) X(2, 4, 1, 2)
 #endif
 
 template <int D, int KVF, bool PAGED>
@@ -1025,7 +1184,11 @@ static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, con
       return true;                                                                                    \
     }                                                                                                 \
   }
-  SPEC_SPLIT_PLANS(SPEC_TRY)
+  if constexpr (KVF == kKvF8Mma) {
+    SPEC_F8_PLANS(SPEC_TRY)
+  } else {
+    SPEC_SPLIT_PLANS(SPEC_TRY)
+  }
 #undef SPEC_TRY
   return false;
 }
@@ -1042,8 +1205,9 @@ extern "C" size_t spec_tree_attn_workspace_bytes(int B, int N, int Hq, int Hkv, 
 
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// The bf16 / e4m3 split kernel for either cache layout (pg.table set: paged).
-static spec_status run_split(const AttnPlan& pl, bool bf16, const void* q, const void* k, const void* v,
+// The split kernel for either cache layout (pg.table set: paged); kvf is
+// SPEC_BF16, SPEC_FP8_E4M3 (decoded to bf16) or kKvF8Mma (fp8 arithmetic).
+static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const void* k, const void* v,
                              const float* k_scale, const float* v_scale, const int32_t* prefix_lens,
                              const uint64_t* anc_mask, int B, int N, int Hq, int Hkv, int D, int S_max,
                              float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
@@ -1069,8 +1233,11 @@ static spec_status run_split(const AttnPlan& pl, bool bf16, const void* q, const
          : dispatch_shape<D_, KVF_, false>(pl, q, k, v, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq,    \
                                            Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, stream))
   bool launched;
-  if (bf16) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_BF16) : SPEC_DISPATCH(128, SPEC_BF16);
-  else launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_FP8_E4M3) : SPEC_DISPATCH(128, SPEC_FP8_E4M3);
+  if (kvf == SPEC_BF16) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_BF16) : SPEC_DISPATCH(128, SPEC_BF16);
+  else if (kvf == SPEC_FP8_E4M3) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_FP8_E4M3) : SPEC_DISPATCH(128, SPEC_FP8_E4M3);
+  else launched = (D == 128) && dispatch_shape<128, kKvF8Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
+                                                                     anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
+                                                                     lse, po, pml, cnt, err_word, pg, stream);
 #undef SPEC_DISPATCH
   if (!launched) return SPEC_ERR_SHAPE;
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
@@ -1113,7 +1280,24 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
   }
 
-  return run_split(pl, bf16, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
+  return run_split(pl, bf16 ? SPEC_BF16 : SPEC_FP8_E4M3, q, k_cache, v_cache, k_scale, v_scale, prefix_lens,
+                   anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
+                   PagedArgs{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cache, const void* v_cache,
+                                                const float* k_scale, const float* v_scale,
+                                                const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N,
+                                                int Hq, int Hkv, int D, int S_max, float sm_scale, void* out,
+                                                float* lse, void* workspace, size_t workspace_bytes,
+                                                uint32_t* err_word, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !prefix_lens || !anc_mask || !out) return SPEC_ERR_NULL;
+  AttnPlan pl;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl) || D != 128) return SPEC_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_ERR_ALIGN;
+  pl.wt = 1;                                         // whole tiles per wave; same rows, same workspace
+  return run_split(pl, kKvF8Mma, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
                    S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word, PagedArgs{nullptr, 0, 0, 0},
                    stream);
 }
@@ -1142,7 +1326,7 @@ extern "C" spec_status spec_tree_attn_verify_paged(const void* q, spec_dtype q_d
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out)) return SPEC_ERR_ALIGN;
   int ps_log2 = 0;
   while ((1 << ps_log2) < page_size) ++ps_log2;
-  return run_split(pl, bf16, q, k_pages, v_pages, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
-                   S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
+  return run_split(pl, bf16 ? SPEC_BF16 : SPEC_FP8_E4M3, q, k_pages, v_pages, k_scale, v_scale, prefix_lens,
+                   anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
                    PagedArgs{block_table, max_pages, ps_log2, num_pages}, stream);
 }
