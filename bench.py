@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 METRIC = "tree-verify steps/sec and achieved HBM GB/s (% of peak) on 1 MI355X"
 DEFAULT_WORKLOAD = "chain6_b8_h32x8_d128_p2048_bf16"
 
@@ -409,6 +410,31 @@ def main():
                      frac=round(pbytes / paged_us / 1e3 / PEAK_HBM_GBS, 4))
         del kps, vps
 
+    # ---- e4m3 caches: the same attention in fp8 arithmetic (both products on
+    # the fp8 matrix cores, q and p quantized in the kernel)
+    f8 = None
+    if w.kv_dtype == "e4m3" and w.D == 128:
+        fg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fg):
+            for c in range(calls):
+                st.tree_attn_verify_f8(qs[c % R], kcs[c % R], vcs[c % R], prefix, anc, x["sm_scale"], ks, vs,
+                                       out=out, lse=lse, workspace=ws, err=err)
+        torch.cuda.synchronize()
+        fg.replay()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(reps):
+            fg.replay()
+        f1.record()
+        torch.cuda.synchronize()
+        f8_us = f0.elapsed_time(f1) * 1e3 / (reps * calls)
+        f8 = dict(kernel="tree_attn_split_kernel (fp8 arithmetic)", launch_us=round(f8_us, 3),
+                  achieved_gbs=round(bytes_["attention"] / f8_us / 1e3, 1),
+                  hbm_frac=round(bytes_["attention"] / f8_us / 1e3 / PEAK_HBM_GBS, 4),
+                  achieved_tflops=round(bytes_["attn_flops"] / f8_us / 1e6, 1),
+                  fp8_mfma_frac=round(bytes_["attn_flops"] / f8_us / 1e6 / PEAK_FP8_TFLOPS, 4))
+
     # ---- the attention's backward pass (training on the verified tree):
     # back-to-back calls over the replicas, each writing its own dK / dV
     backward = None
@@ -477,6 +503,7 @@ def main():
         "commit_step": commit,
         "paged_attention": paged,
         "backward": backward,
+        "f8_attention": f8,
     }
     print(json.dumps(line), flush=True)
 

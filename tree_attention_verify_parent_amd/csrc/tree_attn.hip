@@ -148,7 +148,10 @@ void tree_attn_split_kernel(
   constexpr int CPT = 2 / WT;                        // 32-token chunks per wave per tile
   constexpr int RBYTES = D * EB;                     // bytes per K/V row
   constexpr int UPR = RBYTES / 16;                   // 16-byte units per row
-  constexpr int TB = kTile * RBYTES;                 // bytes per tensor per stage
+  // tokens per ring tile: 64, or 128 for fp8 arithmetic (its PV product
+  // contracts 128 tokens per MFMA); pieces still start on 64-token bounds
+  constexpr int TILE = F8 ? 2 * kTile : kTile;
+  constexpr int TB = TILE * RBYTES;                  // bytes per tensor per stage
   constexpr int NLOAD = TB / 1024;                   // 1-KB wave DMA instructions per tensor
   constexpr int KPW = NLOAD / NW;                    // per wave per tensor per stage
   constexpr int PT = 2 * KPW;                        // DMA instructions per wave per tile
@@ -187,7 +190,7 @@ void tree_attn_split_kernel(
   const int lane0 = threadIdx.x & 63;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // ---- DMA of one 64-token tile (tokens t0 .. t0+63 of the sequence at
+  // ---- DMA of one tile (tokens t0 .. t0+TILE-1 of the sequence at
   // kbase / vbase; rows at or past t_end repeat row t_end - 1) into stage st:
   // wave w issues instructions w, w+NW, ...; lane l of instruction j fills LDS
   // bytes j*1024 + 16l, i.e. row j*RPI + l/UPR at swizzled unit l%UPR.
@@ -287,10 +290,10 @@ void tree_attn_split_kernel(
     stage_pages(f_seg / Hkv, f_begin, f_end);
     const unsigned char* kb = seq_base(kc, f_seg / Hkv, f_seg % Hkv);
     const unsigned char* vb = seq_base(vc, f_seg / Hkv, f_seg % Hkv);
-    const int nt = (f_end - f_begin + kTile - 1) / kTile;
+    const int nt = (f_end - f_begin + TILE - 1) / TILE;
 #pragma unroll
     for (int i = 0; i < NSTAGE - 1; ++i)
-      if (i < nt) dma_tile(kb, vb, f_begin + i * kTile, f_end, i, wave0, lane0, f_begin >> ps_log2);
+      if (i < nt) dma_tile(kb, vb, f_begin + i * TILE, f_end, i, wave0, lane0, f_begin >> ps_log2);
     load_q(f_seg / Hkv, f_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
   }
   // whether every raw prefix length in s_cum is S_max - N (after a barrier
@@ -432,7 +435,7 @@ void tree_attn_split_kernel(
       x = seg_start + L;
     }
     const int P = L - N;
-    const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+    const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
     const bool direct = (t_begin == 0 && t_end == L);   // the whole sequence is in this piece
 
     __syncthreads();                                 // the previous piece is done with the LDS
@@ -457,14 +460,15 @@ void tree_attn_split_kernel(
       out_scale = v_scale[kvh];
     }
     // fp8 arithmetic: P goes to the MFMA as e4m3(p * 2^8), which keeps weights
-    // down to 2^-17 of the row maximum representable (p <= 1 < 448 / 2^8)
-    if constexpr (F8) out_scale *= 1.0f / 256.0f;
+    // down to 2^-17 of the row maximum representable (p * 2^8 <= 256 < 448).
+    // The 2^8 rides in the running max (kept 8 below the true one), so the
+    // row sums, the partials' merge and the log-sum-exp stay consistent.
 
     const unsigned char* kbase = seq_base(kc, b, kvh);
     const unsigned char* vbase = seq_base(vc, b, kvh);
     const int pg0 = t_begin >> ps_log2;
 
-    auto issue = [&](int st, int i) { dma_tile(kbase, vbase, t_begin + i * kTile, t_end, st, wave, lane, pg0); };
+    auto issue = [&](int st, int i) { dma_tile(kbase, vbase, t_begin + i * TILE, t_end, st, wave, lane, pg0); };
 
     // tiles 0 .. NSTAGE-2 go in flight first; everything up to the wait below
     // runs in their shadow
@@ -595,71 +599,83 @@ void tree_attn_split_kernel(
       }
     };
 
-    // fp8 arithmetic operands.  K: lane (m = l16, lg) holds K[row][32lg ..
-    // 32lg+31], the A operand of S^T = K . Q^T over all of D = 128.  V^T: lane
-    // (l16, lg) holds V[16b + 4lg + r][16db + l16] at K-slot 4b + r (b, r =
-    // 0..3), the tokens its S^T accumulators hold; K-slots 16..31 are zero.
+    // fp8 arithmetic operands (128-token tiles).  K: lane (m = l16, lg)
+    // holds K[row][32lg .. 32lg+31], the A operand of S^T = K . Q^T over all
+    // of D = 128.  V^T: lane (l16, lg) holds V[16b + 4lg + r][16db + l16] at
+    // K-slot 4b + r (b = 0..7, r = 0..3): exactly the tokens its S^T
+    // accumulators hold, so P goes from accumulators to operand in place.
     auto read_k8 = [&](const unsigned char* st, int row) -> i32x8_t {
       const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + row * RBYTES + (((2 * lg) ^ swz_f8(row)) << 4));
       const u32x4_t c = *reinterpret_cast<const u32x4_t*>(st + row * RBYTES + (((2 * lg + 1) ^ swz_f8(row)) << 4));
       return i32x8_t{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
     };
     auto read_v8 = [&](const unsigned char* st, int db) -> i32x8_t {
-      i32x2_t t[2];
+      i32x2_t t[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 4; ++h) {
         const int kk = l16 >> 1;                     // lanes 2k, 2k+1 point at token k
         const int row = 16 * (2 * h + (kk >> 2)) + 4 * lg + (kk & 3);
         const int off = row * RBYTES + ((db ^ swz_f8(row)) << 4) + ((l16 & 1) << 3);
         t[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(st + off));
       }
-      return i32x8_t{t[0][0], t[0][1], t[1][0], t[1][1], 0, 0, 0, 0};
+      return i32x8_t{t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
     };
 
     auto compute_f8 = [&](int st, int i) {
       const unsigned char* ks = kst(st);
       const unsigned char* vs = vst(st);
-      const int t0 = t_begin + i * kTile;
-      // ---- S^T = K . Q^T: four 16-token blocks, lane holds tokens 16b + 4lg + r
-      f32x4_t sacc[RB][4];
+      const int t0 = t_begin + i * TILE;
+      // ---- S^T = K . Q^T: eight 16-token blocks, lane holds tokens 16b + 4lg + r
+      f32x4_t sacc[RB][8];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 8; ++kb) {
+        if (kb == 4) asm volatile("" ::: "memory");   // K reads in two batches of four (registers)
         const i32x8_t a = read_k8(ks, 16 * kb + l16);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
       }
-      const bool plain = (t0 + kTile <= min(P, t_end));
+      const bool plain = (t0 + TILE <= min(P, t_end));
+      // a 64-token half of the tile: all prefix inside the piece, past the
+      // piece's end, or masked in registers
+      auto half_vis = [&](uint64_t a, int th) -> uint64_t {
+        if (th + kTile <= min(P, t_end)) return ~0ull;
+        if (th >= t_end) return 0ull;
+        return tile_visibility(a, th, P, t_end);
+      };
       i32x8_t pb8[RB];
       float alpha[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const uint64_t vis = plain ? ~0ull : tile_visibility(anc[rb], t0, P, t_end);
+        uint64_t vis[2] = {~0ull, ~0ull};
+        if (!plain) {
+          vis[0] = half_vis(anc[rb], t0);
+          vis[1] = half_vis(anc[rb], t0 + kTile);
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float s = sacc[rb][kb][r];
-            if (!plain) s = ((vis >> (16 * kb + 4 * lg + r)) & 1ull) ? s : -INFINITY;
+            if (!plain) s = ((vis[kb >> 2] >> (16 * (kb & 3) + 4 * lg + r)) & 1ull) ? s : -INFINITY;
             sacc[rb][kb][r] = s;
             mx = fmaxf(mx, s);
           }
-        mx = row4_max(mx) * srow[rb];
+        mx = row4_max(mx) * srow[rb] - 8.0f;
         const float m_new = fmaxf(m_run[rb], mx);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         alpha[rb] = fast_exp2(m_run[rb] - m_use);
         m_run[rb] = m_new;
         float lsum = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 8; ++kb) {
           float p[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             p[r] = fast_exp2(__builtin_fmaf(sacc[rb][kb][r], srow[rb], -m_use));
             lsum += p[r];
           }
-          pb8[rb][kb] = pack_e4m3x4(p[0] * 256.0f, p[1] * 256.0f, p[2] * 256.0f, p[3] * 256.0f);
-          pb8[rb][4 + kb] = 0;
+          pb8[rb][kb] = pack_e4m3x4(p[0], p[1], p[2], p[3]);
         }
         l_run[rb] = l_run[rb] * alpha[rb] + lsum;
       }
@@ -672,7 +688,9 @@ void tree_attn_split_kernel(
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
       }
-      // ---- O^T += V^T . P^T
+      // ---- O^T += V^T . P^T, 128 tokens per MFMA.  (The V reads stay below
+      // the softmax: hoisted above it they hold 64 more registers.)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const i32x8_t a = read_v8(vs, db);
@@ -1149,7 +1167,7 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
 // combine has scratch room.
 template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED>
 constexpr bool split_fits() {
-  constexpr int TB = kTile * D * ((KVF == SPEC_BF16) ? 2 : 1);
+  constexpr int TB = (KVF == kKvF8Mma ? 2 * kTile : kTile) * D * ((KVF == SPEC_BF16) ? 2 : 1);
   constexpr int NW = WM * WT;
   constexpr int NLOAD = TB / 1024;
   if (NS * 2 * TB + kTableBytes + (PAGED ? 4 * kMaxPages : 0) > 160 * 1024) return false;
