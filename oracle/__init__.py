@@ -36,8 +36,8 @@ internal rounding (bf16 probabilities before the PV product, hardware exp2)
 legitimately differs; see each test's docstring.
 """
 from .tree import ancestors, build_masks, accept_walk, children_of
-from .attention import (bf16_bits_to_f64, e4m3_decode_table, decode_e4m3, dense_tree_mask,
-                        tree_attention_bh, tree_attention)
+from .attention import (bf16_bits_to_f64, e4m3_decode_table, decode_e4m3, e2m1_decode_table,
+                        decode_e2m1_packed, dense_tree_mask, tree_attention_bh, tree_attention)
 from .argmax import vocab_argmax
 from .step import verify_step
 from .commit import commit_accepted, LABEL_ACCEPTED, LABEL_REJECTED, LABEL_ROOT
@@ -47,7 +47,8 @@ from .fp8 import encode_e4m3, quantize_rows_e4m3, dequantize_rows_e4m3
 
 __all__ = [
     "ancestors", "build_masks", "accept_walk", "children_of",
-    "bf16_bits_to_f64", "e4m3_decode_table", "decode_e4m3", "dense_tree_mask",
+    "bf16_bits_to_f64", "e4m3_decode_table", "decode_e4m3", "e2m1_decode_table", "decode_e2m1_packed",
+    "dense_tree_mask",
     "tree_attention_bh", "tree_attention", "vocab_argmax", "verify_step",
     "commit_accepted", "LABEL_ACCEPTED", "LABEL_REJECTED", "LABEL_ROOT", "gather_pages",
     "tree_attention_backward", "encode_e4m3", "quantize_rows_e4m3", "dequantize_rows_e4m3",

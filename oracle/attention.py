@@ -20,8 +20,9 @@ Training, "Overview"):
     lse[b,i,h]  = max s + log(sum_c exp(s_c - max s)).
 
 Inputs are upcast exactly to float64: float32 as is, bf16 from its bit
-pattern (the upper 16 bits of a float32), OCP e4m3fn from its definition
-times the per-KV-head float32 scale.
+pattern (the upper 16 bits of a float32), OCP e4m3fn and e2m1 (two codes a
+byte, element 2j in the low nibble of byte j) from their definitions times
+the per-KV-head float32 scale.
 """
 from __future__ import annotations
 
@@ -60,6 +61,34 @@ def e4m3_decode_table() -> np.ndarray:
 _E4M3 = e4m3_decode_table()
 
 
+def e2m1_decode_table() -> np.ndarray:
+    """Value of each of the 16 OCP FP4 E2M1 codes, float64.
+
+    Layout: sign bit, 2 exponent bits (bias 1), 1 mantissa bit.  Exponent
+    field 0 encodes the subnormal m * 0.5; there are no infinities or NaNs,
+    so the largest magnitude is 1.5 * 2^2 = 6.
+    """
+    tab = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        s = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        m = code & 0x1
+        tab[code] = s * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return tab
+
+
+_E2M1 = e2m1_decode_table()
+
+
+def decode_e2m1_packed(packed, scale: float) -> np.ndarray:
+    """Packed e2m1 rows [..., D/2] (element 2j in the low nibble of byte j)
+    -> float64 [..., D], times the fp32 scale."""
+    b = np.asarray(packed, dtype=np.uint8)
+    lo, hi = _E2M1[b & 0xF], _E2M1[b >> 4]
+    out = np.stack([lo, hi], axis=-1).reshape(*b.shape[:-1], 2 * b.shape[-1])
+    return out * float(scale)
+
+
 def decode_e4m3(codes, scale: float) -> np.ndarray:
     return _E4M3[np.asarray(codes, dtype=np.uint8)] * float(scale)
 
@@ -91,6 +120,8 @@ def _kv_rows(cache, b: int, kvh: int, L: int, fmt: str, scale) -> np.ndarray:
     rows = np.asarray(cache[b, kvh, :L])
     if fmt == "e4m3":
         return decode_e4m3(rows, scale[kvh])
+    if fmt == "e2m1":
+        return decode_e2m1_packed(rows, scale[kvh])
     return _as_f64(rows, fmt)
 
 

@@ -47,7 +47,7 @@ class Workload:
     prefix_hi: int
     V: int
     q_dtype: str           # "f32" | "bf16"
-    kv_dtype: str          # "f32" | "bf16" | "e4m3"
+    kv_dtype: str          # "f32" | "bf16" | "e4m3" | "e2m1" (packed, two codes a byte)
     p_match: float
     tree: str = "chain"    # "chain" | "random"
     max_depth: int = 0
@@ -157,13 +157,36 @@ def quantize_e4m3_per_head(x: np.ndarray) -> tuple[torch.Tensor, np.ndarray]:
     return t.to(torch.float8_e4m3fn), scale
 
 
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def quantize_e2m1_per_head(x: np.ndarray) -> tuple[torch.Tensor, np.ndarray]:
+    """x: [B][Hkv][S][D] float32 -> (packed uint8 [B][Hkv][S][D/2], scale
+    float32[Hkv]): scale[h] = amax(|x[:, h]|) / 6, each x/scale rounded to the
+    nearest e2m1 value (ties to the even code), element 2j in the low nibble
+    of byte j."""
+    amax = np.abs(x).max(axis=(0, 2, 3)).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(6.0), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[None, :, None, None]).astype(np.float64)
+    a = np.minimum(np.abs(y), 6.0)
+    # nearest magnitude index; a tie goes to the even index (the even code)
+    d = np.abs(a[..., None] - E2M1_VALUES)
+    best = d.min(axis=-1, keepdims=True)
+    cand = (d == best)
+    even_pref = cand & ((np.arange(8) % 2) == 0)
+    idx = np.where(even_pref.any(axis=-1), even_pref.argmax(axis=-1), cand.argmax(axis=-1))
+    code = (idx | np.where((y < 0) & (idx > 0), 8, 0)).astype(np.uint8)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(np.ascontiguousarray(packed)), scale
+
+
 def make_inputs(w: Workload, seed: Optional[int] = None, with_logits: bool = True) -> dict:
     """Draw one batch of verify-step inputs for workload ``w``.
 
     Returns CPU tensors / arrays:
       parents int32[B][N], draft_tokens int32[B][N], planted int32[B][N],
       prefix_lens int32[B], q [B][N][Hq][D], k_cache/v_cache [B][Hkv][S_max][D],
-      k_scale/v_scale float32[Hkv] (fp8 only, else None),
+      k_scale/v_scale float32[Hkv] (fp8 and fp4 only, else None),
       logits float32[B*N][V] (unless with_logits=False), sm_scale.
     Tree node j of request b lives in cache row prefix_lens[b] + j.
     """
@@ -236,6 +259,8 @@ def make_backward_inputs(w: Workload, seed: Optional[int] = None) -> dict:
 def _kv_storage(x: np.ndarray, w: Workload):
     if w.kv_dtype == "e4m3":
         return quantize_e4m3_per_head(x)
+    if w.kv_dtype == "e2m1":
+        return quantize_e2m1_per_head(x)
     return _to_storage(x, w.kv_dtype), None
 
 

@@ -644,3 +644,25 @@ def check_row_quantization(quantize_rows_e4m3, dequantize_rows_e4m3, seed: int =
     amax = np.abs(q).max(axis=-1, keepdims=True)
     step = np.maximum(np.abs(q) * 2.0 ** -4, amax / 448 * 2.0 ** -10)
     assert (np.abs(qh - q) <= step * (1 + 1e-6)).all()
+
+
+def check_e2m1_table(e2m1_decode_table):
+    """The 16 OCP E2M1 values, listed by hand: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6},
+    sign in the top bit of the nibble."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    tab = e2m1_decode_table()
+    assert list(tab[:8]) == want
+    assert list(-tab[8:]) == want
+
+
+def check_e2m1_packing(decode_e2m1_packed, seed: int = 17):
+    """Element 2j sits in the low nibble of byte j: decoding codes packed by a
+    packer written here gives the codes' values in order, times the scale."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+    codes = rng.integers(0, 16, size=(3, 5, 128))
+    packed = np.zeros((3, 5, 64), dtype=np.uint8)
+    for j in range(64):
+        packed[..., j] = codes[..., 2 * j] + 16 * codes[..., 2 * j + 1]
+    got = decode_e2m1_packed(packed, 0.375)
+    np.testing.assert_array_equal(got, vals[codes] * 0.375)

@@ -90,6 +90,10 @@ MUTANTS = {
                           lambda o: pins.check_attention_one_node_is_decode(o.attention.tree_attention)),
     "e4m3_bias_8": ([("attention", "2.0 ** (e - 7)", "2.0 ** (e - 8)")],
                     lambda o: _check_e4m3(o)),
+    "e2m1_bias_2": ([("attention", "(1.0 + m / 2.0) * 2.0 ** (e - 1)", "(1.0 + m / 2.0) * 2.0 ** (e - 2)")],
+                    lambda o: pins.check_e2m1_table(o.attention.e2m1_decode_table)),
+    "e2m1_high_nibble_first": ([("attention", "out = np.stack([lo, hi], axis=-1)", "out = np.stack([hi, lo], axis=-1)")],
+                               lambda o: pins.check_e2m1_packing(o.attention.decode_e2m1_packed)),
     "e4m3_subnormal_dropped": ([("attention", "tab[code] = s * (m / 8.0) * 2.0 ** -6", "tab[code] = 0.0")],
                                lambda o: _check_e4m3(o)),
     # commit step
