@@ -14,6 +14,7 @@
  *   spec_commit_accepted   (after the step) keep the accepted path's K/V, label outcomes
  *   spec_tree_attn_backward (training) gradients of the tree-masked attention
  *   spec_tree_attn_verify_f8 the attention in fp8 arithmetic over an e4m3 cache
+ *   spec_tree_attn_verify_f4 ... over an e2m1 (FP4) cache
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -59,7 +60,9 @@ typedef enum {
 typedef enum {
   SPEC_F32 = 0,
   SPEC_BF16 = 1,
-  SPEC_FP8_E4M3 = 2       /* OCP FP8 E4M3 ("e4m3fn"): bias 7, no inf, max 448 */
+  SPEC_FP8_E4M3 = 2,      /* OCP FP8 E4M3 ("e4m3fn"): bias 7, no inf, max 448 */
+  SPEC_FP4_E2M1 = 3       /* OCP FP4 E2M1: two codes per byte, element 2j in the
+                             low nibble of byte j; values 0, .5, 1, 1.5, 2, 3, 4, 6 */
 } spec_dtype;
 
 /* Device-detected data errors, OR'ed into *err_word. */
@@ -280,6 +283,31 @@ spec_status spec_commit_accepted(void* k_cache, void* v_cache, spec_dtype kv_dty
  *   same workspace size (spec_tree_attn_workspace_bytes) and rules.
  */
 spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                     int B, int N, int Hq, int Hkv, int D, int S_max,
+                                     float sm_scale, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_tree_attn_verify_f4 -- the same attention over an e2m1 (FP4) cache,
+ * in the fp8 arithmetic of spec_tree_attn_verify_f8.
+ *
+ * FP4 is the other precision the pages name (Aurora, section 1).  The
+ * cache holds OCP E2M1 codes, two a byte (element 2j in the low nibble of
+ * byte j), with one fp32 scale per KV head for K and one for V (the same
+ * scheme as the e4m3 cache): K = code * k_scale[kvh].  The codes are the A
+ * operands of e2m1 x e4m3 matrix-core products; q and p are quantized to
+ * e4m3 exactly as in spec_tree_attn_verify_f8.  The cache moves half the
+ * bytes of an e4m3 one.
+ *
+ *   k_cache,
+ *   v_cache    [B][Hkv][S_max][D/2] bytes, 16-B aligned
+ *   Other arguments as spec_tree_attn_verify_f8 (D = 128 only; the same
+ *   workspace size and rules).
+ */
+spec_status spec_tree_attn_verify_f4(const void* q, const void* k_cache, const void* v_cache,
                                      const float* k_scale, const float* v_scale,
                                      const int32_t* prefix_lens, const uint64_t* anc_mask,
                                      int B, int N, int Hq, int Hkv, int D, int S_max,

@@ -1,4 +1,5 @@
-"""GPU parity of the fp8-arithmetic attention (spec_tree_attn_verify_f8).
+"""GPU parity of the fp8-arithmetic attention over e4m3 caches
+(spec_tree_attn_verify_f8) and e2m1 (FP4) caches (spec_tree_attn_verify_f4).
 
 Reference: the oracle's exact attention of the e4m3-quantized query
 (``oracle.quantize_rows_e4m3``: the same per-row recipe the kernel follows,
@@ -62,26 +63,31 @@ def run_case(w):
     x = synth.make_inputs(w, with_logits=False)
     d = to_device(x)
     anc, _, err = st.tree_mask_build(d["parents"])
-    out, lse, err = st.tree_attn_verify_f8(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc,
-                                           x["sm_scale"], d["k_scale"], d["v_scale"], err=err)
+    call = st.tree_attn_verify_f4 if w.kv_dtype == "e2m1" else st.tree_attn_verify_f8
+    out, lse, err = call(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc, x["sm_scale"], d["k_scale"],
+                         d["v_scale"], err=err)
     torch.cuda.synchronize()
     qb = bits16(x["q"])
     kc, vc = x["k_cache"].view(torch.uint8).numpy(), x["v_cache"].view(torch.uint8).numpy()
+    fmt = w.kv_dtype
     codes, scale = oracle.quantize_rows_e4m3(oracle.bf16_bits_to_f64(qb).astype(np.float32))
     qh = oracle.dequantize_rows_e4m3(codes, scale)
     ro, rl = oracle.tree_attention(qh, kc, vc, x["prefix_lens"], x["parents"], x["sm_scale"], q_fmt="f64",
-                                   kv_fmt="e4m3", k_scale=x["k_scale"], v_scale=x["v_scale"])
+                                   kv_fmt=fmt, k_scale=x["k_scale"], v_scale=x["v_scale"])
     ex, _ = oracle.tree_attention(qb, kc, vc, x["prefix_lens"], x["parents"], x["sm_scale"], q_fmt="bf16",
-                                  kv_fmt="e4m3", k_scale=x["k_scale"], v_scale=x["v_scale"])
-    vdec = oracle.decode_e4m3(vc, 1.0) * x["v_scale"][None, :, None, None]
+                                  kv_fmt=fmt, k_scale=x["k_scale"], v_scale=x["v_scale"])
+    dec = oracle.decode_e2m1_packed(vc, 1.0) if fmt == "e2m1" else oracle.decode_e4m3(vc, 1.0)
+    vdec = dec * x["v_scale"][None, :, None, None]
     vmax = np.repeat(max_visible_v(vdec, x["prefix_lens"], x["parents"], w.N), w.Hq // w.Hkv, axis=2)
     return out.float().cpu().numpy(), lse.cpu().numpy(), int(err[0]), ro, rl, ex, vmax
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_f8_attention_matches_oracle(name):
-    w = CASES[name]
-    log(f"[f8] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P=[{w.prefix_lo},{w.prefix_hi}] seed={w.seed}")
+def test_f8_attention_matches_oracle(name, fmt):
+    w = CASES[name].replace(kv_dtype=fmt)
+    log(f"[f8] {name} cache={fmt} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P=[{w.prefix_lo},{w.prefix_hi}] "
+        f"seed={w.seed}")
     out, lse, err, ro, rl, ex, vmax = run_case(w)
     assert err == 0
     assert np.isfinite(out).all()
@@ -105,6 +111,9 @@ def test_f8_rejects_what_it_does_not_cover():
     with pytest.raises(st.SpecError):          # bf16 caches go to spec_tree_attn_verify
         st.tree_attn_verify_f8(d["q"], d["k_cache"].to(torch.bfloat16), d["v_cache"].to(torch.bfloat16),
                                d["prefix_lens"], anc, x["sm_scale"], d["k_scale"], d["v_scale"])
+    with pytest.raises(st.SpecError):          # an e4m3 cache is not a packed e2m1 one
+        st.tree_attn_verify_f4(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc, x["sm_scale"],
+                               d["k_scale"], d["v_scale"])
     lib = st.lib()
     assert lib.spec_tree_attn_verify_f8(None, None, None, None, None, None, None, 1, 1, 1, 1, 128, 8, 0.1,
                                         None, None, None, 0, None, None) == 1

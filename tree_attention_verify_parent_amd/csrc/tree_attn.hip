@@ -66,12 +66,33 @@ constexpr int kKvF8Mma = 16 + SPEC_FP8_E4M3;
 // exhaustive search over linear maps) gives both distinct banks.
 __device__ __forceinline__ int swz_f8(int row) { return ((row >> 1) & 3) | ((((row >> 3) ^ (row >> 4)) & 1) << 2); }
 
+// ... and e2m1 (fp4) caches, read by the same fp8 arithmetic: the codes are
+// the A operands of fp4 x fp8 MFMAs (q and p stay e4m3).
+constexpr int kKvF4Mma = 16 + SPEC_FP4_E2M1;
+
+// LDS swizzle of the fp4 path (64-byte rows, 4 units): its K reads take 16
+// consecutive rows at one unit, its V transpose reads the 16 tokens
+// {16a + 4g' + r} of one contraction run; both land on distinct banks.
+__device__ __forceinline__ int swz_f4(int row) { return ((row >> 2) ^ (row >> 4)) & 3; }
+
+// Contraction slot k of an e2m1 A operand, for lane group g and nibble n (of
+// the low four dwords, element 2j in the low nibble of byte j): the hardware
+// order, measured.  (An e4m3 operand has k = 32g + byte.)
+__device__ __forceinline__ int f4_slot(int g, int n) {
+  return 64 * (g & 1) + 16 * (g >> 1) + (n & 15) + 32 * (n >> 4);
+}
+
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // 16x16x128 e4m3 x e4m3 MFMA, fp32 accumulate (the zero scale operands select
 // the unscaled instruction)
 __device__ __forceinline__ f32x4_t mfma_f8(i32x8_t a, i32x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 16x16x128 e2m1 (A) x e4m3 (B) MFMA, fp32 accumulate
+__device__ __forceinline__ f32x4_t mfma_f4f8(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, 0, 0, 0);
 }
 
 // four floats -> four e4m3 codes (round to nearest even) in one dword, first in the low byte
@@ -142,11 +163,12 @@ void tree_attn_split_kernel(
   static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
   static_assert(NSTAGE >= 2 && NSTAGE <= 8, "ring depth");
   constexpr int NW = WM * WT;
-  constexpr int EB = (KVF == SPEC_BF16) ? 2 : 1;     // bytes per cached element
-  constexpr bool F8 = (KVF == kKvF8Mma);             // fp8 arithmetic on an e4m3 cache
+  constexpr bool F4 = (KVF == kKvF4Mma);             // fp8 arithmetic on an e2m1 cache
+  constexpr bool F8 = (KVF == kKvF8Mma) || F4;       // fp8 arithmetic (e4m3 or e2m1 cache)
+  constexpr int EB = (KVF == SPEC_BF16) ? 2 : 1;     // bytes per cached element (fp4: half)
   static_assert(!F8 || (WT == 1 && D == 128), "the fp8 path covers whole tiles per wave, D = 128");
   constexpr int CPT = 2 / WT;                        // 32-token chunks per wave per tile
-  constexpr int RBYTES = D * EB;                     // bytes per K/V row
+  constexpr int RBYTES = F4 ? D / 2 : D * EB;        // bytes per K/V row
   constexpr int UPR = RBYTES / 16;                   // 16-byte units per row
   // tokens per ring tile: 64, or 128 for fp8 arithmetic (its PV product
   // contracts 128 tokens per MFMA); pieces still start on 64-token bounds
@@ -205,7 +227,8 @@ void tree_attn_split_kernel(
       const int j = wave + qd * NW;
       const int row = j * RPI + lane / UPR;
       int sw;
-      if constexpr (F8) sw = swz_f8(row);
+      if constexpr (F4) sw = swz_f4(row);
+      else if constexpr (F8) sw = swz_f8(row);
       else sw = swz<UPR>(row);
       const int unit16 = (lane % UPR) ^ sw;
       const int c = min(t0 + row, t_end - 1);
@@ -621,6 +644,34 @@ void tree_attn_split_kernel(
       return i32x8_t{t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
     };
 
+    // fp4: K row m at lane group lg holds d = f4_slot(lg, n), two 8-byte runs
+    // of the 64-byte row; V^T nibble n of lane (d, lg) is the token whose P
+    // sits at the B operand's slot f4_slot(lg, n) (byte s of group g': token
+    // 16(s/4) + 4g' + s%4), fetched by the 4-bit transpose reads, one token
+    // per supplier lane.
+    auto read_k4 = [&](const unsigned char* st, int row) -> i32x8_t {
+      const int b0 = 32 * (lg & 1) + 8 * (lg >> 1);
+      uint2 w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int bb = b0 + 16 * h;
+        w[h] = *reinterpret_cast<const uint2*>(st + row * RBYTES + (((bb >> 4) ^ swz_f4(row)) << 4) + (bb & 8));
+      }
+      return i32x8_t{(int)w[0].x, (int)w[0].y, (int)w[1].x, (int)w[1].y, 0, 0, 0, 0};
+    };
+    auto read_v4 = [&](const unsigned char* st, int db) -> i32x8_t {
+      i32x2_t t[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = f4_slot(lg, 16 * h + l16);       // this supplier lane's slot
+        const int gs = k >> 5, s8 = k & 31;
+        const int row = 16 * (s8 >> 2) + 4 * gs + (s8 & 3);
+        const int off = row * RBYTES + (((db >> 1) ^ swz_f4(row)) << 4) + ((db & 1) << 3);
+        t[h] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2_t*)(st + off));
+      }
+      return i32x8_t{t[0][0], t[0][1], t[1][0], t[1][1], 0, 0, 0, 0};
+    };
+
     auto compute_f8 = [&](int st, int i) {
       const unsigned char* ks = kst(st);
       const unsigned char* vs = vst(st);
@@ -630,9 +681,15 @@ void tree_attn_split_kernel(
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
         if (kb == 4) asm volatile("" ::: "memory");   // K reads in two batches of four (registers)
-        const i32x8_t a = read_k8(ks, 16 * kb + l16);
+        if constexpr (F4) {
+          const i32x8_t a = read_k4(ks, 16 * kb + l16);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma_f4f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        } else {
+          const i32x8_t a = read_k8(ks, 16 * kb + l16);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
       }
       const bool plain = (t0 + TILE <= min(P, t_end));
       // a 64-token half of the tile: all prefix inside the piece, past the
@@ -693,9 +750,15 @@ void tree_attn_split_kernel(
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const i32x8_t a = read_v8(vs, db);
+        if constexpr (F4) {
+          const i32x8_t a = read_v4(vs, db);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma_f8(a, pb8[rb], oacc[rb][db]);
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma_f4f8(a, pb8[rb], oacc[rb][db]);
+        } else {
+          const i32x8_t a = read_v8(vs, db);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma_f8(a, pb8[rb], oacc[rb][db]);
+        }
       }
     };
 
@@ -1167,13 +1230,14 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
 // combine has scratch room.
 template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED>
 constexpr bool split_fits() {
-  constexpr int TB = (KVF == kKvF8Mma ? 2 * kTile : kTile) * D * ((KVF == SPEC_BF16) ? 2 : 1);
+  constexpr bool FA = (KVF == kKvF8Mma || KVF == kKvF4Mma);
+  constexpr int TB = (FA ? 2 * kTile : kTile) * (KVF == kKvF4Mma ? D / 2 : D * ((KVF == SPEC_BF16) ? 2 : 1));
   constexpr int NW = WM * WT;
   constexpr int NLOAD = TB / 1024;
   if (NS * 2 * TB + kTableBytes + (PAGED ? 4 * kMaxPages : 0) > 160 * 1024) return false;
   if (NLOAD % NW != 0) return false;
   if ((NS - 1) * 2 * (NLOAD / NW) >= 64) return false;   // a full ring start fits the vmcnt counter
-  if (KVF == kKvF8Mma && (WT != 1 || D != 128 || PAGED)) return false;
+  if ((KVF == kKvF8Mma || KVF == kKvF4Mma) && (WT != 1 || D != 128 || PAGED)) return false;
   if (WT == 2 && WM * RB * (D / 16) * 1024 + WM * RB * 512 > NS * 2 * TB) return false;
   return true;
 }
@@ -1202,7 +1266,7 @@ static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, con
       return true;                                                                                    \
     }                                                                                                 \
   }
-  if constexpr (KVF == kKvF8Mma) {
+  if constexpr (KVF == kKvF8Mma || KVF == kKvF4Mma) {
     SPEC_F8_PLANS(SPEC_TRY)
   } else {
     SPEC_SPLIT_PLANS(SPEC_TRY)
@@ -1253,9 +1317,14 @@ static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const v
   bool launched;
   if (kvf == SPEC_BF16) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_BF16) : SPEC_DISPATCH(128, SPEC_BF16);
   else if (kvf == SPEC_FP8_E4M3) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_FP8_E4M3) : SPEC_DISPATCH(128, SPEC_FP8_E4M3);
-  else launched = (D == 128) && dispatch_shape<128, kKvF8Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
-                                                                     anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
-                                                                     lse, po, pml, cnt, err_word, pg, stream);
+  else if (kvf == kKvF8Mma)
+    launched = (D == 128) && dispatch_shape<128, kKvF8Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
+                                                                  anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
+                                                                  lse, po, pml, cnt, err_word, pg, stream);
+  else
+    launched = (D == 128) && dispatch_shape<128, kKvF4Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
+                                                                  anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
+                                                                  lse, po, pml, cnt, err_word, pg, stream);
 #undef SPEC_DISPATCH
   if (!launched) return SPEC_ERR_SHAPE;
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
@@ -1301,6 +1370,23 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   return run_split(pl, bf16 ? SPEC_BF16 : SPEC_FP8_E4M3, q, k_cache, v_cache, k_scale, v_scale, prefix_lens,
                    anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
                    PagedArgs{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" spec_status spec_tree_attn_verify_f4(const void* q, const void* k_cache, const void* v_cache,
+                                                const float* k_scale, const float* v_scale,
+                                                const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N,
+                                                int Hq, int Hkv, int D, int S_max, float sm_scale, void* out,
+                                                float* lse, void* workspace, size_t workspace_bytes,
+                                                uint32_t* err_word, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !prefix_lens || !anc_mask || !out) return SPEC_ERR_NULL;
+  AttnPlan pl;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl) || D != 128) return SPEC_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_ERR_ALIGN;
+  pl.wt = 1;
+  return run_split(pl, kKvF4Mma, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
+                   S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word, PagedArgs{nullptr, 0, 0, 0},
+                   stream);
 }
 
 extern "C" spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cache, const void* v_cache,
