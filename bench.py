@@ -434,6 +434,32 @@ def main():
                   hbm_frac=round(bytes_["attention"] / f8_us / 1e3 / PEAK_HBM_GBS, 4),
                   achieved_tflops=round(bytes_["attn_flops"] / f8_us / 1e6, 1),
                   fp8_mfma_frac=round(bytes_["attn_flops"] / f8_us / 1e6 / PEAK_FP8_TFLOPS, 4))
+        # the same shapes over an e2m1 (FP4) cache: half the K/V bytes
+        x4 = synth.make_inputs(w.replace(kv_dtype="e2m1"), with_logits=False)
+        k4, v4 = x4["k_cache"].to(dev), x4["v_cache"].to(dev)
+        ks4, vs4 = torch.from_numpy(x4["k_scale"]).to(dev), torch.from_numpy(x4["v_scale"]).to(dev)
+        R4 = int(max(1, min(64, math.ceil(args.replica_bytes / (2 * k4.numel())))))
+        k4s = [k4] + [k4.clone() for _ in range(R4 - 1)]
+        v4s = [v4] + [v4.clone() for _ in range(R4 - 1)]
+        g4 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g4):
+            for c in range(calls):
+                st.tree_attn_verify_f4(qs[c % R], k4s[c % R4], v4s[c % R4], prefix, anc, x["sm_scale"], ks4, vs4,
+                                       out=out, lse=lse, workspace=ws, err=err)
+        torch.cuda.synchronize()
+        g4.replay()
+        torch.cuda.synchronize()
+        f0.record()
+        for _ in range(reps):
+            g4.replay()
+        f1.record()
+        torch.cuda.synchronize()
+        f4_us = f0.elapsed_time(f1) * 1e3 / (reps * calls)
+        b4 = bytes_["attention"] - bytes_["kv"] // 2             # K/V at half a byte per element
+        f8["fp4_cache"] = dict(launch_us=round(f4_us, 3), achieved_gbs=round(b4 / f4_us / 1e3, 1),
+                               hbm_frac=round(b4 / f4_us / 1e3 / PEAK_HBM_GBS, 4),
+                               achieved_tflops=round(bytes_["attn_flops"] / f4_us / 1e6, 1))
+        del k4s, v4s
 
     # ---- the attention's backward pass (training on the verified tree):
     # back-to-back calls over the replicas, each writing its own dK / dV
