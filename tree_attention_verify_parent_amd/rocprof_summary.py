@@ -26,7 +26,8 @@ import sqlite3
 import sys
 
 SHORT = ("tree_attn_split_kernel", "tree_attn_f32_kernel", "vocab_argmax_kernel", "accept_walk_kernel",
-         "tree_mask_build_kernel", "commit_accepted_kernel")
+         "tree_mask_build_kernel", "commit_accepted_kernel", "tree_attn_bwd_kernel", "tree_attn_bwd_f32_dq_kernel",
+         "tree_attn_bwd_f32_dkv_kernel")
 
 
 def _mangled_args(tail: str) -> str:
@@ -44,7 +45,7 @@ def _mangled_args(tail: str) -> str:
 def short_name(name: str) -> str:
     """Kernel name without namespace and argument list, template arguments kept
     (demangled names from the trace, or mangled ones from the counter runs)."""
-    for k in SHORT:
+    for k in sorted(SHORT, key=len, reverse=True):
         if k in name:
             tpl = name.split(k, 1)[1]
             if tpl.startswith("<"):
