@@ -3,13 +3,15 @@
 
 One step = the whole verify hot path for one batch of synthetic inputs that
 are already resident in HBM: ancestor-mask build, tree-masked split-KV
-attention, per-node vocabulary argmax, accept walk.  The default workload is
+attention, per-node vocabulary argmax, accept walk -- by default one
+spec_verify_step call (two launches: masks + argmax + walk, then the
+attention); --unfused times the four separate calls instead.  The default workload is
 the batch-8 lookahead-5 chain in bf16 (32 query heads over 8 KV heads,
 head dim 128, 2048-token prefixes, 32000-token vocabulary).
 
 Timing: W untimed warm-up steps, then K steps timed with torch.cuda
-synchronisation on both sides.  Each step replays a HIP graph holding the four
-library calls for one of R input replicas; R is chosen so that the replicas
+synchronisation on both sides.  Each step replays a HIP graph holding the
+step's library calls for one of R input replicas; R is chosen so that the replicas
 together exceed the GPU's last-level (MALL) cache, so every step streams its
 K/V and logits from HBM.
 
@@ -47,7 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, help="workload name or index 0-4")
-    ap.add_argument("--no-graph", action="store_true", help="launch the four calls eagerly each step")
+    ap.add_argument("--no-graph", action="store_true", help="launch each step's calls eagerly")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the four separate calls (mask, attention, argmax, walk) instead of spec_verify_step")
     ap.add_argument("--two-streams", action="store_true",
                     help="run argmax and accept walk on a second stream, concurrent with mask build "
                          "and attention (default: one stream)")
@@ -224,6 +228,10 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     ws_bytes = st.attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, w.S_max)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # zeroed once, reused
+    step_ws = torch.zeros(st.verify_step_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, w.S_max), dtype=torch.uint8,
+                          device=dev)
+    outs = dict(mask=anc, depth=depth, out=out, lse=lse, argmax=amax, accept_len=acc_len, path_nodes=path,
+                out_tokens=toks, err=err)
     side = torch.cuda.Stream(device=dev) if args.two_streams else None
     ev_mask = torch.cuda.Event()
 
@@ -236,6 +244,10 @@ def main():
         and order.index("mask") < order.index("walk") and order.index("argmax") < order.index("walk"), order
 
     def step(r):
+        if not args.unfused:
+            st.verify_step(parents, draft, prefix, qs[r], kcs[r], vcs[r], lgs[r], x["sm_scale"], k_scale=ks,
+                           v_scale=vs, workspace=step_ws, outs=outs)
+            return
         if side is None:
             for name in order:
                 if name == "mask":
@@ -518,7 +530,9 @@ def main():
         "config": {"workload": w.name, "batch": B, "tree_nodes": N, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "prefix": [w.prefix_lo, w.prefix_hi], "vocab": w.V,
                    "graph": graphs is not None, "steps_per_graph": S if graphs is not None else None,
-                   "two_streams": side is not None, "order": args.order, "replicas": R},
+                   "step": "unfused (4 calls)" if args.unfused else "spec_verify_step (2 launches)",
+                   "two_streams": side is not None and args.unfused,
+                   "order": args.order if args.unfused else None, "replicas": R},
         "tree_tokens_per_s": round(steps_per_s * B * N, 1),
         "step_hbm_gbs": round(bytes_["step"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(bytes_["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

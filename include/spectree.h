@@ -15,6 +15,7 @@
  *   spec_tree_attn_backward (training) gradients of the tree-masked attention
  *   spec_tree_attn_verify_f8 the attention in fp8 arithmetic over an e4m3 cache
  *   spec_tree_attn_verify_f4 ... over an e2m1 (FP4) cache
+ *   spec_verify_step       mask, attention, argmax and accept walk in two launches
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -362,6 +363,56 @@ spec_status spec_tree_attn_backward(const void* q, const void* k_cache, const vo
                                     int D, int S_max, float sm_scale, void* dq, void* dk, void* dv,
                                     void* workspace, size_t workspace_bytes, uint32_t* err_word,
                                     hipStream_t stream);
+
+/*
+ * spec_verify_step_workspace_bytes -- scratch needed by spec_verify_step for
+ * these sizes: a per-node argmax key and a per-request counter, rounded up to
+ * 256 bytes, followed by spec_tree_attn_workspace_bytes(...).  0 for sizes
+ * that spec_verify_step would reject.
+ */
+size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max);
+
+/*
+ * spec_verify_step -- one whole verify step: spec_tree_mask_build,
+ * spec_tree_attn_verify, spec_vocab_argmax and spec_accept_walk in two launches.
+ *
+ * The target verifies the draft's whole tree in one parallel pass and keeps
+ * the longest path it agrees with (Aurora, section 2; Runtime Draft Model
+ * Training, "Overview" and "Evaluation").  The walk needs the argmax and the
+ * tree but not the attention's output, so the first launch builds the masks,
+ * takes the argmax (each logits row cut into chunks over many workgroups,
+ * folded with 64-bit atomic maxima) and runs each request's walk as soon as
+ * its last chunk is done; the second is the attention.  Every output equals
+ * that of the four separate calls on the same inputs.
+ *
+ *   parents, draft_tokens, prefix_lens, q, q_dtype, k_cache, v_cache,
+ *   kv_dtype, k_scale, v_scale, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse
+ *                 as in spec_tree_mask_build / spec_tree_attn_verify /
+ *                 spec_accept_walk
+ *   logits        float[B*N][logits_row_stride]: node (b, i)'s V logits at
+ *                 row b*N + i; finite; V in 1..2^31-1, row stride >= V
+ *   anc_mask      uint64[B][N] out (as spec_tree_mask_build)
+ *   depth         int32[B][N] out, nullable
+ *   target_argmax int32[B][N] out (as spec_vocab_argmax)
+ *   accept_len, path_nodes, out_tokens  out (as spec_accept_walk)
+ *   workspace     >= spec_verify_step_workspace_bytes(...) bytes, 16-B
+ *                 aligned, zero-filled before its first use; every call
+ *                 leaves it zeroed again, so it is reused without clearing.
+ *                 Calls that overlap in time must not share one workspace.
+ *   err_word      nullable: SPEC_DERR_ROOT / _PARENT / _TOKEN / _PREFIX
+ * Every argument check of spec_tree_attn_verify is made before the first
+ * launch, so a non-SPEC_OK status other than SPEC_ERR_HIP means nothing was
+ * enqueued.
+ */
+spec_status spec_verify_step(const int32_t* parents, const int32_t* draft_tokens, const int32_t* prefix_lens,
+                             const void* q, spec_dtype q_dtype, const void* k_cache, const void* v_cache,
+                             spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                             const float* logits, int64_t V, int64_t logits_row_stride,
+                             int B, int N, int Hq, int Hkv, int D, int S_max, float sm_scale,
+                             uint64_t* anc_mask, int32_t* depth, void* out, float* lse,
+                             int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
+                             int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                             uint32_t* err_word, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* spec_status_string(spec_status status);

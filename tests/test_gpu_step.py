@@ -1,0 +1,178 @@
+"""The fused verify step (spec_verify_step: masks + argmax + accept walk in
+one launch, then the attention) on the GPU.
+
+Every other GPU parity test of the whole step (test_gpu_parity,
+test_gpu_fullsize) already runs through the fused entry point against the
+oracle.  Here: it equals the four separate calls bit for bit (the attention
+kernel is the same, and integer outputs are exact), its argmax keeps the
+lowest index when equal maxima sit in different chunks (each chunk is a
+different workgroup folding into one 64-bit key), rows that are strided or
+not 16-byte aligned, the workspace it leaves zeroed, and the device error
+flags.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tree_attention_verify_parent_amd as st
+from tests.gpu_util import check_integers, log, oracle_step, to_device
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+# (workload, what it exercises): rows are cut into chunks of whole 8192-logit
+# passes until about 1024 workgroups scan them, so V = 32000 is 4 chunks per
+# row, 151936 is 19 (B=3, N=16) and 4099 one chunk (N = 60); 5003 ends on a
+# scalar tail; an fp8 cache.
+CASES = {
+    "chain6_b8_bf16_p2048": W[1],
+    "tree16_ragged_V5003": W[2].replace(B=4, prefix_lo=100, prefix_hi=1500, V=5003, seed=21),
+    "tree16_V151936": W[2].replace(B=3, prefix_lo=64, prefix_hi=300, seed=22),
+    "tree60_V4099": W[3].replace(B=2, prefix_lo=777, prefix_hi=777, V=4099, seed=23),
+    "tree16_fp8kv": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=6000, seed=24),
+    "chain6_f32_V1000": W[0],
+}
+
+KEYS = ("mask", "depth", "argmax", "accept_len", "path_nodes", "out_tokens", "err")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    st.lib()
+
+
+def _run(d, x, logits=None, fused=True, workspace=None):
+    r = st.verify_step(d["parents"], d["draft_tokens"], d["prefix_lens"], d["q"], d["k_cache"], d["v_cache"],
+                       d["logits"] if logits is None else logits, x["sm_scale"], k_scale=d["k_scale"],
+                       v_scale=d["v_scale"], fused=fused, workspace=workspace)
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in r.items()}
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).numpy()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_step_equals_the_four_calls(name):
+    w = CASES[name]
+    log(f"[step] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} V={w.V} kv={w.kv_dtype} seed={w.seed}")
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    a = _run(d, x, fused=True)
+    b = _run(d, x, fused=False)
+    for k in KEYS:
+        assert np.array_equal(a[k].numpy(), b[k].numpy()), k
+    assert np.array_equal(_bits(a["out"]), _bits(b["out"]))
+    assert np.array_equal(a["lse"].numpy(), b["lse"].numpy())
+    assert int(a["err"][0]) == 0
+    # and the integer outputs against the oracle's
+    r = oracle_step(x)
+    got = {k: (v.numpy().view(np.uint64) if k == "mask" else v.numpy()) for k, v in a.items() if k in KEYS}
+    check_integers(got, r, name)
+
+
+def _small_step(V, seed=5):
+    w = W[0].replace(B=2, V=V, seed=seed)
+    x = synth.make_inputs(w)
+    return w, x, to_device(x)
+
+
+def test_ties_across_chunks_go_to_the_lowest_index():
+    # V = 70001 over 12 rows: 9 chunks of 8192 per row; equal maxima placed in
+    # different chunks, signed zeros, an all-equal row, the scalar tail
+    w, x, d = _small_step(70001)
+    rows = w.B * w.N
+    lg = torch.full((rows, w.V), -5.0)
+    lg[0] = 1.0                                                 # all equal -> 0
+    lg[1, [70000, 40000, 8192 * 3 + 5]] = 3.0                   # -> 24581
+    lg[2, [69999, 8191, 8192]] = 2.0                            # neighbouring chunks -> 8191
+    lg[3] = -0.0
+    lg[3, 60000] = 0.0                                          # -0 == +0 everywhere -> 0
+    lg[4, 70000] = 9.0                                          # the scalar tail's only element
+    lg[5, [69998, 70000]] = 4.0                                 # the tail against a float4 -> 69998
+    lg[6, [30000]] = -0.0
+    lg[6, [10000]] = 0.0
+    lg[6] = torch.where(lg[6] == -5.0, torch.tensor(-1.0), lg[6])   # zeros in two chunks -> 10000
+    lg[7] = -3.4e38
+    lg[8, 16383] = 1e-30
+    lg[8, 16384] = 1e-30                                        # a chunk boundary -> 16383
+    lg[9] = torch.arange(w.V, dtype=torch.float32) % 1000       # maxima in every chunk -> 999
+    lg[10, 50000] = 7.0
+    lg[11, 12345] = -4.0
+    got = _run(d, x, logits=lg.cuda())["argmax"].numpy()
+    want = oracle.vocab_argmax(lg.numpy())
+    assert want.tolist()[:10] == [0, 24581, 8191, 0, 70000, 69998, 10000, 0, 16383, 999]
+    assert np.array_equal(got, want)
+
+
+def test_strided_and_misaligned_logits():
+    w, x, d = _small_step(5003, seed=6)
+    rows = w.B * w.N
+    g = torch.Generator().manual_seed(7)
+    base = torch.randn(rows, 5005, generator=g).cuda()
+    for lg in (base[:, :5003], base[:, 1:5004], base[:, 2:]):    # stride 5005; 4- and 8-byte offsets
+        got = _run(d, x, logits=lg)
+        ref = _run(d, x, logits=lg, fused=False)
+        for k in KEYS:
+            assert np.array_equal(got[k].numpy(), ref[k].numpy()), k
+        assert np.array_equal(got["argmax"].numpy(), oracle.vocab_argmax(lg.cpu().contiguous().numpy()))
+
+
+def test_workspace_is_left_zeroed_and_reused():
+    w = CASES["tree16_ragged_V5003"]
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    nbytes = st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    a = _run(d, x, workspace=ws)
+    prep = (w.B * w.N * 12 + w.B * 4 + 255) // 256 * 256
+    assert int(ws[:prep].count_nonzero()) == 0
+    b = _run(d, x, workspace=ws)
+    for k in KEYS:
+        assert np.array_equal(a[k].numpy(), b[k].numpy()), k
+    assert np.array_equal(_bits(a["out"]), _bits(b["out"]))
+    # a different batch on the same workspace
+    x2 = synth.make_inputs(w.replace(seed=99))
+    d2 = to_device(x2)
+    c = _run(d2, x2, workspace=ws)
+    r = oracle_step(x2)
+    got = {k: (v.numpy().view(np.uint64) if k == "mask" else v.numpy()) for k, v in c.items() if k in KEYS}
+    check_integers(got, r, "second batch")
+
+
+def test_flags_bad_parents_and_tokens():
+    w = CASES["tree16_ragged_V5003"]
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    par = d["parents"].clone()
+    par[1, 5] = 7                                               # not an earlier node
+    r = st.verify_step(par, d["draft_tokens"], d["prefix_lens"], d["q"], d["k_cache"], d["v_cache"], d["logits"],
+                       x["sm_scale"])
+    torch.cuda.synchronize()
+    assert int(r["err"][0]) & st.DERR_PARENT
+    want = oracle_step(x)
+    for b in (0, 2, 3):                                         # the other requests are untouched
+        assert r["accept_len"][b].item() == want["accept_len"][b]
+        assert np.array_equal(r["path_nodes"][b].cpu().numpy(), want["path_nodes"][b])
+    tok = d["draft_tokens"].clone()
+    tok[2, 3] = w.V
+    r = st.verify_step(d["parents"], tok, d["prefix_lens"], d["q"], d["k_cache"], d["v_cache"], d["logits"],
+                       x["sm_scale"])
+    torch.cuda.synchronize()
+    assert int(r["err"][0]) == st.DERR_TOKEN
+
+
+def test_too_small_workspace_is_rejected_before_any_launch():
+    w = CASES["chain6_f32_V1000"]
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    nbytes = st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max)
+    ws = torch.zeros(nbytes - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(st.SpecError):
+        _run(d, x, workspace=ws)

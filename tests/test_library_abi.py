@@ -176,3 +176,41 @@ def test_backward_host_checks(L):
     assert bwd() == SPEC_ERR_WORKSPACE
     need = L.spec_tree_attn_backward_workspace_bytes(8, 6, 32, 8, 128, 2054)
     assert bwd(ws=FAKE, wsb=need - 1) == SPEC_ERR_WORKSPACE
+
+
+def test_verify_step_workspace_bytes(L):
+    f = L.spec_verify_step_workspace_bytes
+    # a 64-bit argmax key and a counter per node, a counter per request (8*6*12 + 8*4 = 608 bytes,
+    # rounded up to 768), then the attention's workspace
+    assert f(8, 6, 32, 8, 128, 2054) == 768 + L.spec_tree_attn_workspace_bytes(8, 6, 32, 8, 128, 2054)
+    assert f(64, 64, 64, 8, 128, 4160) == 64 * 64 * 12 + 256 + L.spec_tree_attn_workspace_bytes(64, 64, 64, 8, 128,
+                                                                                                4160)
+    for bad in [(0, 6, 32, 8, 128, 2054), (8, 0, 32, 8, 128, 2054), (8, 65, 32, 8, 128, 2054),
+                (8, 6, 32, 8, 96, 2054), (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 128, 5)]:
+        assert f(*bad) == 0, bad
+
+
+def test_verify_step_host_checks(L):
+    need = L.spec_verify_step_workspace_bytes(8, 6, 32, 8, 128, 2054)
+
+    def step(parents=FAKE, logits=FAKE, out=FAKE, V=32000, stride=32000, qd=1, kvd=1,
+             shape=(8, 6, 32, 8, 128, 2054), scale=0.088, ws=FAKE, wsb=need, q=FAKE):
+        return L.spec_verify_step(parents, FAKE, FAKE, q, qd, FAKE, FAKE, kvd, None, None, logits, V, stride,
+                                  *shape, scale, FAKE, None, out, None, FAKE, FAKE, FAKE, FAKE, ws, wsb, None,
+                                  None)
+    assert step(parents=None) == SPEC_ERR_NULL
+    assert step(logits=None) == SPEC_ERR_NULL
+    assert step(out=None) == SPEC_ERR_NULL                        # the attention's checks come first too
+    assert step(V=0, stride=0) == SPEC_ERR_SHAPE
+    assert step(stride=31999) == SPEC_ERR_SHAPE
+    assert step(V=2 ** 31, stride=2 ** 31) == SPEC_ERR_SHAPE
+    assert step(shape=(8, 65, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE
+    assert step(shape=(8, 6, 32, 8, 96, 2054)) == SPEC_ERR_SHAPE
+    assert step(qd=0) == SPEC_ERR_DTYPE
+    assert step(kvd=2) == SPEC_ERR_NULL                           # fp8 cache without scales
+    assert step(scale=0.0) == SPEC_ERR_SHAPE
+    assert step(q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
+    assert step(ws=None) == SPEC_ERR_WORKSPACE
+    assert step(wsb=need - 1) == SPEC_ERR_WORKSPACE               # the attention's part is one byte short
+    assert step(wsb=100) == SPEC_ERR_WORKSPACE                    # not even the argmax keys fit
+    assert step(ws=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN

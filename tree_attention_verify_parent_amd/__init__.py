@@ -18,7 +18,7 @@ __all__ = [
     "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify", "tree_attn_verify_paged",
     "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "attn_backward_workspace_bytes",
     "tree_attn_backward", "tree_attn_verify_f8", "tree_attn_verify_f4", "DERR_ROOT", "DERR_PARENT",
-    "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "DERR_PAGE", "library_path",
+    "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "DERR_PAGE", "library_path", "verify_step_workspace_bytes", "step_outputs",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,8 @@ _DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3f
 EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
            "spec_tree_attn_verify_paged", "spec_tree_attn_verify_f8", "spec_tree_attn_verify_f4",
            "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted",
-           "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_status_string"]
+           "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_verify_step_workspace_bytes",
+           "spec_verify_step", "spec_status_string"]
 
 
 class SpecError(RuntimeError):
@@ -80,6 +81,12 @@ def lib() -> ctypes.CDLL:
     L.spec_tree_attn_backward.argtypes = [c_p, c_p, c_p, c_i, c_p, c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_i,
                                           c_f, c_p, c_p, c_p, c_p, c_sz, c_p, c_p]
     L.spec_tree_attn_backward.restype = c_i
+    L.spec_verify_step_workspace_bytes.argtypes = [c_i] * 6
+    L.spec_verify_step_workspace_bytes.restype = c_sz
+    L.spec_verify_step.argtypes = [c_p, c_p, c_p, c_p, c_i, c_p, c_p, c_i, c_p, c_p, c_p, c_i64, c_i64,
+                                   c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                   c_p, c_sz, c_p, c_p]
+    L.spec_verify_step.restype = c_i
     L.spec_status_string.argtypes = [c_i]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -324,23 +331,67 @@ def tree_attn_backward(q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_o
     return dq, dk, dv, err
 
 
-def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *,
-                k_scale=None, v_scale=None, debug=False, stream=None):
-    """One verify step on the GPU: mask -> attention -> argmax -> accept walk.
+def verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max) -> int:
+    return int(lib().spec_verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max))
 
-    All four calls are enqueued on one stream; nothing synchronises unless
-    ``debug`` is set, in which case the device error word is read and a
-    non-zero value raises.
+
+def step_outputs(B, N, q):
+    """Preallocated outputs for verify_step(..., outs=...)."""
+    dev = q.device
+    return dict(mask=torch.empty((B, N), dtype=torch.int64, device=dev),
+                depth=torch.empty((B, N), dtype=torch.int32, device=dev),
+                out=torch.empty_like(q),
+                lse=torch.empty((B, N, q.shape[2]), dtype=torch.float32, device=dev),
+                argmax=torch.empty(B * N, dtype=torch.int32, device=dev),
+                accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+                path_nodes=torch.empty((B, N), dtype=torch.int32, device=dev),
+                out_tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+                err=torch.zeros(1, dtype=torch.int32, device=dev))
+
+
+def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *,
+                k_scale=None, v_scale=None, workspace=None, fused=True, outs=None, debug=False, stream=None):
+    """One verify step on the GPU: masks, attention, argmax, accept walk.
+
+    ``fused`` (default): spec_verify_step, two launches (masks + argmax +
+    walk, then the attention), with ``workspace`` (zero-filled before its
+    first use, left zeroed; allocated here when None).  ``fused=False``: the
+    four separate calls (``workspace`` is then the attention's).  Both enqueue on one stream and give the same
+    results; nothing synchronises unless ``debug`` is set, in which case the
+    device error word is read and a non-zero value raises.  ``outs``
+    (from step_outputs; its error word is OR'ed into, not cleared) receives
+    the results instead of fresh tensors.
     """
     dev = q.device
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    anc, depth, _ = tree_mask_build(parents, err=err, stream=stream)
-    out, lse, _ = tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc, sm_scale, k_scale=k_scale,
-                                   v_scale=v_scale, err=err, stream=stream)
-    t = vocab_argmax(logits, stream=stream)
     B, N = parents.shape
-    L, path, toks, _ = accept_walk(parents, anc, draft_tokens, t.view(B, N), logits.shape[1], err=err,
-                                   stream=stream)
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    o = step_outputs(B, N, q) if outs is None else outs
+    anc, depth, out, lse, t = o["mask"], o["depth"], o["out"], o["lse"], o["argmax"]
+    L, path, toks, err = o["accept_len"], o["path_nodes"], o["out_tokens"], o["err"]
+    if not fused:
+        tree_mask_build(parents, anc_mask=anc, depth=depth, err=err, stream=stream)
+        tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc, sm_scale, k_scale=k_scale, v_scale=v_scale,
+                         out=out, lse=lse, workspace=workspace, err=err, stream=stream)
+        vocab_argmax(logits, out=t, stream=stream)
+        accept_walk(parents, anc, draft_tokens, t.view(B, N), logits.shape[1], accept_len=L, path_nodes=path,
+                    out_tokens=toks, err=err, stream=stream)
+    else:
+        if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] != B * N:
+            raise SpecError("logits must be a float32 [B*N][V] tensor with unit column stride")
+        if q.dtype not in _DTYPE or k_cache.dtype not in _DTYPE or v_cache.dtype != k_cache.dtype:
+            raise SpecError(f"unsupported dtypes q={q.dtype} k={k_cache.dtype} v={v_cache.dtype}")
+        V = logits.shape[1]
+        if workspace is None:
+            workspace = torch.zeros(max(verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max), 16),
+                                    dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib().spec_verify_step(
+            _ptr(parents), _ptr(draft_tokens), _ptr(prefix_lens), _ptr(q), _DTYPE[q.dtype], _ptr(k_cache),
+            _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(k_scale), _ptr(v_scale),
+            ctypes.c_void_p(logits.data_ptr()), V, logits.stride(0), B, N, Hq, Hkv, D, S_max, float(sm_scale),
+            _ptr(anc), _ptr(depth), _ptr(out), _ptr(lse), _ptr(t), _ptr(L), _ptr(path), _ptr(toks),
+            _ptr(workspace), ws_bytes, _ptr(err), _stream(stream)))
     res = dict(mask=anc, depth=depth, out=out, lse=lse, argmax=t, accept_len=L, path_nodes=path,
                out_tokens=toks, err=err)
     if debug:

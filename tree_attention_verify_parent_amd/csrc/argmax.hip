@@ -1,26 +1,12 @@
-// Per-row argmax of float32 logits, lowest index on ties.
+// Per-row argmax of float32 logits, lowest index on ties, as a stand-alone
+// launch (the scan and reductions are in argmax_ops.h).
 //
-// Under greedy verification the target's token at a draft node is the argmax
-// of its logits (the target verifies the draft's proposal: Aurora, section 2).
 // This is a pure HBM stream: one workgroup per row, 16-byte loads, UNROLL
-// loads in flight per thread, each thread scanning its indices in increasing
-// order with a strict '>' (so it keeps its lowest maximal index), then a wave
-// and a workgroup reduction that break value ties by the smaller index.
-#include "common.h"
+// loads in flight per thread, then a wave and a workgroup reduction that
+// break value ties by the smaller index.
+#include "argmax_ops.h"
 
 namespace spectree {
-
-struct ArgBest {
-  float v;
-  int i;
-};
-
-// b beats a: larger value, or equal value and smaller index.  Float compare,
-// so -0.0 == +0.0.
-__device__ __forceinline__ ArgBest arg_better(ArgBest a, ArgBest b) {
-  const bool take = (b.v > a.v) || (b.v == a.v && b.i < a.i);
-  return take ? b : a;
-}
 
 template <int NT, int UNROLL, bool VEC>
 __global__ __launch_bounds__(NT) void vocab_argmax_kernel(const float* __restrict__ logits,
@@ -30,61 +16,16 @@ __global__ __launch_bounds__(NT) void vocab_argmax_kernel(const float* __restric
   const float* row = logits + r * row_stride;
   const int tid = threadIdx.x;
   ArgBest best{-INFINITY, 0x7fffffff};
-
   if (VEC) {
     const int64_t V4 = V >> 2;
-    const f32x4_t* row4 = reinterpret_cast<const f32x4_t*>(row);
-    // every pass issues all UNROLL loads before using any; the last pass is
-    // predicated instead of falling back to one load at a time
-    for (int64_t base = 0; base < V4; base += (int64_t)NT * UNROLL) {
-      f32x4_t x[UNROLL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int64_t k = base + u * NT + tid;
-        x[u] = (k < V4) ? __builtin_nontemporal_load(&row4[k]) : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int j = (int)((base + u * NT + tid) << 2);
-        if (x[u].x > best.v) { best.v = x[u].x; best.i = j; }
-        if (x[u].y > best.v) { best.v = x[u].y; best.i = j + 1; }
-        if (x[u].z > best.v) { best.v = x[u].z; best.i = j + 2; }
-        if (x[u].w > best.v) { best.v = x[u].w; best.i = j + 3; }
-      }
-    }
-    for (int64_t k = (V4 << 2) + tid; k < V; k += NT) {
-      const float x = row[k];
-      if (x > best.v) { best.v = x; best.i = (int)k; }
-    }
+    best = scan_vec4<NT, UNROLL>(row, 0, V4, tid, best);
+    best = scan_scalar<NT>(row, V4 << 2, V, tid, best);
   } else {
-    for (int64_t k = tid; k < V; k += NT) {
-      const float x = row[k];
-      if (x > best.v) { best.v = x; best.i = (int)k; }
-    }
+    best = scan_scalar<NT>(row, 0, V, tid, best);
   }
-  // A thread that saw only -inf (or nothing) keeps index INT_MAX; any real
-  // element with an equal value then wins the tie by its smaller index.
-
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ArgBest other{__shfl_xor(best.v, o, kWave), __shfl_xor(best.i, o, kWave)};
-    best = arg_better(best, other);
-  }
-  __shared__ float sv[NT / kWave];
-  __shared__ int si[NT / kWave];
-  const int wave = tid / kWave, lane = tid % kWave;
-  if (lane == 0) {
-    sv[wave] = best.v;
-    si[wave] = best.i;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    ArgBest b{sv[0], si[0]};
-#pragma unroll
-    for (int w = 1; w < NT / kWave; ++w) b = arg_better(b, ArgBest{sv[w], si[w]});
-    // V >= 1 and logits are finite, so some element was seen
-    out_idx[r] = b.i;
-  }
+  best = wg_best<NT>(best, tid);
+  // V >= 1 and logits are finite, so some element was seen
+  if (tid == 0) out_idx[r] = best.i;
 }
 
 }  // namespace spectree

@@ -1,15 +1,9 @@
-// Ancestor-mask build and accept walk: one wave per request, lane = node.
-//
-// The mask is the custom tree-attention mask that follows the speculative
-// tree's causal structure (Aurora, section 2, closing paragraph); the walk
-// yields the acceptance length, the number of draft tokens the target accepts
-// per verification step (Runtime Draft Model Training, "Evaluation").
-#include "common.h"
+// Ancestor-mask build and accept walk as stand-alone launches: one wave per
+// request, lane = node (the wave logic is in tree_ops.h).
+#include "tree_ops.h"
 
 namespace spectree {
 
-// Ancestor-or-self sets by pointer doubling: after round r a node's set holds
-// every ancestor within 2^r edges, so six rounds cover N <= 64.
 __global__ __launch_bounds__(kWave) void tree_mask_build_kernel(
     const int32_t* __restrict__ parents, int N, uint64_t* __restrict__ anc_mask,
     int32_t* __restrict__ depth, uint32_t* __restrict__ err_word) {
@@ -17,35 +11,15 @@ __global__ __launch_bounds__(kWave) void tree_mask_build_kernel(
   const int i = threadIdx.x;
   const bool live = i < N;
   const int p = live ? parents[(size_t)b * N + i] : 0;
-
-  uint32_t bad = 0;
-  if (live) {
-    if (i == 0 && p != -1) bad |= SPEC_DERR_ROOT;
-    if (i > 0 && (p < 0 || p >= i)) bad |= SPEC_DERR_PARENT;
-  }
-  // any lane's error marks the whole request
-  const bool any_bad = __any(bad != 0);
-  if (bad) flag_error(err_word, bad);
-
-  int jump = (i == 0 || !live || bad) ? 0 : p;
-  uint64_t set = (1ull << i) | (1ull << jump);
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    set |= shfl_u64(set, jump);
-    jump = __shfl(jump, jump, kWave);
-  }
+  bool req_bad;
+  const uint64_t set = ancestor_set(p, i, live, err_word, &req_bad);
   if (live) {
     const size_t o = (size_t)b * N + i;
-    anc_mask[o] = any_bad ? (1ull << i) : set;
-    if (depth) depth[o] = any_bad ? -1 : (__popcll(set) - 1);
+    anc_mask[o] = set;
+    if (depth) depth[o] = req_bad ? -1 : (__popcll(set) - 1);
   }
 }
 
-// Accept walk.  Node i >= 1 matches when its draft token equals the target's
-// argmax at its parent; it is accepted when every node on its root path
-// (root excluded) matches, i.e. (anc(i) & ~matched) == 0.  The path ends at
-// the accepted node with the largest depth, ties to the lowest index:
-// maximise the key depth*64 + (63 - i) over the wave.
 __global__ __launch_bounds__(kWave) void accept_walk_kernel(
     const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc_mask,
     const int32_t* __restrict__ draft_tokens, const int32_t* __restrict__ target_argmax, int N,
@@ -59,45 +33,7 @@ __global__ __launch_bounds__(kWave) void accept_walk_kernel(
   const uint64_t anc = live ? anc_mask[o] : 0ull;
   const int d = live ? draft_tokens[o] : 0;
   const int t = live ? target_argmax[o] : 0;
-
-  uint32_t bad = 0;
-  if (live) {
-    if (i == 0 && p != -1) bad |= SPEC_DERR_ROOT;
-    if (i > 0 && (p < 0 || p >= i)) bad |= SPEC_DERR_PARENT;
-    if (i > 0 && (d < 0 || d >= V)) bad |= SPEC_DERR_TOKEN;
-    if (t < 0 || t >= V) bad |= SPEC_DERR_TOKEN;
-  }
-  if (bad) flag_error(err_word, bad);
-
-  const int t_parent = __shfl(t, (p >= 0 && p < kWave) ? p : 0, kWave);
-  const bool match = live && i > 0 && d == t_parent;
-  const uint64_t matched = __ballot(match) | 1ull;
-  const bool accepted = live && (anc & ~matched) == 0ull;
-  const int dep = __popcll(anc) - 1;
-
-  int key = accepted ? dep * 64 + (63 - i) : -1;
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) key = max(key, __shfl_xor(key, s, kWave));
-  // the root is always accepted, so key >= 63
-  const int end = 63 - (key & 63);
-  const int L = key >> 6;
-  const uint64_t path = shfl_u64(anc, end);
-
-  if (live) {
-    // ancestors of the end node write themselves at their depth; the slots
-    // past L get -1 from the lane with that index
-    if ((path >> i) & 1ull) {
-      if (dep >= 0 && dep < N) {
-        path_nodes[(size_t)b * N + dep] = i;
-        out_tokens[(size_t)b * N + dep] = t;
-      }
-    }
-    if (i > L) {
-      path_nodes[o] = -1;
-      out_tokens[o] = -1;
-    }
-    if (i == 0) accept_len[b] = L;
-  }
+  accept_walk_wave(b, i, live, N, V, p, anc, d, t, accept_len, path_nodes, out_tokens, err_word);
 }
 
 }  // namespace spectree
