@@ -4,8 +4,9 @@
 One step = the whole verify hot path for one batch of synthetic inputs that
 are already resident in HBM: ancestor-mask build, tree-masked split-KV
 attention, per-node vocabulary argmax, accept walk -- by default one
-spec_verify_step call (two launches: masks + argmax + walk, then the
-attention); --unfused times the four separate calls instead.  The default workload is
+spec_verify_step call (one launch: the attention kernel's grid also holds
+the mask, argmax and walk workgroups); --unfused times the four separate
+calls instead.  The default workload is
 the batch-8 lookahead-5 chain in bf16 (32 query heads over 8 KV heads,
 head dim 128, 2048-token prefixes, 32000-token vocabulary).
 
@@ -530,7 +531,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "tree_nodes": N, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "prefix": [w.prefix_lo, w.prefix_hi], "vocab": w.V,
                    "graph": graphs is not None, "steps_per_graph": S if graphs is not None else None,
-                   "step": "unfused (4 calls)" if args.unfused else "spec_verify_step (2 launches)",
+                   "step": "unfused (4 calls)" if args.unfused else "spec_verify_step (1 launch)",
                    "two_streams": side is not None and args.unfused,
                    "order": args.order if args.unfused else None, "replicas": R},
         "tree_tokens_per_s": round(steps_per_s * B * N, 1),

@@ -15,7 +15,7 @@
  *   spec_tree_attn_backward (training) gradients of the tree-masked attention
  *   spec_tree_attn_verify_f8 the attention in fp8 arithmetic over an e4m3 cache
  *   spec_tree_attn_verify_f4 ... over an e2m1 (FP4) cache
- *   spec_verify_step       mask, attention, argmax and accept walk in two launches
+ *   spec_verify_step       mask, attention, argmax and accept walk in one launch
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -374,16 +374,19 @@ size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv, int D, in
 
 /*
  * spec_verify_step -- one whole verify step: spec_tree_mask_build,
- * spec_tree_attn_verify, spec_vocab_argmax and spec_accept_walk in two launches.
+ * spec_tree_attn_verify, spec_vocab_argmax and spec_accept_walk in one launch
+ * (two for fp32).
  *
  * The target verifies the draft's whole tree in one parallel pass and keeps
  * the longest path it agrees with (Aurora, section 2; Runtime Draft Model
  * Training, "Overview" and "Evaluation").  The walk needs the argmax and the
- * tree but not the attention's output, so the first launch builds the masks,
- * takes the argmax (each logits row cut into chunks over many workgroups,
- * folded with 64-bit atomic maxima) and runs each request's walk as soon as
- * its last chunk is done; the second is the attention.  Every output equals
- * that of the four separate calls on the same inputs.
+ * tree but not the attention's output, so the attention's launch also holds
+ * workgroups that build the masks, take the argmax (each logits row cut into
+ * chunks, folded with 64-bit atomic maxima) and run each request's walk as
+ * soon as its last chunk is done, while the attention builds its rows' masks
+ * itself.  For bf16 / e4m3 caches it is one launch; the fp32 attention runs
+ * after a separate launch of the rest.  Every output equals that of the four
+ * separate calls on the same inputs.
  *
  *   parents, draft_tokens, prefix_lens, q, q_dtype, k_cache, v_cache,
  *   kv_dtype, k_scale, v_scale, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse

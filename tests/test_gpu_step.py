@@ -1,5 +1,6 @@
-"""The fused verify step (spec_verify_step: masks + argmax + accept walk in
-one launch, then the attention) on the GPU.
+"""The fused verify step (spec_verify_step: masks, attention, argmax and
+accept walk in one launch; the fp32 attention after a separate launch of the
+rest) on the GPU.
 
 Every other GPU parity test of the whole step (test_gpu_parity,
 test_gpu_fullsize) already runs through the fused entry point against the

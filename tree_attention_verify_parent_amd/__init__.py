@@ -353,8 +353,8 @@ def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits,
                 k_scale=None, v_scale=None, workspace=None, fused=True, outs=None, debug=False, stream=None):
     """One verify step on the GPU: masks, attention, argmax, accept walk.
 
-    ``fused`` (default): spec_verify_step, two launches (masks + argmax +
-    walk, then the attention), with ``workspace`` (zero-filled before its
+    ``fused`` (default): spec_verify_step, one launch (two for fp32), with
+    ``workspace`` (zero-filled before its
     first use, left zeroed; allocated here when None).  ``fused=False``: the
     four separate calls (``workspace`` is then the attention's).  Both enqueue on one stream and give the same
     results; nothing synchronises unless ``debug`` is set, in which case the

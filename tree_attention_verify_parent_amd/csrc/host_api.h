@@ -7,7 +7,11 @@
 
 #include "spectree.h"
 
+#include <hip/hip_runtime_api.h>
+
 namespace spectree {
+
+struct PrepArgs;
 
 // SPEC_OK when spec_tree_attn_verify would accept these arguments, else the
 // status it would return without launching anything.
@@ -16,5 +20,14 @@ spec_status tree_attn_check(const void* q, spec_dtype q_dtype, const void* k_cac
                             const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N, int Hq,
                             int Hkv, int D, int S_max, float sm_scale, const void* out, const void* workspace,
                             size_t workspace_bytes);
+
+// spec_tree_attn_verify for bf16 or decoded-fp8 caches (arguments already
+// accepted by tree_attn_check), with the verify step's prep role (masks,
+// argmax, accept walk) added to the same launch.
+spec_status tree_attn_verify_with_prep(const void* q, const void* k_cache, const void* v_cache, spec_dtype kv_dtype,
+                                       const float* k_scale, const float* v_scale, const int32_t* prefix_lens,
+                                       int B, int N, int Hq, int Hkv, int D, int S_max, float sm_scale, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                       const PrepArgs& prep, hipStream_t stream);
 
 }  // namespace spectree

@@ -1,0 +1,187 @@
+// The verify step's "prep" work -- ancestor masks, per-node vocabulary argmax
+// and accept walk -- as a workgroup role that either a kernel of its own or
+// the tail workgroups of the attention kernel take on.
+//
+// The walk needs the argmax and the tree, not the attention's output (under
+// greedy verification the target's token at a node is the argmax of its
+// logits, and acceptance follows the tree: Aurora, section 2; Runtime Draft
+// Model Training, "Evaluation").  Prep workgroups [0, n_mask_wg) build the
+// masks, one wave per request; the others each take chunk c of logits row
+// r = b*N + i:
+//   * the chunk's best (value, index) is folded into the row's 64-bit key with
+//     an atomic unsigned max; keys order by value first, then by the smaller
+//     index, so the max is the argmax with ties to the lowest index whatever
+//     order the chunks land in;
+//   * the chunk then counts itself into its row's counter, and the chunk that
+//     completes a row counts the row into its request's counter (two levels,
+//     so that no word takes more than max(chunks, N) atomics: increments of
+//     one word are serialised);
+//   * the workgroup that completes a request has every key of it final: its
+//     first wave swaps the keys back to zero (reading them), recomputes the
+//     request's masks in registers and runs the accept walk.
+// Counters are cleared by the workgroup that completes them, so keys and
+// counters start every call at zero, the state in which the caller hands the
+// workspace over the first time.  Keys and counters are updated with
+// system-scope atomics, which every XCD sees at the same coherence point; a
+// chunk's max has returned before the chunk counts itself, so the last
+// arrival reads complete keys.
+#pragma once
+
+#include "argmax_ops.h"
+#include "gfx950.h"
+#include "tree_ops.h"
+
+namespace spectree {
+
+// float4 loads in flight per thread and pass of the argmax scan
+constexpr int kPrepUnroll = 8;
+// about this many argmax workgroups in all: rows are cut into chunks (a whole
+// number of passes each) only as far as that takes, since every chunk costs
+// atomics on its row's key and counter
+constexpr long long kPrepTargetWgs = 1024;
+
+struct PrepArgs {
+  const int32_t* parents;
+  const int32_t* draft_tokens;
+  const float* logits;
+  int64_t V;
+  int64_t row_stride;
+  int64_t chunk_len;     // logits per chunk, a whole number of scan passes
+  int chunks;            // chunks per row
+  int n_mask_wg;         // workgroups that build the masks
+  int vec;               // rows 16-byte aligned: float4 loads
+  uint64_t* anc_mask;
+  int32_t* depth;
+  int32_t* target_argmax;
+  int32_t* accept_len;
+  int32_t* path_nodes;
+  int32_t* out_tokens;
+  uint64_t* keys;        // [rows], zero between calls
+  uint32_t* row_cnt;     // [rows], zero between calls
+  uint32_t* req_cnt;     // [B], zero between calls
+};
+
+// Bytes of workspace the prep role needs (keys, row and request counters),
+// rounded up to 256.
+inline size_t prep_workspace_bytes(int B, int N) {
+  const size_t raw = (size_t)B * N * (sizeof(uint64_t) + sizeof(uint32_t)) + (size_t)B * sizeof(uint32_t);
+  return (raw + 255) & ~(size_t)255;
+}
+
+// Fill in the work split of pa for workgroups of nt threads; returns the
+// number of prep workgroups.
+inline long long plan_prep(PrepArgs* pa, int B, int N, int nt) {
+  const long long rows = (long long)B * N;
+  long long target = kPrepTargetWgs;
+#ifdef SPEC_PREP_HOOK
+  SPEC_PREP_HOOK(target);
+#endif
+  const long long pass = (long long)nt * kPrepUnroll * 4;
+  long long want = (target + rows - 1) / rows;
+  const long long max_chunks = (pa->V + pass - 1) / pass;
+  if (want > max_chunks) want = max_chunks;
+  if (want < 1) want = 1;
+  const long long per = (pa->V + want - 1) / want;
+  pa->chunk_len = ((per + pass - 1) / pass) * pass;
+  pa->chunks = (int)((pa->V + pa->chunk_len - 1) / pa->chunk_len);
+  pa->n_mask_wg = (B + nt / kWave - 1) / (nt / kWave);
+  return pa->n_mask_wg + rows * pa->chunks;
+}
+
+// Point the keys and counters at the start of a workspace.
+inline void place_prep_workspace(PrepArgs* pa, void* ws, int B, int N) {
+  const size_t rows = (size_t)B * N;
+  pa->keys = static_cast<uint64_t*>(ws);
+  pa->row_cnt = reinterpret_cast<uint32_t*>(pa->keys + rows);
+  pa->req_cnt = pa->row_cnt + rows;
+}
+
+// Unsigned-orderable key of a (value, index) pair: the float's bits mapped so
+// that unsigned order is float order (-0.0 taken as +0.0), and the index
+// stored as 0xFFFFFFFF - i so that, for equal values, the smaller index has
+// the larger key.  Every key of a finite value or of -inf is non-zero, so a
+// zeroed key is below all of them.
+__device__ __forceinline__ uint64_t arg_key(ArgBest a) {
+  uint32_t bits = __float_as_uint(a.v);
+  if ((bits << 1) == 0u) bits = 0u;
+  const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)a.i);
+}
+
+// Prep workgroup blk of NT threads (every thread of the workgroup calls it).
+template <int NT>
+__device__ __forceinline__ void prep_block(const PrepArgs& pa, int blk, int B, int N, uint32_t* err_word) {
+  constexpr int SCOPE = __HIP_MEMORY_SCOPE_SYSTEM;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+
+  if (blk < pa.n_mask_wg) {
+    const int b = blk * (NT / kWave) + tid / kWave;
+    if (b >= B) return;                                // the whole wave leaves; no barrier follows
+    const bool live = lane < N;
+    const size_t o = (size_t)b * N + lane;
+    const int p = live ? pa.parents[o] : 0;
+    bool req_bad;
+    const uint64_t set = ancestor_set(p, lane, live, err_word, &req_bad);
+    if (live) {
+      pa.anc_mask[o] = set;
+      if (pa.depth) pa.depth[o] = req_bad ? -1 : (__popcll(set) - 1);
+    }
+    return;
+  }
+
+  // chunk c of row r: logits [c * chunk_len, min(V, (c + 1) * chunk_len))
+  const int u = blk - pa.n_mask_wg;
+  const int r = u / pa.chunks, c = u - r * pa.chunks;
+  const float* row = pa.logits + (int64_t)r * pa.row_stride;
+  const int64_t V = pa.V;
+  const int64_t lo = (int64_t)c * pa.chunk_len;
+  const int64_t end = lo + pa.chunk_len;
+  ArgBest best{-INFINITY, 0x7fffffff};
+  if (pa.vec) {
+    const int64_t V4 = V >> 2;
+    best = scan_vec4<NT, kPrepUnroll>(row, lo / 4, end / 4 < V4 ? end / 4 : V4, tid, best);
+    if (c == pa.chunks - 1) best = scan_scalar<NT>(row, V4 << 2, V, tid, best);
+  } else {
+    best = scan_scalar<NT>(row, lo, end < V ? end : V, tid, best);
+  }
+  best = wg_best<NT>(best, tid);
+
+  __shared__ uint32_t s_last;
+  const int b = r / N;
+  if (tid == 0) {
+    const uint64_t prev = __hip_atomic_fetch_max(pa.keys + r, arg_key(best), __ATOMIC_RELAXED, SCOPE);
+    asm volatile("" ::"v"(prev));                      // keep the returning form ...
+    wait_vmcnt<0>();                                   // ... and wait for its return
+    bool row_done = true;
+    if (pa.chunks > 1) {
+      const uint32_t seen = __hip_atomic_fetch_add(pa.row_cnt + r, 1u, __ATOMIC_RELAXED, SCOPE);
+      row_done = seen == (uint32_t)(pa.chunks - 1);
+      if (row_done) __hip_atomic_store(pa.row_cnt + r, 0u, __ATOMIC_RELAXED, SCOPE);
+    }
+    uint32_t last = 0u;
+    if (row_done) {
+      const uint32_t seen = __hip_atomic_fetch_add(pa.req_cnt + b, 1u, __ATOMIC_RELAXED, SCOPE);
+      last = (seen == (uint32_t)(N - 1)) ? 1u : 0u;
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last || tid >= kWave) return;
+
+  // last row of request b: every key of the request is final
+  const bool live = lane < N;
+  const size_t o = (size_t)b * N + lane;
+  const int p = live ? pa.parents[o] : 0;
+  const int d = live ? pa.draft_tokens[o] : 0;
+  const uint64_t key = live ? __hip_atomic_exchange(pa.keys + o, 0ull, __ATOMIC_RELAXED, SCOPE) : 0ull;
+  const int t = (int)(0xFFFFFFFFu - (uint32_t)key);
+  if (live) pa.target_argmax[o] = t;
+  bool req_bad;
+  const uint64_t anc = ancestor_set(p, lane, live, nullptr, &req_bad);   // the mask workgroup flags errors
+  accept_walk_wave(b, lane, live, N, (int)V, p, anc, d, t, pa.accept_len, pa.path_nodes, pa.out_tokens,
+                   err_word);
+  if (lane == 0) __hip_atomic_store(pa.req_cnt + b, 0u, __ATOMIC_RELAXED, SCOPE);
+}
+
+}  // namespace spectree

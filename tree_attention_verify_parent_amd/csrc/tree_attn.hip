@@ -28,6 +28,7 @@
 
 #include "gfx950.h"
 #include "host_api.h"
+#include "step_ops.h"
 
 namespace spectree {
 
@@ -160,7 +161,8 @@ void tree_attn_split_kernel(
     float sm_scale, int split_len, int n_splits, int n_units, int n_mt, __bf16* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float2* __restrict__ part_ml,
     uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word,
-    const int32_t* __restrict__ block_table, int max_pages, int ps_log2, int num_pages) {
+    const int32_t* __restrict__ block_table, int max_pages, int ps_log2, int num_pages, int attn_grid,
+    const PrepArgs pa) {
   static_assert(WT == 1 || WT == 2, "waves split a 64-token tile in one or two 32-token halves");
   static_assert(NSTAGE >= 2 && NSTAGE <= 8, "ring depth");
   constexpr int NW = WM * WT;
@@ -184,6 +186,18 @@ void tree_attn_split_kernel(
   constexpr int DB = D / 16;
   static_assert(NLOAD % NW == 0, "DMA instructions must split evenly over the waves");
   static_assert((NSTAGE - 1) * PT < 64, "tiles in flight must fit the vmcnt counter");
+  // The whole verify step in one launch (contiguous bf16 / decoded-fp8
+  // caches): workgroups past the attention's grid take the prep role (masks,
+  // argmax, accept walk), and the attention builds its rows' ancestor masks
+  // from pa.parents itself.  They come last, so they fill the CUs that the
+  // attention's workgroups leave as they finish.
+  constexpr bool FUSABLE = !PAGED && !F8;
+  if constexpr (FUSABLE) {
+    if ((int)blockIdx.x >= attn_grid) {
+      prep_block<NW * kWave>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
+      return;
+    }
+  }
 
 
   // the ring: stage s holds K at smem + 2s*TB and V at smem + (2s+1)*TB
@@ -273,7 +287,15 @@ void tree_attn_split_kernel(
   // the rows' ancestor masks, for sequence (b, kvh)
   bf16x8_t qreg[RB][KC];
   uint64_t anc[RB];
+  // in one-launch mode: the lane's node's parent (lane = node), for the
+  // ancestor masks built after the loads complete
+  const bool own_masks = FUSABLE && pa.parents != nullptr;
+  int par_lane = 0;
   auto load_q = [&](int b, int kvh, int row0, int l16, int lg) {
+    if (own_masks) {
+      const int nd = l16 + 16 * lg;
+      par_lane = nd < N ? pa.parents[(size_t)b * N + nd] : 0;
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = row0 + rb * 16 + l16;
@@ -285,7 +307,7 @@ void tree_attn_split_kernel(
 #pragma unroll
         for (int c = 0; c < KC; ++c)
           qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + (F8 ? 32 * lg + 8 * c : 32 * c + 8 * lg));
-        anc[rb] = anc_mask[(size_t)b * N + i];
+        anc[rb] = own_masks ? 0ull : anc_mask[(size_t)b * N + i];
       } else {
 #pragma unroll
         for (int c = 0; c < KC; ++c) qreg[rb][c] = bf16x8_t{};
@@ -531,6 +553,20 @@ void tree_attn_split_kernel(
       asm volatile("" ::"v"(anc[rb]));
 #pragma unroll
       for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
+    }
+    if (own_masks) {
+      // the request's ancestor-or-self sets by pointer doubling across the
+      // wave (lane = node), then each row takes its node's set; a request
+      // with a bad parent gets self-only sets, as the mask build writes them
+      asm volatile("" ::"v"(par_lane));
+      bool req_bad;
+      const uint64_t set = ancestor_set(par_lane, lane, lane < N, nullptr, &req_bad);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = row0 + rb * 16 + l16;
+        const uint64_t a = shfl_u64(set, row < M ? row / g : 0);
+        anc[rb] = row < M ? a : 0ull;
+      }
     }
     // fp8 arithmetic: each (node, head) row of Q as e4m3 codes with its own
     // scale amax / 448 (rows of zeros get scale 1); the four lanes of a row
@@ -1213,16 +1249,23 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
                          const float* ks, const float* vs, const int32_t* pre, const uint64_t* anc,
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
                          float* lse, float* po, float2* pml, uint32_t* cnt, uint32_t* err,
-                         const PagedArgs& pg, hipStream_t st) {
+                         const PagedArgs& pg, const PrepArgs* prep, hipStream_t st) {
   const int units = std::max(B * Hkv * pl.n_splits, pl.n_units);
   const int units_pad = ((units + 7) / 8) * 8;
-  const unsigned grid = (unsigned)units_pad * (unsigned)pl.n_mt;
-  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS, PAGED>), dim3(grid),
+  const long long attn_grid = (long long)units_pad * pl.n_mt;
+  // one-launch verify step: the prep workgroups follow the attention's
+  PrepArgs pa{};
+  long long grid = attn_grid;
+  if (prep) {
+    pa = *prep;
+    grid += plan_prep(&pa, B, N, WM * WT * kWave);
+  }
+  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS, PAGED>), dim3((unsigned)grid),
                      dim3(WM * WT * kWave), 0, st, static_cast<const __bf16*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), ks, vs, pre,
                      anc, B, N, Hq, Hkv, S_max, sm_scale, pl.split_len, pl.n_splits, pl.n_units, pl.n_mt,
                      static_cast<__bf16*>(out), lse, po, pml, cnt, err, pg.table, pg.max_pages, pg.ps_log2,
-                     pg.num_pages);
+                     pg.num_pages, (int)attn_grid, pa);
 }
 
 // Whether an instantiation is buildable: the ring (plus the length table and,
@@ -1258,12 +1301,13 @@ static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, con
                            const float* ks, const float* vs, const int32_t* pre,
                            const uint64_t* anc, int B, int N, int Hq, int Hkv, int S_max,
                            float sm_scale, void* out, float* lse, float* po, float2* pml,
-                           uint32_t* cnt, uint32_t* err, const PagedArgs& pg, hipStream_t st) {
+                           uint32_t* cnt, uint32_t* err, const PagedArgs& pg, const PrepArgs* prep,
+                           hipStream_t st) {
 #define SPEC_TRY(RB_, WM_, WT_, NS_)                                                                  \
   if constexpr (split_fits<D, KVF, RB_, WM_, WT_, NS_, PAGED>()) {                                    \
     if (pl.rb == RB_ && pl.wm == WM_ && pl.wt == WT_ && pl.nstage == NS_) {                           \
       launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, \
-                                                      sm_scale, out, lse, po, pml, cnt, err, pg, st);   \
+                                                      sm_scale, out, lse, po, pml, cnt, err, pg, prep, st); \
       return true;                                                                                    \
     }                                                                                                 \
   }
@@ -1294,7 +1338,8 @@ static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const v
                              const float* k_scale, const float* v_scale, const int32_t* prefix_lens,
                              const uint64_t* anc_mask, int B, int N, int Hq, int Hkv, int D, int S_max,
                              float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                             uint32_t* err_word, const PagedArgs& pg, hipStream_t stream) {
+                             uint32_t* err_word, const PagedArgs& pg, hipStream_t stream,
+                             const PrepArgs* prep = nullptr) {
   float* po = nullptr;
   float2* pml = nullptr;
   uint32_t* cnt = nullptr;
@@ -1312,20 +1357,20 @@ static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const v
   const bool paged = pg.table != nullptr;
 #define SPEC_DISPATCH(D_, KVF_)                                                                           \
   (paged ? dispatch_shape<D_, KVF_, true>(pl, q, k, v, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, \
-                                          S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, stream)     \
+                                          S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, prep, stream)     \
          : dispatch_shape<D_, KVF_, false>(pl, q, k, v, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq,    \
-                                           Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, stream))
+                                           Hkv, S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, prep, stream))
   bool launched;
   if (kvf == SPEC_BF16) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_BF16) : SPEC_DISPATCH(128, SPEC_BF16);
   else if (kvf == SPEC_FP8_E4M3) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_FP8_E4M3) : SPEC_DISPATCH(128, SPEC_FP8_E4M3);
   else if (kvf == kKvF8Mma)
     launched = (D == 128) && dispatch_shape<128, kKvF8Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
                                                                   anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
-                                                                  lse, po, pml, cnt, err_word, pg, stream);
+                                                                  lse, po, pml, cnt, err_word, pg, prep, stream);
   else
     launched = (D == 128) && dispatch_shape<128, kKvF4Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
                                                                   anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
-                                                                  lse, po, pml, cnt, err_word, pg, stream);
+                                                                  lse, po, pml, cnt, err_word, pg, prep, stream);
 #undef SPEC_DISPATCH
   if (!launched) return SPEC_ERR_SHAPE;
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
@@ -1398,6 +1443,23 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
                    anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
                    PagedArgs{nullptr, 0, 0, 0}, stream);
 }
+
+namespace spectree {
+
+spec_status tree_attn_verify_with_prep(const void* q, const void* k_cache, const void* v_cache, spec_dtype kv_dtype,
+                                       const float* k_scale, const float* v_scale, const int32_t* prefix_lens,
+                                       int B, int N, int Hq, int Hkv, int D, int S_max, float sm_scale, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                       const PrepArgs& prep, hipStream_t stream) {
+  AttnPlan pl;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return SPEC_ERR_SHAPE;
+  if (kv_dtype != SPEC_BF16 && kv_dtype != SPEC_FP8_E4M3) return SPEC_ERR_DTYPE;
+  return run_split(pl, kv_dtype, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, prep.anc_mask, B, N, Hq, Hkv,
+                   D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word, PagedArgs{nullptr, 0, 0, 0},
+                   stream, &prep);
+}
+
+}  // namespace spectree
 
 extern "C" spec_status spec_tree_attn_verify_f4(const void* q, const void* k_cache, const void* v_cache,
                                                 const float* k_scale, const float* v_scale,
