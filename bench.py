@@ -382,8 +382,9 @@ def main():
     # ---- the same attention over a paged cache: every replica's K/V scattered
     # into a shuffled pool of token-major pages, read through a block table
     paged = None
-    if args.page_size:
-        ps = args.page_size
+    ps = args.page_size
+    # no fp32 paged path; a block table holds at most 2048 pages per request
+    if ps and w.kv_dtype != "f32" and -(-w.S_max // ps) <= 2048:
         maxp = -(-w.S_max // ps)
         num_pages = B * maxp
         g = torch.Generator().manual_seed(11)

@@ -1,7 +1,10 @@
 """Summarise rocprofv3 result databases into short text tables.
 
-    python -m tree_attention_verify_parent_amd.rocprof_summary stats DIR [--cmd "..."]
-        per-kernel call count and average / min / max duration (kernel trace)
+    python -m tree_attention_verify_parent_amd.rocprof_summary stats DIR [--cmd "..."] [--by-grid]
+        per-kernel call count and average / min / max duration (kernel trace);
+        --by-grid keeps launches of one kernel with different grids apart
+        (the verify step's one-launch attention has a larger grid than the
+        attention alone)
     python -m tree_attention_verify_parent_amd.rocprof_summary pmc DIR [--cmd "..."]
         per-kernel average of every collected counter (one --pmc pass)
     python -m tree_attention_verify_parent_amd.rocprof_summary traffic \\
@@ -63,12 +66,15 @@ def dbs(d):
     return out
 
 
-def kernel_stats(d):
+def kernel_stats(d, by_grid=False):
     agg = collections.defaultdict(list)
     for db in dbs(d):
         c = sqlite3.connect(db)
-        for name, start, end in c.execute("select name, start, end from kernels"):
-            agg[short_name(name)].append((end - start) / 1e3)
+        for name, start, end, gx, wx in c.execute("select name, start, end, grid_x, workgroup_x from kernels"):
+            key = short_name(name)
+            if by_grid:
+                key += f" [{gx // max(wx, 1)} wg]"
+            agg[key].append((end - start) / 1e3)
     return agg
 
 
@@ -84,7 +90,8 @@ def pmc(d):
     return agg
 
 
-ATTENTION_SOURCES = ("common.h", "gfx950.h", "tree_attn.hip")
+ATTENTION_SOURCES = ("common.h", "gfx950.h", "tree_attn.hip", "host_api.h", "step_ops.h", "argmax_ops.h",
+                     "tree_ops.h")
 
 
 def source_sha(root):
@@ -106,15 +113,16 @@ def main(argv=None):
     ap.add_argument("--kernel", default="tree_attn_split_kernel")
     ap.add_argument("--copy-bytes", type=float, default=0)
     ap.add_argument("--out", default="")
+    ap.add_argument("--by-grid", action="store_true")
     a = ap.parse_args(argv)
     if a.cmd:
         print(f"command: {a.cmd}")
     if a.mode == "stats":
-        agg = kernel_stats(a.dirs[0])
+        agg = kernel_stats(a.dirs[0], a.by_grid)
         tot = sum(sum(v) for v in agg.values())
         print(f"{'kernel':58s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
         for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-            print(f"{k:58s} {len(v):7d} {sum(v)/len(v):9.3f} {min(v):9.3f} {max(v):9.3f} {100*sum(v)/tot:6.1f}")
+            print(f"{k[:58]:58s} {len(v):7d} {sum(v)/len(v):9.3f} {min(v):9.3f} {max(v):9.3f} {100*sum(v)/tot:6.1f}")
     elif a.mode == "pmc":
         agg = pmc(a.dirs[0])
         for k, ctrs in sorted(agg.items()):
