@@ -366,9 +366,10 @@ spec_status spec_tree_attn_backward(const void* q, const void* k_cache, const vo
 
 /*
  * spec_verify_step_workspace_bytes -- scratch needed by spec_verify_step for
- * these sizes: a per-node argmax key and a per-request counter, rounded up to
- * 256 bytes, followed by spec_tree_attn_workspace_bytes(...).  0 for sizes
- * that spec_verify_step would reject.
+ * these sizes: a 64-bit argmax key and a counter per node, a counter per
+ * request and a chunk queue, rounded up to 256 bytes, followed by
+ * spec_tree_attn_workspace_bytes(...).  0 for sizes that spec_verify_step
+ * would reject.
  */
 size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int S_max);
 

@@ -78,25 +78,33 @@ def test_fused_step_equals_the_four_calls(name):
     check_integers(got, r, name)
 
 
-def _small_step(V, seed=5):
-    w = W[0].replace(B=2, V=V, seed=seed)
+def _small_step(V, seed=5, base=None):
+    w = (W[0] if base is None else base).replace(B=2, V=V, seed=seed)
     x = synth.make_inputs(w)
     return w, x, to_device(x)
 
 
-def test_ties_across_chunks_go_to_the_lowest_index():
-    # V = 70001 over 12 rows: 9 chunks of 8192 per row; equal maxima placed in
-    # different chunks, signed zeros, an all-equal row, the scalar tail
-    w, x, d = _small_step(70001)
+# Where the argmax runs: the fp32 path's own prep launch; bf16 with V a
+# multiple of 4 and few rows: the attention workgroups' prologue (one chunk
+# each, the mask waves walking); bf16 otherwise: the tail's queue of chunks.
+TIE_PATHS = {"f32_own_launch": (W[0], 70001), "bf16_prologue": (W[1], 70000), "bf16_tail_queue": (W[1], 70001)}
+
+
+@pytest.mark.parametrize("path", list(TIE_PATHS))
+def test_ties_across_chunks_go_to_the_lowest_index(path):
+    # 12 rows of V ~ 70000 logits: 9 to 18 chunks per row; equal maxima placed
+    # in different chunks, signed zeros, an all-equal row, the last elements
+    base, V = TIE_PATHS[path]
+    w, x, d = _small_step(V, base=base)
     rows = w.B * w.N
     lg = torch.full((rows, w.V), -5.0)
     lg[0] = 1.0                                                 # all equal -> 0
-    lg[1, [70000, 40000, 8192 * 3 + 5]] = 3.0                   # -> 24581
-    lg[2, [69999, 8191, 8192]] = 2.0                            # neighbouring chunks -> 8191
+    lg[1, [V - 1, 40000, 8192 * 3 + 5]] = 3.0                   # -> 24581
+    lg[2, [V - 2, 8191, 8192]] = 2.0                            # neighbouring chunks -> 8191
     lg[3] = -0.0
     lg[3, 60000] = 0.0                                          # -0 == +0 everywhere -> 0
-    lg[4, 70000] = 9.0                                          # the scalar tail's only element
-    lg[5, [69998, 70000]] = 4.0                                 # the tail against a float4 -> 69998
+    lg[4, V - 1] = 9.0                                          # the last element
+    lg[5, [V - 3, V - 1]] = 4.0                                 # the tail against a float4 -> V - 3
     lg[6, [30000]] = -0.0
     lg[6, [10000]] = 0.0
     lg[6] = torch.where(lg[6] == -5.0, torch.tensor(-1.0), lg[6])   # zeros in two chunks -> 10000
@@ -106,10 +114,13 @@ def test_ties_across_chunks_go_to_the_lowest_index():
     lg[9] = torch.arange(w.V, dtype=torch.float32) % 1000       # maxima in every chunk -> 999
     lg[10, 50000] = 7.0
     lg[11, 12345] = -4.0
-    got = _run(d, x, logits=lg.cuda())["argmax"].numpy()
+    got = _run(d, x, logits=lg.cuda())
     want = oracle.vocab_argmax(lg.numpy())
-    assert want.tolist()[:10] == [0, 24581, 8191, 0, 70000, 69998, 10000, 0, 16383, 999]
-    assert np.array_equal(got, want)
+    assert want.tolist()[:10] == [0, 24581, 8191, 0, V - 1, V - 3, 10000, 0, 16383, 999]
+    assert np.array_equal(got["argmax"].numpy(), want)
+    ref = _run(d, x, logits=lg.cuda(), fused=False)
+    for k in KEYS:
+        assert np.array_equal(got[k].numpy(), ref[k].numpy()), k
 
 
 def test_strided_and_misaligned_logits():
@@ -132,7 +143,7 @@ def test_workspace_is_left_zeroed_and_reused():
     nbytes = st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     a = _run(d, x, workspace=ws)
-    prep = (w.B * w.N * 12 + w.B * 4 + 255) // 256 * 256
+    prep = (w.B * w.N * 12 + w.B * 4 + 4 + 255) // 256 * 256
     assert int(ws[:prep].count_nonzero()) == 0
     b = _run(d, x, workspace=ws)
     for k in KEYS:

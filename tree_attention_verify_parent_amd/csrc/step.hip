@@ -10,7 +10,7 @@ namespace spectree {
 
 template <int NT>
 __global__ __launch_bounds__(NT) void verify_prep_kernel(const PrepArgs pa, int B, int N, uint32_t* err_word) {
-  prep_block<NT>(pa, (int)blockIdx.x, B, N, err_word);
+  prep_block<NT, kPrepUnroll>(pa, (int)blockIdx.x, B, N, err_word);
 }
 
 static bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -69,7 +69,7 @@ extern "C" spec_status spec_verify_step(
     return tree_attn_verify_with_prep(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, B, N, Hq, Hkv,
                                       D, S_max, sm_scale, out, lse, attn_ws, attn_ws_bytes, err_word, pa, stream);
 
-  const long long grid = plan_prep(&pa, B, N, 256);
+  const long long grid = plan_prep(&pa, B, N, 256, 0);
   if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
   hipLaunchKernelGGL(verify_prep_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, pa, B, N, err_word);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;

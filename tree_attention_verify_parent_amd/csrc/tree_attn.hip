@@ -194,7 +194,7 @@ void tree_attn_split_kernel(
   constexpr bool FUSABLE = !PAGED && !F8;
   if constexpr (FUSABLE) {
     if ((int)blockIdx.x >= attn_grid) {
-      prep_block<NW * kWave>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
+      prep_block<NW * kWave, kPrepTailUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
       return;
     }
   }
@@ -221,11 +221,120 @@ void tree_attn_split_kernel(
   const int mt = (id % per) / 8;
   const int u = (id / per) * 8 + (id % 8);
   const int n_fixed = B * Hkv * n_splits;
-  if (u >= max(n_fixed, n_units)) return;
-  const int g = Hq / Hkv;
-  const int M = g * N;
   const int lane0 = threadIdx.x & 63;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // One-launch verify step with the argmax in the prologue (when pa.held >
+  // 0): workgroup id scans logits chunk id.  The chunk goes out first, as
+  // LDS DMA into the ring's last stage (empty until the loop refills it), and
+  // is reduced while the first tiles are still in flight; its max is folded
+  // into the row's key, and counted in once the workgroup's first loads have
+  // drained.  The count's result is read only when the workgroup leaves:
+  // usually the request's mask wave, in the tail, arrives after every chunk
+  // and runs the walk; if a chunk's count came last, its workgroup runs it on
+  // the way out.
+  constexpr int PU = (2 * TB) / (NW * kWave * 16) < kPrepUnroll ? (2 * TB) / (NW * kWave * 16) : kPrepUnroll;
+  static_assert(!FUSABLE || PU >= 1, "a logits chunk fits the ring's last stage");
+  const int held_g = (FUSABLE && pa.parents != nullptr && id < pa.held) ? id : -1;
+  uint32_t prep_seen = 0;                            // thread 0: the count's result
+  bool prep_counted = false;
+  __shared__ float s_pv[NW];
+  __shared__ int s_pi[NW];
+  __shared__ uint32_t s_walk;                        // prep_leave's own flag (s_last may still be being read)
+  // the chunk's PU 1-KB DMA instructions per wave (addresses past the row's
+  // end read its last float4, which the reduction ignores)
+  auto prep_issue = [&]() {
+    if constexpr (FUSABLE) {
+      const int r = held_g / pa.chunks, c = held_g - r * pa.chunks;
+      const float* row = pa.logits + (int64_t)r * pa.row_stride;
+      const int64_t V4 = pa.V >> 2;
+#pragma unroll
+      for (int j = 0; j < PU; ++j) {
+        const int64_t e4 = (int64_t)c * (NW * kWave * PU) + (int64_t)(wave0 * PU + j) * kWave + lane0;
+        dma16(row + 4 * (e4 < V4 ? e4 : V4 - 1), LDS_ADDR(smem) + (2 * (NSTAGE - 1)) * TB + (wave0 * PU + j) * 1024);
+      }
+    }
+  };
+  // after the wave issued n_tiles more tiles: wait for the chunk, reduce it,
+  // fold (thread 0); every wave calls it
+  auto prep_reduce = [&](int n_tiles) {
+    if constexpr (FUSABLE) {
+      switch (n_tiles) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<PT>(); break;
+        case 2: if constexpr (NSTAGE > 2) wait_vmcnt<2 * PT>(); break;
+        case 3: if constexpr (NSTAGE > 3) wait_vmcnt<3 * PT>(); break;
+        case 4: if constexpr (NSTAGE > 4) wait_vmcnt<4 * PT>(); break;
+        case 5: if constexpr (NSTAGE > 5) wait_vmcnt<5 * PT>(); break;
+        default: if constexpr (NSTAGE > 6) wait_vmcnt<6 * PT>(); break;
+      }
+      const int r = held_g / pa.chunks, c = held_g - r * pa.chunks;
+      const int64_t V4 = pa.V >> 2;
+      ArgBest best{-INFINITY, 0x7fffffff};
+#pragma unroll
+      for (int j = 0; j < PU; ++j) {
+        const int64_t e4 = (int64_t)c * (NW * kWave * PU) + (int64_t)(wave0 * PU + j) * kWave + lane0;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(smem + (2 * (NSTAGE - 1)) * TB +
+                                                           (wave0 * PU + j) * 1024 + 16 * lane0);
+        if (e4 < V4) {
+          const int i0 = (int)(e4 << 2);
+          if (x.x > best.v) { best.v = x.x; best.i = i0; }
+          if (x.y > best.v) { best.v = x.y; best.i = i0 + 1; }
+          if (x.z > best.v) { best.v = x.z; best.i = i0 + 2; }
+          if (x.w > best.v) { best.v = x.w; best.i = i0 + 3; }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) best = arg_better(best, ArgBest{__shfl_xor(best.v, o, kWave), __shfl_xor(best.i, o, kWave)});
+      if (lane0 == 0) {
+        s_pv[wave0] = best.v;
+        s_pi[wave0] = best.i;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): the wave's best is in LDS
+      wg_barrier();
+      if (threadIdx.x == 0) {
+        ArgBest b{s_pv[0], s_pi[0]};
+#pragma unroll
+        for (int w = 1; w < NW; ++w) b = arg_better(b, ArgBest{s_pv[w], s_pi[w]});
+        prep_fold(pa, held_g, b);
+      }
+    }
+  };
+  // count the chunk in (thread 0) once the fold has been performed (the wait
+  // costs nothing where the caller's loads have just drained)
+  auto prep_count_in = [&]() {
+    if constexpr (FUSABLE) {
+      if (threadIdx.x == 0) {
+        wait_vmcnt<0>();
+        prep_seen = __hip_atomic_fetch_add(pa.req_cnt + held_g / pa.chunks / N, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      prep_counted = true;
+    }
+  };
+  auto prep_leave = [&]() {
+    if constexpr (FUSABLE) {
+      if (!prep_counted) prep_count_in();
+      if (threadIdx.x == 0) s_walk = (prep_seen == prep_arrivals(pa, N) - 1) ? 1u : 0u;
+      __syncthreads();
+      if (s_walk && threadIdx.x < kWave) {
+        const int b = held_g / pa.chunks / N, ln = (int)threadIdx.x;
+        const bool live = ln < N;
+        const int p = live ? pa.parents[(size_t)b * N + ln] : 0;
+        const int d = live ? pa.draft_tokens[(size_t)b * N + ln] : 0;
+        prep_walk(pa, b, N, ln, p, d, err_word);
+      }
+    }
+  };
+  if (held_g >= 0) prep_issue();
+  if (u >= max(n_fixed, n_units)) {
+    if (held_g >= 0) {
+      prep_reduce(0);
+      prep_leave();
+    }
+    return;
+  }
+  const int g = Hq / Hkv;
+  const int M = g * N;
 
   // ---- DMA of one tile (tokens t0 .. t0+TILE-1 of the sequence at
   // kbase / vbase; rows at or past t_end repeat row t_end - 1) into stage st:
@@ -329,6 +438,7 @@ void tree_attn_split_kernel(
   if (wave0 == 0)
     for (int c0 = 0; c0 < B; c0 += kWave) dma4(prefix_lens + min(c0 + lane0, B - 1), LDS_ADDR(s_cum) + 4 * c0);
   int f_seg = -1, f_begin = 0, f_end = 0;
+  int pro_tiles = 0;                                 // tiles issued below
   if (u < n_fixed) {
     f_seg = u / n_splits;
     f_begin = (u % n_splits) * split_len;
@@ -340,8 +450,10 @@ void tree_attn_split_kernel(
 #pragma unroll
     for (int i = 0; i < NSTAGE - 1; ++i)
       if (i < nt) dma_tile(kb, vb, f_begin + i * TILE, f_end, i, wave0, lane0, f_begin >> ps_log2);
-    load_q(f_seg / Hkv, f_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
+    pro_tiles = min(nt, NSTAGE - 1);
   }
+  if (held_g >= 0) prep_reduce(pro_tiles);
+  if (u < n_fixed) load_q(f_seg / Hkv, f_seg % Hkv, mt * MT + (wave0 % WM) * RB * 16, lane0 & 15, lane0 >> 4);
   // whether every raw prefix length in s_cum is S_max - N (after a barrier
   // that follows wave 0's wait for its DMAs)
   auto uniform = [&]() -> bool {
@@ -457,7 +569,10 @@ void tree_attn_split_kernel(
     // no fixed split for this unit: it only has work under the balanced schedule
     wait_vmcnt<0>();
     __syncthreads();
-    if (uniform() || !to_balanced()) return;
+    if (uniform() || !to_balanced()) {
+      if (held_g >= 0) prep_leave();
+      return;
+    }
   }
   for (long long x = fixed ? 0 : u_start; x < (fixed ? 1 : u_end);) {
     int b, kvh, L, t_begin, t_end;
@@ -554,6 +669,8 @@ void tree_attn_split_kernel(
 #pragma unroll
       for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
     }
+    // the loads above have drained, the chunk's fold with them
+    if (held_g >= 0 && !prep_counted) prep_count_in();
     if (own_masks) {
       // the request's ancestor-or-self sets by pointer doubling across the
       // wave (lane = node), then each row takes its node's set; a request
@@ -1091,6 +1208,7 @@ void tree_attn_split_kernel(
     if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   wait_vmcnt<0>();   // a unit whose range came out empty still has its guessed tiles in flight
+  if (held_g >= 0) prep_leave();
 }
 
 // fp32 Q/K/V: one wave per (request, node, head), exact fp32 arithmetic on the
@@ -1258,7 +1376,10 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
   long long grid = attn_grid;
   if (prep) {
     pa = *prep;
-    grid += plan_prep(&pa, B, N, WM * WT * kWave);
+    constexpr int TBB = (KVF == kKvF8Mma || KVF == kKvF4Mma ? 2 * kTile : kTile) *
+                        (KVF == kKvF4Mma ? D / 2 : D * (KVF == SPEC_BF16 ? 2 : 1));
+    constexpr int PU = std::min(kPrepUnroll, (2 * TBB) / (WM * WT * kWave * 16));
+    grid += plan_prep(&pa, B, N, WM * WT * kWave, attn_grid, PU);
   }
   hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS, PAGED>), dim3((unsigned)grid),
                      dim3(WM * WT * kWave), 0, st, static_cast<const __bf16*>(q),
