@@ -150,7 +150,7 @@ struct Seg {
   long long start;
 };
 
-template <int D, int KVF, int RB, int WM, int WT, int NSTAGE, bool PAGED>
+template <int D, int KVF, int RB, int WM, int WT, int NSTAGE, bool PAGED, bool STEP>
 __global__ __launch_bounds__(WM * WT * kWave)
 __attribute__((amdgpu_waves_per_eu(SplitOccupancy<D, RB, WM, WT, NSTAGE>::value)))
 void tree_attn_split_kernel(
@@ -186,12 +186,13 @@ void tree_attn_split_kernel(
   constexpr int DB = D / 16;
   static_assert(NLOAD % NW == 0, "DMA instructions must split evenly over the waves");
   static_assert((NSTAGE - 1) * PT < 64, "tiles in flight must fit the vmcnt counter");
-  // The whole verify step in one launch (contiguous bf16 / decoded-fp8
+  // The whole verify step in one launch (STEP; contiguous bf16 / decoded-fp8
   // caches): workgroups past the attention's grid take the prep role (masks,
   // argmax, accept walk), and the attention builds its rows' ancestor masks
   // from pa.parents itself.  They come last, so they fill the CUs that the
   // attention's workgroups leave as they finish.
-  constexpr bool FUSABLE = !PAGED && !F8;
+  constexpr bool FUSABLE = STEP;
+  static_assert(!STEP || (!PAGED && !F8), "the one-launch step covers contiguous bf16 / decoded-fp8 caches");
   if constexpr (FUSABLE) {
     if ((int)blockIdx.x >= attn_grid) {
       prep_block<NW * kWave, kPrepTailUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
@@ -1362,7 +1363,7 @@ struct PagedArgs {
   int max_pages, ps_log2, num_pages;
 };
 
-template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED>
+template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED, bool STEP>
 static void launch_split(const AttnPlan& pl, const void* q, const void* k, const void* v,
                          const float* ks, const float* vs, const int32_t* pre, const uint64_t* anc,
                          int B, int N, int Hq, int Hkv, int S_max, float sm_scale, void* out,
@@ -1374,14 +1375,14 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
   // one-launch verify step: the prep workgroups follow the attention's
   PrepArgs pa{};
   long long grid = attn_grid;
-  if (prep) {
+  if constexpr (STEP) {
     pa = *prep;
     constexpr int TBB = (KVF == kKvF8Mma || KVF == kKvF4Mma ? 2 * kTile : kTile) *
                         (KVF == kKvF4Mma ? D / 2 : D * (KVF == SPEC_BF16 ? 2 : 1));
     constexpr int PU = std::min(kPrepUnroll, (2 * TBB) / (WM * WT * kWave * 16));
     grid += plan_prep(&pa, B, N, WM * WT * kWave, attn_grid, PU);
   }
-  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS, PAGED>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((tree_attn_split_kernel<D, KVF, RB, WM, WT, NS, PAGED, STEP>), dim3((unsigned)grid),
                      dim3(WM * WT * kWave), 0, st, static_cast<const __bf16*>(q),
                      static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), ks, vs, pre,
                      anc, B, N, Hq, Hkv, S_max, sm_scale, pl.split_len, pl.n_splits, pl.n_units, pl.n_mt,
@@ -1427,9 +1428,19 @@ static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, con
 #define SPEC_TRY(RB_, WM_, WT_, NS_)                                                                  \
   if constexpr (split_fits<D, KVF, RB_, WM_, WT_, NS_, PAGED>()) {                                    \
     if (pl.rb == RB_ && pl.wm == WM_ && pl.wt == WT_ && pl.nstage == NS_) {                           \
-      launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, S_max, \
-                                                      sm_scale, out, lse, po, pml, cnt, err, pg, prep, st); \
-      return true;                                                                                    \
+      if (!prep) {                                                                                    \
+        launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED, false>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, \
+                                                               S_max, sm_scale, out, lse, po, pml, cnt, err, \
+                                                               pg, prep, st);                          \
+        return true;                                                                                  \
+      }                                                                                               \
+      if constexpr (!PAGED && KVF != kKvF8Mma && KVF != kKvF4Mma) {                                   \
+        launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED, true>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, \
+                                                              S_max, sm_scale, out, lse, po, pml, cnt, err, pg, \
+                                                              prep, st);                              \
+        return true;                                                                                  \
+      }                                                                                               \
+      return false;                                                                                   \
     }                                                                                                 \
   }
   if constexpr (KVF == kKvF8Mma || KVF == kKvF4Mma) {
