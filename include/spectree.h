@@ -366,8 +366,8 @@ spec_status spec_tree_attn_backward(const void* q, const void* k_cache, const vo
 
 /*
  * spec_verify_step_workspace_bytes -- scratch needed by spec_verify_step for
- * these sizes: a 64-bit argmax key and a counter per node, a counter per
- * request and a chunk queue, rounded up to 256 bytes, followed by
+ * these sizes: a 64-bit argmax key and a counter per node and a counter per
+ * request, rounded up to 256 bytes, followed by
  * spec_tree_attn_workspace_bytes(...).  0 for sizes that spec_verify_step
  * would reject.
  */

@@ -24,10 +24,10 @@ pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
 
-# (workload, what it exercises): rows are cut into chunks of whole 8192-logit
-# passes until about 1024 workgroups scan them, so V = 32000 is 4 chunks per
-# row, 151936 is 19 (B=3, N=16) and 4099 one chunk (N = 60); 5003 ends on a
-# scalar tail; an fp8 cache.
+# (workload, what it exercises): the prologue scan (bf16 and the fp8 cache's
+# half-size chunks, V a multiple of 4, few rows) or tail scanners (V = 5003
+# ending on a scalar tail, 151936 in 19 chunks per row, 4099 in one, N = 60);
+# the fp32 path's separate launch.
 CASES = {
     "chain6_b8_bf16_p2048": W[1],
     "tree16_ragged_V5003": W[2].replace(B=4, prefix_lo=100, prefix_hi=1500, V=5003, seed=21),
@@ -86,8 +86,9 @@ def _small_step(V, seed=5, base=None):
 
 # Where the argmax runs: the fp32 path's own prep launch; bf16 with V a
 # multiple of 4 and few rows: the attention workgroups' prologue (one chunk
-# each, the mask waves walking); bf16 otherwise: the tail's queue of chunks.
-TIE_PATHS = {"f32_own_launch": (W[0], 70001), "bf16_prologue": (W[1], 70000), "bf16_tail_queue": (W[1], 70001)}
+# each, the mask waves walking); bf16 otherwise: scanning workgroups in the
+# attention's tail.
+TIE_PATHS = {"f32_own_launch": (W[0], 70001), "bf16_prologue": (W[1], 70000), "bf16_tail": (W[1], 70001)}
 
 
 @pytest.mark.parametrize("path", list(TIE_PATHS))
@@ -143,7 +144,7 @@ def test_workspace_is_left_zeroed_and_reused():
     nbytes = st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     a = _run(d, x, workspace=ws)
-    prep = (w.B * w.N * 12 + w.B * 4 + 4 + 255) // 256 * 256
+    prep = (w.B * w.N * 12 + w.B * 4 + 255) // 256 * 256
     assert int(ws[:prep].count_nonzero()) == 0
     b = _run(d, x, workspace=ws)
     for k in KEYS:

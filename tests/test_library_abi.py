@@ -180,10 +180,10 @@ def test_backward_host_checks(L):
 
 def test_verify_step_workspace_bytes(L):
     f = L.spec_verify_step_workspace_bytes
-    # a 64-bit argmax key and a counter per node, a counter per request, the chunk queue
-    # (8*6*12 + 8*4 + 4 = 612 bytes, rounded up to 768), then the attention's workspace
+    # a 64-bit argmax key and a counter per node, a counter per request (8*6*12 + 8*4 = 608 bytes,
+    # rounded up to 768), then the attention's workspace
     assert f(8, 6, 32, 8, 128, 2054) == 768 + L.spec_tree_attn_workspace_bytes(8, 6, 32, 8, 128, 2054)
-    assert f(64, 64, 64, 8, 128, 4160) == 64 * 64 * 12 + 512 + L.spec_tree_attn_workspace_bytes(64, 64, 64, 8, 128,
+    assert f(64, 64, 64, 8, 128, 4160) == 64 * 64 * 12 + 256 + L.spec_tree_attn_workspace_bytes(64, 64, 64, 8, 128,
                                                                                                 4160)
     for bad in [(0, 6, 32, 8, 128, 2054), (8, 0, 32, 8, 128, 2054), (8, 65, 32, 8, 128, 2054),
                 (8, 6, 32, 8, 96, 2054), (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 128, 5)]:

@@ -36,20 +36,14 @@
 
 namespace spectree {
 
-// float4 loads in flight per thread and pass of the argmax scan: in a launch
-// of its own, and in the attention's tail (one pass per chunk there: the
-// chunks start as attention workgroups leave their CUs, so fewer, wider
-// chunks need fewer free CUs)
+// float4 loads in flight per thread and pass of the argmax scan
 constexpr int kPrepUnroll = 8;
-constexpr int kPrepTailUnroll = 16;
-// in a launch of its own: about this many argmax workgroups in all -- rows
-// are cut into chunks (a whole number of passes each) only as far as that
-// takes, since every chunk costs atomics on its row's key and counter
+// about this many scanning workgroups in all: rows are cut into chunks (a
+// whole number of passes each) only as far as that takes, since every chunk
+// costs atomics on its row's key and counter
 constexpr long long kPrepTargetWgs = 1024;
 // a request with at most this many chunks counts them on one word
 constexpr int kPrepOneLevel = 64;
-// at most this many scan workgroups in the attention's tail
-constexpr long long kPrepTailWgs = 2048;
 
 struct PrepArgs {
   const int32_t* parents;
@@ -61,8 +55,7 @@ struct PrepArgs {
   int chunks;            // chunks per row
   int one_level;         // count chunks straight into the request's counter
   int n_mask_wg;         // workgroups that build the masks
-  int n_scan_wg;         // workgroups that scan (tail: they draw chunks from a queue)
-  int tail;              // in the attention's tail: chunks go to whichever workgroup draws them
+  int n_scan_wg;         // workgroups that scan a chunk each
   int held;              // chunks [0, held) are scanned by the attention's workgroups (chunk g by workgroup g)
   int mask_counts;       // each request's mask wave counts itself in as one more arrival
   int vec;               // rows 16-byte aligned: float4 loads
@@ -75,14 +68,12 @@ struct PrepArgs {
   uint64_t* keys;        // [rows], zero between calls
   uint32_t* row_cnt;     // [rows], zero between calls
   uint32_t* req_cnt;     // [B], zero between calls
-  uint32_t* queue;       // [1], zero between calls: chunks drawn so far
 };
 
-// Bytes of workspace the prep role needs (keys, row and request counters,
-// the chunk queue), rounded up to 256.
+// Bytes of workspace the prep role needs (keys, row and request counters),
+// rounded up to 256.
 inline size_t prep_workspace_bytes(int B, int N) {
-  const size_t raw =
-      (size_t)B * N * (sizeof(uint64_t) + sizeof(uint32_t)) + (size_t)B * sizeof(uint32_t) + sizeof(uint32_t);
+  const size_t raw = (size_t)B * N * (sizeof(uint64_t) + sizeof(uint32_t)) + (size_t)B * sizeof(uint32_t);
   return (raw + 255) & ~(size_t)255;
 }
 
@@ -91,22 +82,20 @@ inline size_t prep_workspace_bytes(int B, int N) {
 // attention's launch, whose first host_wgs workgroups are the attention's.
 // Then, when every chunk (host_unroll float4 per thread, what the attention's
 // LDS stage holds) fits one attention workgroup each and a request's chunks
-// fit one counter, the attention's
-// workgroups scan them in their prologue (in the shadow of their first
-// tiles) and count them in at once, and the mask waves in the tail arrive
-// last and run the walks while the attention still works.  Otherwise the
-// tail's scanners take the chunks (one pass of kPrepTailUnroll loads each).
+// fit one counter, the attention's workgroups scan them in their prologue (in
+// the shadow of their first tiles) and count them in at once, and the mask
+// waves in the tail arrive last and run the walks while the attention still
+// works.  Otherwise scanning workgroups take the chunks, about
+// kPrepTargetWgs of them (in the attention's tail they start as its
+// workgroups leave their CUs).
 inline long long plan_prep(PrepArgs* pa, int B, int N, int nt, long long host_wgs, int host_unroll = 0) {
   const long long rows = (long long)B * N;
   pa->n_mask_wg = (B + nt / kWave - 1) / (nt / kWave);
-  pa->tail = host_wgs > 0;
   pa->held = 0;
   pa->mask_counts = 0;
-  const long long pass = (long long)nt * kPrepUnroll * 4;
-  const long long max_chunks = (pa->V + pass - 1) / pass;
   const long long hpass = (long long)nt * host_unroll * 4;   // a chunk in the attention's prologue
   const long long h_chunks = host_unroll > 0 ? (pa->V + hpass - 1) / hpass : 0;
-  if (pa->tail && host_unroll > 0 && pa->vec && pa->V % 4 == 0 && N * h_chunks <= kPrepOneLevel &&
+  if (host_wgs > 0 && host_unroll > 0 && pa->vec && pa->V % 4 == 0 && N * h_chunks <= kPrepOneLevel &&
       rows * h_chunks <= host_wgs) {
     pa->chunk_len = hpass;
     pa->chunks = (int)h_chunks;
@@ -116,22 +105,20 @@ inline long long plan_prep(PrepArgs* pa, int B, int N, int nt, long long host_wg
     pa->n_scan_wg = 0;
     return pa->n_mask_wg;
   }
-  if (pa->tail) {
-    pa->chunk_len = (long long)nt * kPrepTailUnroll * 4;
-  } else {
-    long long target = kPrepTargetWgs;
+  long long target = kPrepTargetWgs;
 #ifdef SPEC_PREP_HOOK
-    SPEC_PREP_HOOK(target);
+  SPEC_PREP_HOOK(target);
 #endif
-    long long want = (target + rows - 1) / rows;
-    if (want > max_chunks) want = max_chunks;
-    if (want < 1) want = 1;
-    const long long per = (pa->V + want - 1) / want;
-    pa->chunk_len = ((per + pass - 1) / pass) * pass;
-  }
+  const long long pass = (long long)nt * kPrepUnroll * 4;
+  const long long max_chunks = (pa->V + pass - 1) / pass;
+  long long want = (target + rows - 1) / rows;
+  if (want > max_chunks) want = max_chunks;
+  if (want < 1) want = 1;
+  const long long per = (pa->V + want - 1) / want;
+  pa->chunk_len = ((per + pass - 1) / pass) * pass;
   pa->chunks = (int)((pa->V + pa->chunk_len - 1) / pa->chunk_len);
   pa->one_level = (long long)N * pa->chunks <= kPrepOneLevel;
-  pa->n_scan_wg = (int)(pa->tail ? std::min<long long>(rows * pa->chunks, kPrepTailWgs) : rows * pa->chunks);
+  pa->n_scan_wg = (int)(rows * pa->chunks);
   return pa->n_mask_wg + pa->n_scan_wg;
 }
 
@@ -146,7 +133,6 @@ inline void place_prep_workspace(PrepArgs* pa, void* ws, int B, int N) {
   pa->keys = static_cast<uint64_t*>(ws);
   pa->row_cnt = reinterpret_cast<uint32_t*>(pa->keys + rows);
   pa->req_cnt = pa->row_cnt + rows;
-  pa->queue = pa->req_cnt + B;
 }
 
 // Unsigned-orderable key of a (value, index) pair: the float's bits mapped so
@@ -249,14 +235,7 @@ __device__ __forceinline__ void prep_chunk(const PrepArgs& pa, int g, int B, int
 }
 
 // Prep workgroup blk of NT threads (every thread of the workgroup calls it):
-// a mask builder, or a scanner.  In a launch of its own scanner k takes chunk
-// k.  In the attention's tail the scanners start only as attention
-// workgroups leave their CUs -- the XCDs free theirs at different times
-// (workgroups go round-robin over the XCDs, and the split merges gather on
-// some of them) -- so each draws chunks from a queue until it runs dry and
-// the first free CUs take the most.  Every scanner draws once past the end, so
-// a call makes exactly chunks + scanners draws, and the last of them resets
-// the queue.
+// a mask builder, or the scanner of chunk blk - n_mask_wg.
 template <int NT, int UNROLL>
 __device__ __forceinline__ void prep_block(const PrepArgs& pa, int blk, int B, int N, uint32_t* err_word) {
   const int tid = threadIdx.x;
@@ -285,24 +264,7 @@ __device__ __forceinline__ void prep_block(const PrepArgs& pa, int blk, int B, i
     }
     return;
   }
-  if (!pa.tail) {
-    prep_chunk<NT, UNROLL>(pa, blk - pa.n_mask_wg, B, N, err_word);
-    return;
-  }
-  const uint32_t total = (uint32_t)(B * N * pa.chunks);
-  const uint32_t draws = total + (uint32_t)pa.n_scan_wg;
-  __shared__ uint32_t s_g;
-  for (;;) {
-    if (tid == 0) {
-      const uint32_t gg = __hip_atomic_fetch_add(pa.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      if (gg == draws - 1) __hip_atomic_store(pa.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      s_g = gg;
-    }
-    __syncthreads();
-    const uint32_t gg = s_g;
-    if (gg >= total) return;                           // every thread read s_g before any leaves
-    prep_chunk<NT, UNROLL>(pa, (int)gg, B, N, err_word);   // its barriers order the next write of s_g
-  }
+  prep_chunk<NT, UNROLL>(pa, blk - pa.n_mask_wg, B, N, err_word);
 }
 
 }  // namespace spectree

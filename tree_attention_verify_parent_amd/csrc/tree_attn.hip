@@ -195,7 +195,7 @@ void tree_attn_split_kernel(
   static_assert(!STEP || (!PAGED && !F8), "the one-launch step covers contiguous bf16 / decoded-fp8 caches");
   if constexpr (FUSABLE) {
     if ((int)blockIdx.x >= attn_grid) {
-      prep_block<NW * kWave, kPrepTailUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
+      prep_block<NW * kWave, kPrepUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
       return;
     }
   }
