@@ -189,3 +189,50 @@ def test_too_small_workspace_is_rejected_before_any_launch():
     ws = torch.zeros(nbytes - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(st.SpecError):
         _run(d, x, workspace=ws)
+
+
+# Edge cases through the fused entry point, each against the four calls and the
+# oracle: a single-node tree (nothing to accept), a one-token vocabulary, one
+# request, a full 64-node tree with an fp8 cache, a prefix of zero.
+EDGE = {
+    "one_node": W[1].replace(B=3, N=1, prefix_lo=100, prefix_hi=300, V=4096, seed=41),
+    "vocab_1": W[1].replace(B=2, V=1, seed=42),
+    "one_request": W[2].replace(B=1, prefix_lo=2000, prefix_hi=2000, V=8192, seed=43),
+    "tree64_fp8": W[4].replace(B=2, N=64, Hq=8, Hkv=4, max_depth=12, max_children=4, prefix_lo=130,
+                               prefix_hi=700, V=1024, seed=44),
+    "prefix_0": W[2].replace(B=2, prefix_lo=0, prefix_hi=0, V=2000, seed=45),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_fused_step_edge_cases(name):
+    w = EDGE[name]
+    log(f"[step edge] {name} B={w.B} N={w.N} V={w.V} kv={w.kv_dtype} seed={w.seed}")
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    a = _run(d, x, fused=True)
+    b = _run(d, x, fused=False)
+    for k in KEYS:
+        assert np.array_equal(a[k].numpy(), b[k].numpy()), k
+    assert np.array_equal(_bits(a["out"]), _bits(b["out"]))
+    assert int(a["err"][0]) == 0
+    r = oracle_step(x)
+    got = {k: (v.numpy().view(np.uint64) if k == "mask" else v.numpy()) for k, v in a.items() if k in KEYS}
+    check_integers(got, r, name)
+
+
+def test_fused_step_flags_a_bad_prefix_and_keeps_the_others():
+    w = CASES["chain6_b8_bf16_p2048"].replace(B=4, prefix_lo=500, prefix_hi=1500, seed=46)
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    bad = d["prefix_lens"].clone()
+    bad[2] = w.S_max - w.N + 1                                  # its tree would run past the cache
+    r = st.verify_step(d["parents"], d["draft_tokens"], bad, d["q"], d["k_cache"], d["v_cache"], d["logits"],
+                       x["sm_scale"])
+    torch.cuda.synchronize()
+    assert int(r["err"][0]) == st.DERR_PREFIX
+    want = oracle_step(x)
+    # masks, argmax and walk do not depend on the prefix lengths: every request's are exact
+    assert np.array_equal(r["argmax"].cpu().numpy(), want["argmax"])
+    assert np.array_equal(r["accept_len"].cpu().numpy(), want["accept_len"])
+    assert np.array_equal(r["mask"].cpu().numpy().view(np.uint64), want["mask"])
