@@ -236,3 +236,49 @@ def test_fused_step_flags_a_bad_prefix_and_keeps_the_others():
     assert np.array_equal(r["argmax"].cpu().numpy(), want["argmax"])
     assert np.array_equal(r["accept_len"].cpu().numpy(), want["accept_len"])
     assert np.array_equal(r["mask"].cpu().numpy().view(np.uint64), want["mask"])
+
+
+def test_fused_step_replays_in_a_graph():
+    """Steps captured in a HIP graph on one workspace: every replay, with eager
+    work and synchronisation in between, repeats the eager results bit for bit
+    (the workspace's keys and counters are left zeroed by each step, and the
+    step records no memset)."""
+    w = CASES["tree16_fp8kv"]
+    cases = [synth.make_inputs(w.replace(seed=s)) for s in (51, 52)]
+    devs = [to_device(x) for x in cases]
+    ws = torch.zeros(st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max), dtype=torch.uint8,
+                     device="cuda")
+    outs = [st.step_outputs(w.B, w.N, d["q"]) for d in devs]
+
+    def step(j):
+        d = devs[j]
+        st.verify_step(d["parents"], d["draft_tokens"], d["prefix_lens"], d["q"], d["k_cache"], d["v_cache"],
+                       d["logits"], cases[j]["sm_scale"], k_scale=d["k_scale"], v_scale=d["v_scale"], workspace=ws,
+                       outs=outs[j])
+
+    for j in range(2):
+        step(j)
+    torch.cuda.synchronize()
+    eager = [{k: v.clone() for k, v in o.items()} for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)                                                 # warm the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in (0, 1, 0):
+            step(j)
+    for rep in range(3):
+        for o in outs:
+            for k in o:
+                o[k].fill_(-7 if o[k].dtype != torch.int8 else 0)
+        g.replay()
+        torch.cuda.synchronize()
+        for j in range(2):
+            for k in KEYS[:-1]:
+                assert torch.equal(outs[j][k], eager[j][k]), (rep, j, k)
+            assert torch.equal(outs[j]["out"].view(torch.int16), eager[j]["out"].view(torch.int16)), (rep, j)
+        assert int(ws[:(w.B * w.N * 12 + w.B * 4 + 255) // 256 * 256].count_nonzero()) == 0
+        torch.cuda.synchronize()
