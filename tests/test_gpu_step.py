@@ -124,12 +124,13 @@ def test_ties_across_chunks_go_to_the_lowest_index(path):
         assert np.array_equal(got[k].numpy(), ref[k].numpy()), k
 
 
-def test_strided_and_misaligned_logits():
-    w, x, d = _small_step(5003, seed=6)
+@pytest.mark.parametrize("base", ["f32_own_launch", "bf16_one_launch"])
+def test_strided_and_misaligned_logits(base):
+    w, x, d = _small_step(5003, seed=6, base=W[0] if base == "f32_own_launch" else W[1])
     rows = w.B * w.N
     g = torch.Generator().manual_seed(7)
-    base = torch.randn(rows, 5005, generator=g).cuda()
-    for lg in (base[:, :5003], base[:, 1:5004], base[:, 2:]):    # stride 5005; 4- and 8-byte offsets
+    base_lg = torch.randn(rows, 5005, generator=g).cuda()
+    for lg in (base_lg[:, :5003], base_lg[:, 1:5004], base_lg[:, 2:]):   # stride 5005; 4- and 8-byte offsets
         got = _run(d, x, logits=lg)
         ref = _run(d, x, logits=lg, fused=False)
         for k in KEYS:
