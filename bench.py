@@ -68,7 +68,8 @@ def parse():
     ap.add_argument("--no-commit", action="store_true", help="skip timing the commit step")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the attention's backward pass")
     ap.add_argument("--page-size", type=int, default=16,
-                    help="also time the attention over a paged copy of the cache with this page size (0: skip)")
+                    help="also time the attention, and the whole step (spec_verify_step_paged), over a paged "
+                         "copy of the cache with this page size (0: skip)")
     ap.add_argument("--copy-calibration", type=float, default=0,
                     help="only run a plain float32 elementwise copy that reads and writes this many "
                          "bytes (5 launches) and exit: the reference point that scales the HBM byte "
@@ -422,7 +423,26 @@ def main():
         pbytes = bytes_["attention"] + B * maxp * 4
         paged = dict(page_size=ps, launch_us=round(paged_us, 3), achieved_gbs=round(pbytes / paged_us / 1e3, 1),
                      frac=round(pbytes / paged_us / 1e3 / PEAK_HBM_GBS, 4))
-        del kps, vps
+        # the whole step over the pages (spec_verify_step_paged, one launch)
+        ws_sp = torch.zeros(st.verify_step_workspace_bytes(B, N, w.Hq, w.Hkv, w.D, maxp * ps), dtype=torch.uint8,
+                            device=dev)
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg):
+            for c in range(calls):
+                st.verify_step(parents, draft, prefix, qs[c % R], kps[c % R], vps[c % R], lgs[c % R], x["sm_scale"],
+                               k_scale=ks, v_scale=vs, block_table=table, workspace=ws_sp, outs=outs)
+        torch.cuda.synchronize()
+        sg.replay()
+        torch.cuda.synchronize()
+        if int(err.item()) != 0:
+            raise SystemExit(f"paged step: device error word 0x{int(err.item()):x}")
+        p0.record()
+        for _ in range(reps):
+            sg.replay()
+        p1.record()
+        torch.cuda.synchronize()
+        paged["step_us"] = round(p0.elapsed_time(p1) * 1e3 / (reps * calls), 3)
+        del kps, vps, sg
 
     # ---- e4m3 caches: the same attention in fp8 arithmetic (both products on
     # the fp8 matrix cores, q and p quantized in the kernel)

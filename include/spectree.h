@@ -16,6 +16,7 @@
  *   spec_tree_attn_verify_f8 the attention in fp8 arithmetic over an e4m3 cache
  *   spec_tree_attn_verify_f4 ... over an e2m1 (FP4) cache
  *   spec_verify_step       mask, attention, argmax and accept walk in one launch
+ *   spec_verify_step_paged the same over a paged cache
  *
  * Conventions shared by every entry point
  *   - Every array argument is DEVICE memory owned by the caller.  The library
@@ -401,7 +402,9 @@ size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv, int D, in
  *   accept_len, path_nodes, out_tokens  out (as spec_accept_walk)
  *   workspace     >= spec_verify_step_workspace_bytes(...) bytes, 16-B
  *                 aligned, zero-filled before its first use; every call
- *                 leaves it zeroed again, so it is reused without clearing.
+ *                 leaves it ready for the next one (its argmax keys and
+ *                 counters back at zero, as the attention's split counters),
+ *                 so it is reused without clearing.
  *                 Calls that overlap in time must not share one workspace.
  *   err_word      nullable: SPEC_DERR_ROOT / _PARENT / _TOKEN / _PREFIX
  * Every argument check of spec_tree_attn_verify is made before the first
@@ -417,6 +420,37 @@ spec_status spec_verify_step(const int32_t* parents, const int32_t* draft_tokens
                              int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
                              int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                              uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_verify_step_paged -- spec_verify_step over a paged cache, in one
+ * launch.
+ *
+ * The same step (Aurora, section 2; Runtime Draft Model Training, "Overview")
+ * with the K/V caches in the page layout of spec_tree_attn_verify_paged, for
+ * the serving engine that keeps its caches paged.  Every output equals that
+ * of spec_tree_mask_build, spec_tree_attn_verify_paged, spec_vocab_argmax and
+ * spec_accept_walk on the same inputs.
+ *
+ *   k_pages, v_pages, kv_dtype, block_table, max_pages, page_size, num_pages
+ *                 as in spec_tree_attn_verify_paged (bf16 q; bf16 or e4m3
+ *                 pages)
+ *   workspace     >= spec_verify_step_workspace_bytes(B, N, Hq, Hkv, D,
+ *                 max_pages * page_size) bytes; the rules of spec_verify_step
+ *   err_word      nullable: as spec_verify_step, plus SPEC_DERR_PAGE
+ *   everything else as in spec_verify_step.
+ * Every argument check is made before the launch, so a non-SPEC_OK status
+ * other than SPEC_ERR_HIP means nothing was enqueued.
+ */
+spec_status spec_verify_step_paged(const int32_t* parents, const int32_t* draft_tokens, const int32_t* prefix_lens,
+                                   const void* q, spec_dtype q_dtype, const void* k_pages, const void* v_pages,
+                                   spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                                   const float* logits, int64_t V, int64_t logits_row_stride,
+                                   int B, int N, int Hq, int Hkv, int D, float sm_scale,
+                                   uint64_t* anc_mask, int32_t* depth, void* out, float* lse,
+                                   int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
+                                   int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                   uint32_t* err_word, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* spec_status_string(spec_status status);

@@ -144,3 +144,18 @@ def check_tree_rows(dk, dv, rk, rv, prefix, N):
         rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
         log(f"  {gname} tree rows: rel_l2={rel:.3e}")
         assert rel <= 1e-2, (gname, rel)
+
+
+def paginate(cache: torch.Tensor, page_size: int, rng):
+    """[B][Hkv][S][D] -> (pages [num_pages][page_size][Hkv][D], table int32[B][max_pages]) with the
+    pages of all requests shuffled through one pool (plus unused pages)."""
+    B, Hkv, S, D = cache.shape
+    maxp = -(-S // page_size)
+    num_pages = B * maxp + 5
+    perm = rng.permutation(num_pages)[: B * maxp].reshape(B, maxp).astype(np.int32)
+    padded = torch.zeros(B, Hkv, maxp * page_size, D, dtype=cache.dtype)
+    padded[:, :, :S] = cache
+    pages = torch.zeros(num_pages, page_size, Hkv, D, dtype=cache.dtype)
+    blocks = padded.view(B, Hkv, maxp, page_size, D).permute(0, 2, 3, 1, 4)     # [B][maxp][ps][Hkv][D]
+    pages[torch.from_numpy(perm.reshape(-1)).long()] = blocks.reshape(B * maxp, page_size, Hkv, D)
+    return pages, perm

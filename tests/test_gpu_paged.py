@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 import tree_attention_verify_parent_amd as st
-from tests.gpu_util import check_attention, log, oracle_views, to_device
+from tests.gpu_util import check_attention, log, oracle_views, paginate, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -27,29 +27,14 @@ CASES = {
 }
 
 
-def _paginate(cache: torch.Tensor, page_size: int, rng):
-    """[B][Hkv][S][D] -> (pages [num_pages][page_size][Hkv][D], table int32[B][max_pages]) with the
-    pages of all requests shuffled through one pool (plus unused pages)."""
-    B, Hkv, S, D = cache.shape
-    maxp = -(-S // page_size)
-    num_pages = B * maxp + 5
-    perm = rng.permutation(num_pages)[: B * maxp].reshape(B, maxp).astype(np.int32)
-    padded = torch.zeros(B, Hkv, maxp * page_size, D, dtype=cache.dtype)
-    padded[:, :, :S] = cache
-    pages = torch.zeros(num_pages, page_size, Hkv, D, dtype=cache.dtype)
-    blocks = padded.view(B, Hkv, maxp, page_size, D).permute(0, 2, 3, 1, 4)     # [B][maxp][ps][Hkv][D]
-    pages[torch.from_numpy(perm.reshape(-1)).long()] = blocks.reshape(B * maxp, page_size, Hkv, D)
-    return pages, perm
-
-
 @pytest.mark.parametrize("name", list(CASES))
 def test_paged_attention_matches_oracle(name):
     w, ps = CASES[name]
     log(f"[paged] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} page={ps} kv={w.kv_dtype}")
     x = synth.make_inputs(w, with_logits=False)
     rng = np.random.default_rng(7)
-    kp, table = _paginate(x["k_cache"], ps, rng)
-    vp, _ = _paginate(x["v_cache"], ps, np.random.default_rng(7))
+    kp, table = paginate(x["k_cache"], ps, rng)
+    vp, _ = paginate(x["v_cache"], ps, np.random.default_rng(7))
     d = to_device(x)
     anc, _, _ = st.tree_mask_build(d["parents"])
     out, lse, err = st.tree_attn_verify_paged(d["q"], kp.cuda(), vp.cuda(), d["prefix_lens"], anc,
@@ -73,8 +58,8 @@ def test_paged_attention_matches_oracle(name):
 def test_paged_flags_bad_page_ids():
     w = W[2].replace(B=3, prefix_lo=200, prefix_hi=200, V=10, seed=67)
     x = synth.make_inputs(w, with_logits=False)
-    kp, table = _paginate(x["k_cache"], 16, np.random.default_rng(3))
-    vp, _ = _paginate(x["v_cache"], 16, np.random.default_rng(3))
+    kp, table = paginate(x["k_cache"], 16, np.random.default_rng(3))
+    vp, _ = paginate(x["v_cache"], 16, np.random.default_rng(3))
     table = table.copy()
     table[1, 3] = kp.shape[0] + 4                    # outside the pool, in the used range of request 1
     d = to_device(x)

@@ -214,3 +214,32 @@ def test_verify_step_host_checks(L):
     assert step(wsb=need - 1) == SPEC_ERR_WORKSPACE               # the attention's part is one byte short
     assert step(wsb=100) == SPEC_ERR_WORKSPACE                    # not even the argmax keys fit
     assert step(ws=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN
+
+
+def test_verify_step_paged_host_checks(L):
+    # 8 requests of 6 nodes over 16-token pages, 129 pages each (S_max 2064)
+    need = L.spec_verify_step_workspace_bytes(8, 6, 32, 8, 128, 129 * 16)
+    assert need > 0
+
+    def step(parents=FAKE, table=FAKE, out=FAKE, V=32000, stride=32000, qd=1, kvd=1, pages=(129, 16, 1100),
+             shape=(8, 6, 32, 8, 128), scale=0.088, ws=FAKE, wsb=need, q=FAKE):
+        return L.spec_verify_step_paged(parents, FAKE, FAKE, q, qd, FAKE, FAKE, kvd, None, None, table, *pages,
+                                        FAKE, V, stride, *shape, scale, FAKE, None, out, None, FAKE, FAKE, FAKE,
+                                        FAKE, ws, wsb, None, None)
+    assert step(parents=None) == SPEC_ERR_NULL
+    assert step(table=None) == SPEC_ERR_NULL
+    assert step(out=None) == SPEC_ERR_NULL
+    assert step(stride=31999) == SPEC_ERR_SHAPE
+    assert step(shape=(8, 65, 32, 8, 128)) == SPEC_ERR_SHAPE
+    assert step(shape=(8, 6, 32, 8, 96)) == SPEC_ERR_SHAPE
+    assert step(qd=0, kvd=0) == SPEC_ERR_DTYPE                    # no fp32 pages
+    assert step(kvd=2) == SPEC_ERR_NULL                           # fp8 pages without scales
+    assert step(pages=(129, 24, 1100)) == SPEC_ERR_SHAPE          # page size not a power of two
+    assert step(pages=(129, 8192, 1100)) == SPEC_ERR_SHAPE
+    assert step(pages=(2049, 16, 1100)) == SPEC_ERR_SHAPE         # table wider than 2048 pages
+    assert step(pages=(129, 16, 0)) == SPEC_ERR_SHAPE
+    assert step(scale=float("inf")) == SPEC_ERR_SHAPE
+    assert step(q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
+    assert step(ws=None) == SPEC_ERR_WORKSPACE
+    assert step(wsb=need - 1) == SPEC_ERR_WORKSPACE
+    assert step(ws=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN

@@ -34,7 +34,7 @@ EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_
            "spec_tree_attn_verify_paged", "spec_tree_attn_verify_f8", "spec_tree_attn_verify_f4",
            "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted",
            "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_verify_step_workspace_bytes",
-           "spec_verify_step", "spec_status_string"]
+           "spec_verify_step", "spec_verify_step_paged", "spec_status_string"]
 
 
 class SpecError(RuntimeError):
@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
                                    c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                    c_p, c_sz, c_p, c_p]
     L.spec_verify_step.restype = c_i
+    L.spec_verify_step_paged.argtypes = [c_p, c_p, c_p, c_p, c_i, c_p, c_p, c_i, c_p, c_p, c_p, c_i, c_i, c_i,
+                                         c_p, c_i64, c_i64, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_p, c_p,
+                                         c_p, c_p, c_p, c_p, c_sz, c_p, c_p]
+    L.spec_verify_step_paged.restype = c_i
     L.spec_status_string.argtypes = [c_i]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -153,7 +157,7 @@ def tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc_mask, sm_scale, *, k_
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
     ws_need = attn_workspace_bytes(B, N, Hq, Hkv, D, S_max)
     if workspace is None and ws_need:
-        # zero-filled once; the library leaves it zeroed after each call
+        # zero-filled once; every call leaves it ready for the next (counters back at zero)
         workspace = torch.zeros(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     err = _err_word(err, dev)
@@ -350,29 +354,42 @@ def step_outputs(B, N, q):
 
 
 def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *,
-                k_scale=None, v_scale=None, workspace=None, fused=True, outs=None, debug=False, stream=None):
+                k_scale=None, v_scale=None, block_table=None, workspace=None, fused=True, outs=None, debug=False,
+                stream=None):
     """One verify step on the GPU: masks, attention, argmax, accept walk.
 
     ``fused`` (default): spec_verify_step, one launch (two for fp32), with
     ``workspace`` (zero-filled before its
-    first use, left zeroed; allocated here when None).  ``fused=False``: the
+    first use, left ready for reuse; allocated here when None).  ``fused=False``: the
     four separate calls (``workspace`` is then the attention's).  Both enqueue on one stream and give the same
     results; nothing synchronises unless ``debug`` is set, in which case the
     device error word is read and a non-zero value raises.  ``outs``
     (from step_outputs; its error word is OR'ed into, not cleared) receives
-    the results instead of fresh tensors.
+    the results instead of fresh tensors.  With ``block_table`` (int32
+    [B][max_pages]) the caches are pools of pages [num_pages][page_size][Hkv][D]
+    (spec_verify_step_paged; unfused: spec_tree_attn_verify_paged).
     """
     dev = q.device
     B, N = parents.shape
     Hq, D = q.shape[2], q.shape[3]
-    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    paged = block_table is not None
+    if paged:
+        num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+        max_pages = block_table.shape[1]
+        S_max = max_pages * page_size
+    else:
+        Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
     o = step_outputs(B, N, q) if outs is None else outs
     anc, depth, out, lse, t = o["mask"], o["depth"], o["out"], o["lse"], o["argmax"]
     L, path, toks, err = o["accept_len"], o["path_nodes"], o["out_tokens"], o["err"]
     if not fused:
         tree_mask_build(parents, anc_mask=anc, depth=depth, err=err, stream=stream)
-        tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc, sm_scale, k_scale=k_scale, v_scale=v_scale,
-                         out=out, lse=lse, workspace=workspace, err=err, stream=stream)
+        if paged:
+            tree_attn_verify_paged(q, k_cache, v_cache, prefix_lens, anc, block_table, sm_scale, k_scale=k_scale,
+                                   v_scale=v_scale, out=out, lse=lse, workspace=workspace, err=err, stream=stream)
+        else:
+            tree_attn_verify(q, k_cache, v_cache, prefix_lens, anc, sm_scale, k_scale=k_scale, v_scale=v_scale,
+                             out=out, lse=lse, workspace=workspace, err=err, stream=stream)
         vocab_argmax(logits, out=t, stream=stream)
         accept_walk(parents, anc, draft_tokens, t.view(B, N), logits.shape[1], accept_len=L, path_nodes=path,
                     out_tokens=toks, err=err, stream=stream)
@@ -386,12 +403,22 @@ def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits,
             workspace = torch.zeros(max(verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max), 16),
                                     dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
-        _check(lib().spec_verify_step(
-            _ptr(parents), _ptr(draft_tokens), _ptr(prefix_lens), _ptr(q), _DTYPE[q.dtype], _ptr(k_cache),
-            _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(k_scale), _ptr(v_scale),
-            ctypes.c_void_p(logits.data_ptr()), V, logits.stride(0), B, N, Hq, Hkv, D, S_max, float(sm_scale),
-            _ptr(anc), _ptr(depth), _ptr(out), _ptr(lse), _ptr(t), _ptr(L), _ptr(path), _ptr(toks),
-            _ptr(workspace), ws_bytes, _ptr(err), _stream(stream)))
+        if paged:
+            if tuple(k_cache.shape) != (num_pages, page_size, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+                raise SpecError("k / v pages must be [num_pages][page_size][Hkv][D] matching q")
+            _check(lib().spec_verify_step_paged(
+                _ptr(parents), _ptr(draft_tokens), _ptr(prefix_lens), _ptr(q), _DTYPE[q.dtype], _ptr(k_cache),
+                _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(k_scale), _ptr(v_scale), _ptr(block_table), max_pages,
+                page_size, num_pages, ctypes.c_void_p(logits.data_ptr()), V, logits.stride(0), B, N, Hq, Hkv, D,
+                float(sm_scale), _ptr(anc), _ptr(depth), _ptr(out), _ptr(lse), _ptr(t), _ptr(L), _ptr(path),
+                _ptr(toks), _ptr(workspace), ws_bytes, _ptr(err), _stream(stream)))
+        else:
+            _check(lib().spec_verify_step(
+                _ptr(parents), _ptr(draft_tokens), _ptr(prefix_lens), _ptr(q), _DTYPE[q.dtype], _ptr(k_cache),
+                _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(k_scale), _ptr(v_scale),
+                ctypes.c_void_p(logits.data_ptr()), V, logits.stride(0), B, N, Hq, Hkv, D, S_max, float(sm_scale),
+                _ptr(anc), _ptr(depth), _ptr(out), _ptr(lse), _ptr(t), _ptr(L), _ptr(path), _ptr(toks),
+                _ptr(workspace), ws_bytes, _ptr(err), _stream(stream)))
     res = dict(mask=anc, depth=depth, out=out, lse=lse, argmax=t, accept_len=L, path_nodes=path,
                out_tokens=toks, err=err)
     if debug:

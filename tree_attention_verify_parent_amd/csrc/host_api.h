@@ -30,4 +30,22 @@ spec_status tree_attn_verify_with_prep(const void* q, const void* k_cache, const
                                        float* lse, void* workspace, size_t workspace_bytes, uint32_t* err_word,
                                        const PrepArgs& prep, hipStream_t stream);
 
+// SPEC_OK when spec_tree_attn_verify_paged would accept these arguments
+// (workspace aside), else the status it would return without launching.
+spec_status tree_attn_paged_check(const void* q, spec_dtype q_dtype, const void* k_pages, const void* v_pages,
+                                  spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                  const int32_t* prefix_lens, const uint64_t* anc_mask, const int32_t* block_table,
+                                  int max_pages, int page_size, int num_pages, int B, int N, int Hq, int Hkv, int D,
+                                  float sm_scale, const void* out);
+
+// spec_tree_attn_verify_paged; with prep non-null the verify step's prep
+// role joins the same launch.
+spec_status tree_attn_verify_paged_run(const void* q, spec_dtype q_dtype, const void* k_pages, const void* v_pages,
+                                       spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                       const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                       const int32_t* block_table, int max_pages, int page_size, int num_pages, int B,
+                                       int N, int Hq, int Hkv, int D, float sm_scale, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                       const PrepArgs* prep, hipStream_t stream);
+
 }  // namespace spectree

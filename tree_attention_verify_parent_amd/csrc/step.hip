@@ -26,6 +26,55 @@ extern "C" size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv
   return attn ? prep_workspace_bytes(B, N) + attn : 0;
 }
 
+namespace spectree {
+
+// The step's own pointers and sizes.
+static spec_status step_check(const int32_t* parents, const int32_t* draft_tokens, const float* logits, int64_t V,
+                              int64_t logits_row_stride, int B, int N, const uint64_t* anc_mask,
+                              const int32_t* target_argmax, const int32_t* accept_len, const int32_t* path_nodes,
+                              const int32_t* out_tokens) {
+  if (!parents || !draft_tokens || !logits || !anc_mask || !target_argmax || !accept_len || !path_nodes ||
+      !out_tokens)
+    return SPEC_ERR_NULL;
+  if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1 || V > 0x7fffffffLL || logits_row_stride < V)
+    return SPEC_ERR_SHAPE;
+  return SPEC_OK;
+}
+
+// The workspace check (full_ws_bytes: the step's size for these sizes, the
+// same for every dtype; the fp32 attention leaves its part unused) and the
+// prep arguments; on SPEC_OK *attn_ws / *attn_ws_bytes are the attention's
+// part of the workspace.
+static spec_status step_place(const int32_t* parents, const int32_t* draft_tokens, const float* logits, int64_t V,
+                              int64_t logits_row_stride, int B, int N, size_t full_ws_bytes, uint64_t* anc_mask,
+                              int32_t* depth, int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
+                              int32_t* out_tokens, void* workspace, size_t workspace_bytes, PrepArgs* pa,
+                              void** attn_ws, size_t* attn_ws_bytes) {
+  // (0 for sizes the attention rejects: its own check reports them)
+  if (!workspace || workspace_bytes < full_ws_bytes) return SPEC_ERR_WORKSPACE;
+  if (!aligned_to(workspace, 16)) return SPEC_ERR_ALIGN;
+  const size_t prep_bytes = prep_workspace_bytes(B, N);
+  *attn_ws = static_cast<char*>(workspace) + prep_bytes;
+  *attn_ws_bytes = workspace_bytes - prep_bytes;
+  *pa = PrepArgs{};
+  pa->parents = parents;
+  pa->draft_tokens = draft_tokens;
+  pa->logits = logits;
+  pa->V = V;
+  pa->row_stride = logits_row_stride;
+  pa->vec = aligned_to(logits, 16) && (logits_row_stride % 4 == 0);
+  pa->anc_mask = anc_mask;
+  pa->depth = depth;
+  pa->target_argmax = target_argmax;
+  pa->accept_len = accept_len;
+  pa->path_nodes = path_nodes;
+  pa->out_tokens = out_tokens;
+  place_prep_workspace(pa, workspace, B, N);
+  return SPEC_OK;
+}
+
+}  // namespace spectree
+
 extern "C" spec_status spec_verify_step(
     const int32_t* parents, const int32_t* draft_tokens, const int32_t* prefix_lens, const void* q,
     spec_dtype q_dtype, const void* k_cache, const void* v_cache, spec_dtype kv_dtype, const float* k_scale,
@@ -33,38 +82,20 @@ extern "C" spec_status spec_verify_step(
     int Hkv, int D, int S_max, float sm_scale, uint64_t* anc_mask, int32_t* depth, void* out, float* lse,
     int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens, void* workspace,
     size_t workspace_bytes, uint32_t* err_word, hipStream_t stream) {
-  if (!parents || !draft_tokens || !logits || !anc_mask || !target_argmax || !accept_len || !path_nodes ||
-      !out_tokens)
-    return SPEC_ERR_NULL;
-  if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1 || V > 0x7fffffffLL || logits_row_stride < V)
-    return SPEC_ERR_SHAPE;
-  const size_t prep_bytes = prep_workspace_bytes(B, N);
-  // the full size for every dtype (the fp32 attention leaves its part unused)
-  if (!workspace || workspace_bytes < spec_verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max))
-    return SPEC_ERR_WORKSPACE;
-  if (!aligned_to(workspace, 16)) return SPEC_ERR_ALIGN;
-  void* attn_ws = static_cast<char*>(workspace) + prep_bytes;
-  const size_t attn_ws_bytes = workspace_bytes - prep_bytes;
+  spec_status st = step_check(parents, draft_tokens, logits, V, logits_row_stride, B, N, anc_mask, target_argmax,
+                              accept_len, path_nodes, out_tokens);
+  if (st != SPEC_OK) return st;
+  PrepArgs pa;
+  void* attn_ws;
+  size_t attn_ws_bytes;
+  st = step_place(parents, draft_tokens, logits, V, logits_row_stride, B, N,
+                  spec_verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max), anc_mask, depth, target_argmax,
+                  accept_len, path_nodes, out_tokens, workspace, workspace_bytes, &pa, &attn_ws, &attn_ws_bytes);
+  if (st != SPEC_OK) return st;
   // everything the attention would refuse is refused before the first launch
-  const spec_status ast = tree_attn_check(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens,
-                                          anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, attn_ws,
-                                          attn_ws_bytes);
-  if (ast != SPEC_OK) return ast;
-
-  PrepArgs pa{};
-  pa.parents = parents;
-  pa.draft_tokens = draft_tokens;
-  pa.logits = logits;
-  pa.V = V;
-  pa.row_stride = logits_row_stride;
-  pa.vec = aligned_to(logits, 16) && (logits_row_stride % 4 == 0);
-  pa.anc_mask = anc_mask;
-  pa.depth = depth;
-  pa.target_argmax = target_argmax;
-  pa.accept_len = accept_len;
-  pa.path_nodes = path_nodes;
-  pa.out_tokens = out_tokens;
-  place_prep_workspace(&pa, workspace, B, N);
+  st = tree_attn_check(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq,
+                       Hkv, D, S_max, sm_scale, out, attn_ws, attn_ws_bytes);
+  if (st != SPEC_OK) return st;
   if (q_dtype != SPEC_F32)
     return tree_attn_verify_with_prep(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, B, N, Hq, Hkv,
                                       D, S_max, sm_scale, out, lse, attn_ws, attn_ws_bytes, err_word, pa, stream);
@@ -76,4 +107,34 @@ extern "C" spec_status spec_verify_step(
   return spec_tree_attn_verify(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask,
                                B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, attn_ws, attn_ws_bytes, err_word,
                                stream);
+}
+
+extern "C" spec_status spec_verify_step_paged(
+    const int32_t* parents, const int32_t* draft_tokens, const int32_t* prefix_lens, const void* q,
+    spec_dtype q_dtype, const void* k_pages, const void* v_pages, spec_dtype kv_dtype, const float* k_scale,
+    const float* v_scale, const int32_t* block_table, int max_pages, int page_size, int num_pages,
+    const float* logits, int64_t V, int64_t logits_row_stride, int B, int N, int Hq, int Hkv, int D,
+    float sm_scale, uint64_t* anc_mask, int32_t* depth, void* out, float* lse, int32_t* target_argmax,
+    int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+    uint32_t* err_word, hipStream_t stream) {
+  spec_status st = step_check(parents, draft_tokens, logits, V, logits_row_stride, B, N, anc_mask, target_argmax,
+                              accept_len, path_nodes, out_tokens);
+  if (st != SPEC_OK) return st;
+  // the page geometry before the workspace: max_pages * page_size is the
+  // attention's S_max only for accepted sizes
+  st = tree_attn_paged_check(q, q_dtype, k_pages, v_pages, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask,
+                             block_table, max_pages, page_size, num_pages, B, N, Hq, Hkv, D, sm_scale, out);
+  if (st != SPEC_OK) return st;
+  PrepArgs pa;
+  void* attn_ws;
+  size_t attn_ws_bytes;
+  st = step_place(parents, draft_tokens, logits, V, logits_row_stride, B, N,
+                  spec_verify_step_workspace_bytes(B, N, Hq, Hkv, D, max_pages * page_size), anc_mask, depth,
+                  target_argmax, accept_len, path_nodes, out_tokens, workspace, workspace_bytes, &pa, &attn_ws,
+                  &attn_ws_bytes);
+  if (st != SPEC_OK) return st;
+  // one launch: every remaining check of the paged attention comes before it
+  return tree_attn_verify_paged_run(q, q_dtype, k_pages, v_pages, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask,
+                                    block_table, max_pages, page_size, num_pages, B, N, Hq, Hkv, D, sm_scale, out,
+                                    lse, attn_ws, attn_ws_bytes, err_word, &pa, stream);
 }

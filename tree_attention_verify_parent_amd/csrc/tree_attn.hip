@@ -186,13 +186,13 @@ void tree_attn_split_kernel(
   constexpr int DB = D / 16;
   static_assert(NLOAD % NW == 0, "DMA instructions must split evenly over the waves");
   static_assert((NSTAGE - 1) * PT < 64, "tiles in flight must fit the vmcnt counter");
-  // The whole verify step in one launch (STEP; contiguous bf16 / decoded-fp8
-  // caches): workgroups past the attention's grid take the prep role (masks,
-  // argmax, accept walk), and the attention builds its rows' ancestor masks
-  // from pa.parents itself.  They come last, so they fill the CUs that the
-  // attention's workgroups leave as they finish.
+  // The whole verify step in one launch (STEP; bf16 / decoded-fp8 caches,
+  // contiguous or paged): workgroups past the attention's grid take the prep
+  // role (masks, argmax, accept walk), and the attention builds its rows'
+  // ancestor masks from pa.parents itself.  They come last, so they fill the
+  // CUs that the attention's workgroups leave as they finish.
   constexpr bool FUSABLE = STEP;
-  static_assert(!STEP || (!PAGED && !F8), "the one-launch step covers contiguous bf16 / decoded-fp8 caches");
+  static_assert(!STEP || !F8, "the one-launch step covers bf16 / decoded-fp8 caches");
   if constexpr (FUSABLE) {
     if ((int)blockIdx.x >= attn_grid) {
       prep_block<NW * kWave, kPrepUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
@@ -326,7 +326,9 @@ void tree_attn_split_kernel(
       }
     }
   };
-  if (held_g >= 0) prep_issue();
+  // (a paged fixed unit issues it after its page ids, whose loads would
+  // otherwise wait for the chunk as well)
+  if (held_g >= 0 && (!PAGED || u >= n_fixed)) prep_issue();
   if (u >= max(n_fixed, n_units)) {
     if (held_g >= 0) {
       prep_reduce(0);
@@ -445,6 +447,8 @@ void tree_attn_split_kernel(
     f_begin = (u % n_splits) * split_len;
     f_end = min(S_max, f_begin + split_len);
     stage_pages(f_seg / Hkv, f_begin, f_end);
+    if constexpr (PAGED)
+      if (held_g >= 0) prep_issue();
     const unsigned char* kb = seq_base(kc, f_seg / Hkv, f_seg % Hkv);
     const unsigned char* vb = seq_base(vc, f_seg / Hkv, f_seg % Hkv);
     const int nt = (f_end - f_begin + TILE - 1) / TILE;
@@ -1434,7 +1438,7 @@ static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, con
                                                                pg, prep, st);                          \
         return true;                                                                                  \
       }                                                                                               \
-      if constexpr (!PAGED && KVF != kKvF8Mma && KVF != kKvF4Mma) {                                   \
+      if constexpr (KVF != kKvF8Mma && KVF != kKvF4Mma) {                                             \
         launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED, true>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, \
                                                               S_max, sm_scale, out, lse, po, pml, cnt, err, pg, \
                                                               prep, st);                              \
@@ -1627,6 +1631,53 @@ extern "C" spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cac
                    stream);
 }
 
+namespace spectree {
+
+// Every reason spec_tree_attn_verify_paged can refuse a call before it
+// launches anything (the paged verify step checks the same first).
+spec_status tree_attn_paged_check(const void* q, spec_dtype q_dtype, const void* k_pages, const void* v_pages,
+                                  spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                  const int32_t* prefix_lens, const uint64_t* anc_mask, const int32_t* block_table,
+                                  int max_pages, int page_size, int num_pages, int B, int N, int Hq, int Hkv, int D,
+                                  float sm_scale, const void* out) {
+  if (!q || !k_pages || !v_pages || !prefix_lens || !anc_mask || !block_table || !out) return SPEC_ERR_NULL;
+  const bool bf16 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_BF16);
+  const bool fp8 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_FP8_E4M3);
+  if (!bf16 && !fp8) return SPEC_ERR_DTYPE;
+  if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
+  if (page_size < 1 || (page_size & (page_size - 1)) || page_size > 4096) return SPEC_ERR_SHAPE;
+  if (max_pages < 1 || max_pages > kMaxPages || num_pages < 1) return SPEC_ERR_SHAPE;
+  AttnPlan pl;
+  if (!make_plan(B, N, Hq, Hkv, D, max_pages * page_size, &pl)) return SPEC_ERR_SHAPE;
+  if ((long long)num_pages * page_size * Hkv * D >= (1ll << 40)) return SPEC_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out)) return SPEC_ERR_ALIGN;
+  return SPEC_OK;
+}
+
+spec_status tree_attn_verify_paged_run(const void* q, spec_dtype q_dtype, const void* k_pages, const void* v_pages,
+                                       spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                       const int32_t* prefix_lens, const uint64_t* anc_mask,
+                                       const int32_t* block_table, int max_pages, int page_size, int num_pages, int B,
+                                       int N, int Hq, int Hkv, int D, float sm_scale, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                       const PrepArgs* prep, hipStream_t stream) {
+  const spec_status st = tree_attn_paged_check(q, q_dtype, k_pages, v_pages, kv_dtype, k_scale, v_scale, prefix_lens,
+                                               anc_mask, block_table, max_pages, page_size, num_pages, B, N, Hq, Hkv,
+                                               D, sm_scale, out);
+  if (st != SPEC_OK) return st;
+  const int S_max = max_pages * page_size;
+  AttnPlan pl;
+  make_plan(B, N, Hq, Hkv, D, S_max, &pl);
+  int ps_log2 = 0;
+  while ((1 << ps_log2) < page_size) ++ps_log2;
+  return run_split(pl, kv_dtype, q, k_pages, v_pages, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
+                   S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
+                   PagedArgs{block_table, max_pages, ps_log2, num_pages}, stream, prep);
+}
+
+}  // namespace spectree
+
 extern "C" spec_status spec_tree_attn_verify_paged(const void* q, spec_dtype q_dtype, const void* k_pages,
                                                    const void* v_pages, spec_dtype kv_dtype,
                                                    const float* k_scale, const float* v_scale,
@@ -1636,22 +1687,7 @@ extern "C" spec_status spec_tree_attn_verify_paged(const void* q, spec_dtype q_d
                                                    float sm_scale, void* out, float* lse, void* workspace,
                                                    size_t workspace_bytes, uint32_t* err_word,
                                                    hipStream_t stream) {
-  if (!q || !k_pages || !v_pages || !prefix_lens || !anc_mask || !block_table || !out) return SPEC_ERR_NULL;
-  const bool bf16 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_BF16);
-  const bool fp8 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_FP8_E4M3);
-  if (!bf16 && !fp8) return SPEC_ERR_DTYPE;
-  if (fp8 && (!k_scale || !v_scale)) return SPEC_ERR_NULL;
-  if (page_size < 1 || (page_size & (page_size - 1)) || page_size > 4096) return SPEC_ERR_SHAPE;
-  if (max_pages < 1 || max_pages > kMaxPages || num_pages < 1) return SPEC_ERR_SHAPE;
-  const int S_max = max_pages * page_size;
-  AttnPlan pl;
-  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl)) return SPEC_ERR_SHAPE;
-  if ((long long)num_pages * page_size * Hkv * D >= (1ll << 40)) return SPEC_ERR_SHAPE;
-  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out)) return SPEC_ERR_ALIGN;
-  int ps_log2 = 0;
-  while ((1 << ps_log2) < page_size) ++ps_log2;
-  return run_split(pl, bf16 ? SPEC_BF16 : SPEC_FP8_E4M3, q, k_pages, v_pages, k_scale, v_scale, prefix_lens,
-                   anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
-                   PagedArgs{block_table, max_pages, ps_log2, num_pages}, stream);
+  return tree_attn_verify_paged_run(q, q_dtype, k_pages, v_pages, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask,
+                                    block_table, max_pages, page_size, num_pages, B, N, Hq, Hkv, D, sm_scale, out,
+                                    lse, workspace, workspace_bytes, err_word, nullptr, stream);
 }
