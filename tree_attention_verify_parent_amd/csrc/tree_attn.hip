@@ -428,8 +428,12 @@ void tree_attn_split_kernel(
     }
   };
 
-  // ---- Two schedules.  Fixed: unit u < n_fixed is split u % n_splits
-  // (split_len tokens) of sequence u / n_splits.  When every request fills its
+  // ---- Two schedules.  Fixed: unit u < n_fixed is split u % n_splits of
+  // sequence u / n_splits: its ceil(S_max / 64) tiles dealt out in order,
+  // split_len / 64 to a split and one more to each of the last splits that
+  // the remainder needs (so the sequence's final, partial tile goes with a
+  // longer split and no split holds two tiles more than another).  When
+  // every request fills its
   // cache (P_b = S_max - N) that divides the work evenly and needs nothing but
   // the sizes, so the unit's first tiles and Q rows are fetched at once, before
   // the prefix lengths are known.  Balanced (below): for ragged lengths the
@@ -444,8 +448,10 @@ void tree_attn_split_kernel(
   int pro_tiles = 0;                                 // tiles issued below
   if (u < n_fixed) {
     f_seg = u / n_splits;
-    f_begin = (u % n_splits) * split_len;
-    f_end = min(S_max, f_begin + split_len);
+    const int sp = u % n_splits, q_t = split_len / kTile;
+    const int long0 = n_splits - ((S_max + kTile - 1) / kTile - n_splits * q_t);   // first longer split
+    f_begin = (sp * q_t + max(0, sp - long0)) * kTile;
+    f_end = min(S_max, f_begin + (q_t + (sp >= long0 ? 1 : 0)) * kTile);
     stage_pages(f_seg / Hkv, f_begin, f_end);
     if constexpr (PAGED)
       if (held_g >= 0) prep_issue();
@@ -1322,8 +1328,8 @@ constexpr int kTableBytes = 4 * (1024 + 1) + 4;
 // CU, so two waves share each SIMD).  Work then comes in about one unit per
 // resident workgroup slot (256 CUs), each unit for all M-tiles, under one of
 // two schedules the kernel picks from the data: fixed splits of S_max
-// (split_len tokens, never under 256) when every request fills its cache, or
-// equal shares of the actual tokens otherwise.  The plan does not depend on
+// (whole 64-token tiles, at least 4, dealt out evenly) when every request
+// fills its cache, or equal shares of the actual tokens otherwise.  The plan does not depend on
 // the cached dtype, so one workspace size serves every format: partial
 // results for the larger of the two slot counts (a fixed split each, or two
 // per balanced unit) and one counter per (request, kv head, M-tile).
@@ -1348,11 +1354,11 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   p->n_units = (int)std::max<long long>(1, target_wgs / p->n_mt);
   const long long seqs = (long long)B * Hkv;
   const int want = (int)std::max<long long>(1, (p->n_units + seqs - 1) / seqs);
-  int split_len = (S_max + want - 1) / want;
-  split_len = ((split_len + kTile - 1) / kTile) * kTile;
-  if (split_len < 256) split_len = 256;
-  p->split_len = split_len;
-  p->n_splits = (S_max + split_len - 1) / split_len;
+  // fixed splits of whole 64-token tiles, at least 4 each: split_len / 64
+  // tiles to a split, one more to each of the last (tiles mod n_splits)
+  const int tiles = (S_max + kTile - 1) / kTile;
+  p->n_splits = std::min(want, std::max(1, tiles / 4));
+  p->split_len = (tiles / p->n_splits) * kTile;
   if (seqs * p->n_splits * p->n_mt >= (1ll << 31)) return false;
   const size_t slots = (size_t)std::max<long long>(seqs * p->n_splits, 2ll * p->n_units);
   const size_t rows = slots * p->M_pad;
