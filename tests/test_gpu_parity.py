@@ -236,6 +236,28 @@ def test_attention_many_splits_short_requests():
     _attn_case(w, "many_splits", prefix_lens=x["prefix_lens"])
 
 
+# Requests that fill their caches run the fixed splits: a sequence's
+# ceil(S_max / 64) tiles dealt out in order, the same count to each split and
+# one more to each of the last (tiles mod splits).  Lengths chosen for 4
+# splits with two longer ones (1100 tokens), 13 (3333), 2 (520), 64 (16390)
+# and one whole-sequence piece (259), in bf16 and on the e4m3 decode path.
+FIXED = {
+    "S1100_4x_r2": W[1].replace(B=2, Hq=8, Hkv=2, prefix_lo=1094, prefix_hi=1094, V=10, seed=51),
+    "S3333_13x_r1": W[1].replace(B=2, Hq=8, Hkv=2, prefix_lo=3327, prefix_hi=3327, V=10, seed=52),
+    "S520_2x_r1": W[1].replace(B=2, Hq=8, Hkv=2, prefix_lo=514, prefix_hi=514, V=10, seed=53),
+    "S16390_64x_r1": W[1].replace(B=2, Hq=8, Hkv=2, prefix_lo=16384, prefix_hi=16384, V=10, seed=54),
+    "S259_whole": W[1].replace(B=2, Hq=8, Hkv=2, prefix_lo=253, prefix_hi=253, V=10, seed=55),
+    "fp8_S1100": W[4].replace(B=2, Hq=16, Hkv=2, N=6, tree="chain", prefix_lo=1094, prefix_hi=1094, V=10, seed=56),
+}
+
+
+@pytest.mark.parametrize("name", list(FIXED))
+def test_attention_fixed_split_remainders(name):
+    w = FIXED[name]
+    log(f"[fixed] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P={w.prefix_lo} kv={w.kv_dtype}")
+    _attn_case(w, name)
+
+
 def test_attention_balanced_many_requests():
     """More than 64 requests with ragged lengths: the per-request length table
     spans several 64-entry blocks (two-level search), units cross many short
