@@ -68,8 +68,8 @@ def parse():
     ap.add_argument("--no-commit", action="store_true", help="skip timing the commit step")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the attention's backward pass")
     ap.add_argument("--page-size", type=int, default=16,
-                    help="also time the attention, and the whole step (spec_verify_step_paged), over a paged "
-                         "copy of the cache with this page size (0: skip)")
+                    help="also time the attention, the whole step (spec_verify_step_paged) and the commit "
+                         "over a paged copy of the cache with this page size (0: skip)")
     ap.add_argument("--copy-calibration", type=float, default=0,
                     help="only run a plain float32 elementwise copy that reads and writes this many "
                          "bytes (5 launches) and exit: the reference point that scales the HBM byte "
@@ -442,7 +442,27 @@ def main():
         p1.record()
         torch.cuda.synchronize()
         paged["step_us"] = round(p0.elapsed_time(p1) * 1e3 / (reps * calls), 3)
-        del kps, vps, sg
+        # the commit over the pages (spec_commit_accepted_paged), on the accepted
+        # paths of the last step, in place (the rows it moves do not change its cost)
+        newp_p = torch.empty(B, dtype=torch.int32, device=dev)
+        labels_p = torch.empty((B, N), dtype=torch.int8, device=dev)
+        cg_p = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg_p):
+            for c in range(calls):
+                st.commit_accepted(kps[c % R], vps[c % R], prefix, acc_len, path, block_table=table,
+                                   new_prefix_lens=newp_p, labels=labels_p, err=err)
+        torch.cuda.synchronize()
+        cg_p.replay()
+        torch.cuda.synchronize()
+        if int(err.item()) != 0:
+            raise SystemExit(f"paged commit: device error word 0x{int(err.item()):x}")
+        p0.record()
+        for _ in range(reps):
+            cg_p.replay()
+        p1.record()
+        torch.cuda.synchronize()
+        paged["commit_us"] = round(p0.elapsed_time(p1) * 1e3 / (reps * calls), 3)
+        del kps, vps, sg, cg_p
 
     # ---- e4m3 caches: the same attention in fp8 arithmetic (both products on
     # the fp8 matrix cores, q and p quantized in the kernel)

@@ -12,6 +12,7 @@
  *   spec_vocab_argmax      per-node argmax of the target logits
  *   spec_accept_walk       longest matched root-to-node path -> accepted tokens
  *   spec_commit_accepted   (after the step) keep the accepted path's K/V, label outcomes
+ *   spec_commit_accepted_paged  the same over a paged cache
  *   spec_tree_attn_backward (training) gradients of the tree-masked attention
  *   spec_tree_attn_verify_f8 the attention in fp8 arithmetic over an e4m3 cache
  *   spec_tree_attn_verify_f4 ... over an e2m1 (FP4) cache
@@ -262,6 +263,32 @@ spec_status spec_commit_accepted(void* k_cache, void* v_cache, spec_dtype kv_dty
                                  const int32_t* path_nodes, int B, int N, int Hkv, int D, int S_max,
                                  int32_t* new_prefix_lens, int8_t* node_labels,
                                  uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_commit_accepted_paged -- spec_commit_accepted over a paged cache.
+ *
+ * The same step for the serving engine whose caches are paged (Aurora,
+ * section 2), in the page layout of spec_tree_attn_verify_paged: request b's
+ * logical row t is slot t % page_size of page block_table[b][t / page_size].
+ * The moves, outputs and errors are those of spec_commit_accepted on the
+ * logical rows (S_max = max_pages * page_size); pages are never allocated,
+ * freed or reordered.
+ *
+ *   k_pages,
+ *   v_pages      [num_pages][page_size][Hkv][D] of kv_dtype (any of the
+ *                three), 16-B aligned; updated in place
+ *   block_table  int32[B][max_pages], 1 <= max_pages <= 2048
+ *   page_size    a power of two, 1..4096
+ *   err_word     nullable: as spec_commit_accepted, plus SPEC_DERR_PAGE when
+ *                a page holding one of the request's tree rows (P .. P+N-1)
+ *                is outside [0, num_pages); that request is left unchanged
+ */
+spec_status spec_commit_accepted_paged(void* k_pages, void* v_pages, spec_dtype kv_dtype,
+                                       const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                                       const int32_t* prefix_lens, const int32_t* accept_len,
+                                       const int32_t* path_nodes, int B, int N, int Hkv, int D,
+                                       int32_t* new_prefix_lens, int8_t* node_labels,
+                                       uint32_t* err_word, hipStream_t stream);
 
 /*
  * spec_tree_attn_verify_f8 -- the same attention in fp8 arithmetic, for e4m3

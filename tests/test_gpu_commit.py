@@ -1,4 +1,5 @@
-"""GPU parity of the commit step (spec_commit_accepted) against the oracle.
+"""GPU parity of the commit step (spec_commit_accepted, and over a paged
+cache spec_commit_accepted_paged) against the oracle.
 
 The caches are compared byte for byte: the step only moves rows.  The accepted
 paths come from the GPU's own mask / argmax / walk (those are checked against
@@ -11,7 +12,7 @@ import torch
 import oracle
 import synth
 import tree_attention_verify_parent_amd as st
-from tests.gpu_util import log, to_device
+from tests.gpu_util import log, paginate, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +109,71 @@ def test_commit_flags_bad_input_and_leaves_cache_alone():
         ko, vo, po, lo = oracle.commit_accepted(_bytes(k)[[0, 2]], _bytes(v)[[0, 2]], np.array(prefix)[[0, 2]],
                                                 np.array(L)[[0, 2]], path.cpu().numpy()[[0, 2]], N)
         assert np.array_equal(_bytes(kk)[[0, 2]], ko) and np.array_equal(_bytes(vv)[[0, 2]], vo), what
+
+
+# ---- the same step over a paged cache (spec_commit_accepted_paged): the
+# oracle gathers the pool back to the contiguous layout (its own gather) and
+# commits there; the pool's pages that no request uses stay as they were.
+PAGED = {
+    "tree16_ragged_bf16_p16": (CASES["tree16_ragged_bf16"], 16),
+    "tree16_fp8kv_p32": (CASES["tree16_fp8kv"], 32),
+    "chain6_f32_p8": (CASES["chain6_f32"], 8),
+    "tree64_deep_bf16_p1": (CASES["tree64_deep_bf16"], 1),
+}
+
+
+def _paged_case(w, ps, seed=3, corrupt=None):
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    L, path, err = _walk_on_gpu(d, w)
+    kp, table = paginate(x["k_cache"], ps, np.random.default_rng(seed))
+    vp, _ = paginate(x["v_cache"], ps, np.random.default_rng(seed))
+    if corrupt is not None:
+        table = table.copy()
+        corrupt(table, kp.shape[0])
+    kp, vp = kp.cuda(), vp.cuda()
+    kb, vb = _bytes(kp), _bytes(vp)
+    newp, lab, err = st.commit_accepted(kp, vp, d["prefix_lens"], L, path, block_table=torch.from_numpy(table).cuda(),
+                                        err=err)
+    torch.cuda.synchronize()
+    return x, table, kb, vb, kp, vp, L.cpu().numpy(), path.cpu().numpy(), newp.cpu().numpy(), lab.cpu().numpy(), err
+
+
+@pytest.mark.parametrize("name", list(PAGED))
+def test_paged_commit_matches_oracle(name):
+    w, ps = PAGED[name]
+    log(f"[commit paged] {name} B={w.B} N={w.N} Hkv={w.Hkv} D={w.D} kv={w.kv_dtype} page={ps}")
+    x, table, kb, vb, kp, vp, Lc, pc, newp, lab, err = _paged_case(w, ps)
+    assert int(err[0]) == 0
+    S_pad = table.shape[1] * ps
+    ko, vo, po, lo = oracle.commit_accepted(oracle.gather_pages(kb, table, ps, S_pad),
+                                            oracle.gather_pages(vb, table, ps, S_pad), x["prefix_lens"], Lc, pc, w.N)
+    assert np.array_equal(oracle.gather_pages(_bytes(kp), table, ps, S_pad), ko)
+    assert np.array_equal(oracle.gather_pages(_bytes(vp), table, ps, S_pad), vo)
+    assert np.array_equal(newp, po) and np.array_equal(lab, lo)
+    unused = np.setdiff1d(np.arange(kb.shape[0]), table.reshape(-1))
+    assert len(unused) > 0
+    assert np.array_equal(_bytes(kp)[unused], kb[unused]) and np.array_equal(_bytes(vp)[unused], vb[unused])
+
+
+def test_paged_commit_flags_a_page_outside_the_pool():
+    w = CASES["tree16_ragged_bf16"]
+    ps = 16
+    pre = synth.make_inputs(w)["prefix_lens"]
+
+    def corrupt(table, num_pages):
+        table[1, int(pre[1]) // ps] = num_pages + 3          # the page of request 1's root row
+    x, table, kb, vb, kp, vp, Lc, pc, newp, lab, err = _paged_case(w, ps, corrupt=corrupt)
+    assert int(err[0]) == st.DERR_PAGE
+    # request 1 is left alone; the others are committed as the oracle does
+    keep = [b for b in range(w.B) if b != 1]
+    S_pad = table.shape[1] * ps
+    tk = table[keep]
+    ko, vo, po, lo = oracle.commit_accepted(oracle.gather_pages(kb, tk, ps, S_pad), oracle.gather_pages(vb, tk, ps, S_pad),
+                                            x["prefix_lens"][keep], Lc[keep], pc[keep], w.N)
+    assert np.array_equal(oracle.gather_pages(_bytes(kp), tk, ps, S_pad), ko)
+    assert np.array_equal(oracle.gather_pages(_bytes(vp), tk, ps, S_pad), vo)
+    assert np.array_equal(newp[keep], po) and np.array_equal(lab[keep], lo)
+    # every page request 1 maps (inside the pool) is unchanged
+    own = np.array([p for p in table[1] if 0 <= p < kb.shape[0]])
+    assert np.array_equal(_bytes(kp)[own], kb[own]) and np.array_equal(_bytes(vp)[own], vb[own])

@@ -243,3 +243,21 @@ def test_verify_step_paged_host_checks(L):
     assert step(ws=None) == SPEC_ERR_WORKSPACE
     assert step(wsb=need - 1) == SPEC_ERR_WORKSPACE
     assert step(ws=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN
+
+
+def test_commit_paged_host_checks(L):
+    def commit(table=FAKE, kvd=1, pages=(16, 16, 40), shape=(4, 6, 2, 128), k=FAKE, newp=FAKE):
+        return L.spec_commit_accepted_paged(k, FAKE, kvd, table, *pages, FAKE, FAKE, FAKE, *shape, newp, None,
+                                            None, None)
+    assert commit(table=None) == SPEC_ERR_NULL
+    assert commit(k=None) == SPEC_ERR_NULL
+    assert commit(newp=None) == SPEC_ERR_NULL
+    assert commit(kvd=7) == SPEC_ERR_DTYPE
+    assert commit(pages=(16, 12, 40)) == SPEC_ERR_SHAPE           # page size not a power of two
+    assert commit(pages=(16, 8192, 40)) == SPEC_ERR_SHAPE
+    assert commit(pages=(2049, 16, 40)) == SPEC_ERR_SHAPE         # table wider than 2048 pages
+    assert commit(pages=(16, 16, 0)) == SPEC_ERR_SHAPE
+    assert commit(pages=(1, 4, 40)) == SPEC_ERR_SHAPE             # 4 rows cannot hold a 6-node tree
+    assert commit(shape=(4, 6, 2, 96)) == SPEC_ERR_SHAPE
+    assert commit(shape=(4, 65, 2, 128)) == SPEC_ERR_SHAPE
+    assert commit(k=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN

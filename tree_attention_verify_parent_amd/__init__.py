@@ -32,7 +32,7 @@ _DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3f
 
 EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
            "spec_tree_attn_verify_paged", "spec_tree_attn_verify_f8", "spec_tree_attn_verify_f4",
-           "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted",
+           "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted", "spec_commit_accepted_paged",
            "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_verify_step_workspace_bytes",
            "spec_verify_step", "spec_verify_step_paged", "spec_status_string"]
 
@@ -76,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.spec_accept_walk.restype = c_i
     L.spec_commit_accepted.argtypes = [c_p, c_p, c_i, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p]
     L.spec_commit_accepted.restype = c_i
+    L.spec_commit_accepted_paged.argtypes = [c_p, c_p, c_i, c_p, c_i, c_i, c_i, c_p, c_p, c_p, c_i, c_i, c_i, c_i,
+                                             c_p, c_p, c_p, c_p]
+    L.spec_commit_accepted_paged.restype = c_i
     L.spec_tree_attn_backward_workspace_bytes.argtypes = [c_i] * 6
     L.spec_tree_attn_backward_workspace_bytes.restype = c_sz
     L.spec_tree_attn_backward.argtypes = [c_p, c_p, c_p, c_i, c_p, c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_i,
@@ -280,20 +283,30 @@ def accept_walk(parents, anc_mask, draft_tokens, target_argmax, V, *, accept_len
     return accept_len, path_nodes, out_tokens, err
 
 
-def commit_accepted(k_cache, v_cache, prefix_lens, accept_len, path_nodes, *, new_prefix_lens=None,
-                    labels=None, want_labels=True, err=None, stream=None):
+def commit_accepted(k_cache, v_cache, prefix_lens, accept_len, path_nodes, *, block_table=None,
+                    new_prefix_lens=None, labels=None, want_labels=True, err=None, stream=None):
     """In place: request b's accepted path node at depth k moves to cache row
     prefix_lens[b] + k.  Returns (new_prefix_lens int32[B], labels int8[B][N]
-    or None, err)."""
-    B, Hkv, S_max, D = k_cache.shape
-    N = path_nodes.shape[1]
+    or None, err).  With ``block_table`` (int32 [B][max_pages]) the caches are
+    pools of pages [num_pages][page_size][Hkv][D] (spec_commit_accepted_paged)."""
+    B, N = path_nodes.shape
     if k_cache.dtype not in _DTYPE or v_cache.dtype != k_cache.dtype or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise SpecError("k_cache / v_cache must be matching [B][Hkv][S_max][D] tensors of a supported dtype")
+        raise SpecError("k_cache / v_cache must be matching 4-d tensors of a supported dtype")
     dev = k_cache.device
     new_prefix_lens = torch.empty(B, dtype=torch.int32, device=dev) if new_prefix_lens is None else new_prefix_lens
     if labels is None and want_labels:
         labels = torch.empty((B, N), dtype=torch.int8, device=dev)
     err = _err_word(err, dev)
+    if block_table is not None:
+        num_pages, page_size, Hkv, D = k_cache.shape
+        _check(lib().spec_commit_accepted_paged(
+            _ptr(k_cache), _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(block_table), block_table.shape[1],
+            page_size, num_pages, _ptr(prefix_lens), _ptr(accept_len), _ptr(path_nodes), B, N, Hkv, D,
+            _ptr(new_prefix_lens), _ptr(labels), _ptr(err), _stream(stream)))
+        return new_prefix_lens, labels, err
+    if k_cache.shape[0] != B:
+        raise SpecError("k_cache / v_cache must be [B][Hkv][S_max][D]")
+    _, Hkv, S_max, D = k_cache.shape
     _check(lib().spec_commit_accepted(_ptr(k_cache), _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(prefix_lens),
                                       _ptr(accept_len), _ptr(path_nodes), B, N, Hkv, D, S_max,
                                       _ptr(new_prefix_lens), _ptr(labels), _ptr(err), _stream(stream)))
