@@ -403,8 +403,7 @@ size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv, int D, in
 
 /*
  * spec_verify_step -- one whole verify step: spec_tree_mask_build,
- * spec_tree_attn_verify, spec_vocab_argmax and spec_accept_walk in one launch
- * (two for fp32).
+ * spec_tree_attn_verify, spec_vocab_argmax and spec_accept_walk in one launch.
  *
  * The target verifies the draft's whole tree in one parallel pass and keeps
  * the longest path it agrees with (Aurora, section 2; Runtime Draft Model
@@ -413,9 +412,8 @@ size_t spec_verify_step_workspace_bytes(int B, int N, int Hq, int Hkv, int D, in
  * workgroups that build the masks, take the argmax (each logits row cut into
  * chunks, folded with 64-bit atomic maxima) and run each request's walk as
  * soon as its last chunk is done, while the attention builds its rows' masks
- * itself.  For bf16 / e4m3 caches it is one launch; the fp32 attention runs
- * after a separate launch of the rest.  Every output equals that of the four
- * separate calls on the same inputs.
+ * itself.  Every output equals that of the four separate calls on the same
+ * inputs.
  *
  *   parents, draft_tokens, prefix_lens, q, q_dtype, k_cache, v_cache,
  *   kv_dtype, k_scale, v_scale, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse

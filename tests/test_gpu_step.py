@@ -1,6 +1,6 @@
 """The fused verify step (spec_verify_step: masks, attention, argmax and
-accept walk in one launch; the fp32 attention after a separate launch of the
-rest) on the GPU.
+accept walk in one launch, the split kernel's for bf16 and e4m3 caches or the
+fp32 kernel's) on the GPU.
 
 Every other GPU parity test of the whole step (test_gpu_parity,
 test_gpu_fullsize) already runs through the fused entry point against the
@@ -27,7 +27,7 @@ W = synth.WORKLOADS
 # (workload, what it exercises): the prologue scan (bf16 and the fp8 cache's
 # half-size chunks, V a multiple of 4, few rows) or tail scanners (V = 5003
 # ending on a scalar tail, 151936 in 19 chunks per row, 4099 in one, N = 60);
-# the fp32 path's separate launch.
+# the fp32 kernel's launch.
 CASES = {
     "chain6_b8_bf16_p2048": W[1],
     "tree16_ragged_V5003": W[2].replace(B=4, prefix_lo=100, prefix_hi=1500, V=5003, seed=21),
@@ -84,11 +84,11 @@ def _small_step(V, seed=5, base=None):
     return w, x, to_device(x)
 
 
-# Where the argmax runs: the fp32 path's own prep launch; bf16 with V a
+# Where the argmax runs: the fp32 kernel's prep blocks; bf16 with V a
 # multiple of 4 and few rows: the attention workgroups' prologue (one chunk
 # each, the mask waves walking); bf16 otherwise: scanning workgroups in the
 # attention's tail.
-TIE_PATHS = {"f32_own_launch": (W[0], 70001), "bf16_prologue": (W[1], 70000), "bf16_tail": (W[1], 70001)}
+TIE_PATHS = {"f32_kernel": (W[0], 70001), "bf16_prologue": (W[1], 70000), "bf16_tail": (W[1], 70001)}
 
 
 @pytest.mark.parametrize("path", list(TIE_PATHS))
@@ -124,9 +124,9 @@ def test_ties_across_chunks_go_to_the_lowest_index(path):
         assert np.array_equal(got[k].numpy(), ref[k].numpy()), k
 
 
-@pytest.mark.parametrize("base", ["f32_own_launch", "bf16_one_launch"])
+@pytest.mark.parametrize("base", ["f32_kernel", "bf16_one_launch"])
 def test_strided_and_misaligned_logits(base):
-    w, x, d = _small_step(5003, seed=6, base=W[0] if base == "f32_own_launch" else W[1])
+    w, x, d = _small_step(5003, seed=6, base=W[0] if base == "f32_kernel" else W[1])
     rows = w.B * w.N
     g = torch.Generator().manual_seed(7)
     base_lg = torch.randn(rows, 5005, generator=g).cuda()

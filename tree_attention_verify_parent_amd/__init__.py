@@ -371,7 +371,7 @@ def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits,
                 stream=None):
     """One verify step on the GPU: masks, attention, argmax, accept walk.
 
-    ``fused`` (default): spec_verify_step, one launch (two for fp32), with
+    ``fused`` (default): spec_verify_step, one launch, with
     ``workspace`` (zero-filled before its
     first use, left ready for reuse; allocated here when None).  ``fused=False``: the
     four separate calls (``workspace`` is then the attention's).  Both enqueue on one stream and give the same

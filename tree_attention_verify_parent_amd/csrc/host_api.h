@@ -30,6 +30,13 @@ spec_status tree_attn_verify_with_prep(const void* q, const void* k_cache, const
                                        float* lse, void* workspace, size_t workspace_bytes, uint32_t* err_word,
                                        const PrepArgs& prep, hipStream_t stream);
 
+// spec_tree_attn_verify for fp32 (arguments already accepted by
+// tree_attn_check), with the verify step's prep role in the same launch.
+spec_status tree_attn_f32_with_prep(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* prefix_lens, int B, int N, int Hq, int Hkv, int D, int S_max,
+                                    float sm_scale, void* out, float* lse, uint32_t* err_word, const PrepArgs& prep,
+                                    hipStream_t stream);
+
 // SPEC_OK when spec_tree_attn_verify_paged would accept these arguments
 // (workspace aside), else the status it would return without launching.
 spec_status tree_attn_paged_check(const void* q, spec_dtype q_dtype, const void* k_pages, const void* v_pages,

@@ -1,17 +1,12 @@
 // The whole verify step -- ancestor masks, tree attention, per-node
-// vocabulary argmax, accept walk -- in one launch for bf16 and fp8 caches: the
-// attention kernel's grid gains the prep workgroups of step_ops.h and builds
-// its rows' masks itself.  The fp32 attention (a kernel of its own) follows a
-// separate prep launch.
+// vocabulary argmax, accept walk -- in one launch: the attention kernel's grid
+// (the split kernel's for bf16 and fp8 caches, contiguous or paged; the fp32
+// kernel's) gains the prep workgroups of step_ops.h, and its waves build
+// their rows' masks themselves.
 #include "host_api.h"
 #include "step_ops.h"
 
 namespace spectree {
-
-template <int NT>
-__global__ __launch_bounds__(NT) void verify_prep_kernel(const PrepArgs pa, int B, int N, uint32_t* err_word) {
-  prep_block<NT, kPrepUnroll>(pa, (int)blockIdx.x, B, N, err_word);
-}
 
 static bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -96,17 +91,11 @@ extern "C" spec_status spec_verify_step(
   st = tree_attn_check(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq,
                        Hkv, D, S_max, sm_scale, out, attn_ws, attn_ws_bytes);
   if (st != SPEC_OK) return st;
-  if (q_dtype != SPEC_F32)
-    return tree_attn_verify_with_prep(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, B, N, Hq, Hkv,
-                                      D, S_max, sm_scale, out, lse, attn_ws, attn_ws_bytes, err_word, pa, stream);
-
-  const long long grid = plan_prep(&pa, B, N, 256, 0);
-  if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
-  hipLaunchKernelGGL(verify_prep_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, pa, B, N, err_word);
-  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-  return spec_tree_attn_verify(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, anc_mask,
-                               B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, attn_ws, attn_ws_bytes, err_word,
-                               stream);
+  if (q_dtype == SPEC_F32)
+    return tree_attn_f32_with_prep(q, k_cache, v_cache, prefix_lens, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse,
+                                   err_word, pa, stream);
+  return tree_attn_verify_with_prep(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens, B, N, Hq, Hkv, D,
+                                    S_max, sm_scale, out, lse, attn_ws, attn_ws_bytes, err_word, pa, stream);
 }
 
 extern "C" spec_status spec_verify_step_paged(

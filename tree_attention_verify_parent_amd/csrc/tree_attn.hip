@@ -1226,12 +1226,21 @@ void tree_attn_split_kernel(
 // VALU.  Per 64-key chunk: lane = key for the scores (its K row's loads all in
 // flight together), then lane = output column for the PV sum, with the
 // chunk's 64 V rows loaded at once.
-template <int D>
+// The whole verify step in one launch (STEP): blocks past the attention's
+// grid take the prep role (masks, argmax, accept walk), and each attention
+// wave builds its node's ancestor set from pa.parents itself.
+template <int D, bool STEP>
 __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ prefix_lens, const uint64_t* __restrict__ anc_mask, int N,
     int Hq, int Hkv, int S_max, float sm_scale, float* __restrict__ out, float* __restrict__ lse,
-    uint32_t* __restrict__ err_word) {
+    uint32_t* __restrict__ err_word, int B, int attn_grid, const PrepArgs pa) {
+  if constexpr (STEP) {
+    if ((int)blockIdx.x >= attn_grid) {
+      prep_block<kWave, kPrepUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
+      return;
+    }
+  }
   constexpr int DPL = D / kWave;                 // output columns per lane
   const int h = blockIdx.x % Hq;
   const int i = (blockIdx.x / Hq) % N;
@@ -1244,7 +1253,17 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
     return;
   }
   const int L = P + N;
-  const uint64_t anc = anc_mask[(size_t)b * N + i];
+  uint64_t anc;
+  if constexpr (STEP) {
+    // the request's ancestor-or-self sets by pointer doubling across the wave
+    // (lane = node; a request with a bad parent gets self-only sets, as the
+    // mask build writes them), then this node's
+    const int par = lane < N ? pa.parents[(size_t)b * N + lane] : 0;
+    bool req_bad;
+    anc = shfl_u64(ancestor_set(par, lane, lane < N, nullptr, &req_bad), i);
+  } else {
+    anc = anc_mask[(size_t)b * N + i];
+  }
   const float* qp = q + ((size_t)(b * N + i) * Hq + h) * D;
   float qv[D];
 #pragma unroll
@@ -1549,6 +1568,50 @@ spec_status tree_attn_check(const void* q, spec_dtype q_dtype, const void* k_cac
 
 }  // namespace spectree
 
+// The fp32 kernel, alone or (prep set) with the verify step's prep role in
+// the same launch.
+static spec_status launch_f32(const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_lens,
+                              const uint64_t* anc_mask, int B, int N, int Hq, int Hkv, int D, int S_max,
+                              float sm_scale, void* out, float* lse, uint32_t* err_word, const PrepArgs* prep,
+                              hipStream_t stream) {
+  const long long attn_grid = (long long)B * N * Hq;
+  long long grid = attn_grid;
+  PrepArgs pa{};
+  if (prep) {
+    pa = *prep;
+    grid += plan_prep(&pa, B, N, kWave, 0, 0);
+  }
+  if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
+  const float* qf = static_cast<const float*>(q);
+  const float* kf = static_cast<const float*>(k_cache);
+  const float* vf = static_cast<const float*>(v_cache);
+  float* of = static_cast<float*>(out);
+#define SPEC_F32_LAUNCH(D_, STEP_)                                                                             \
+  hipLaunchKernelGGL((tree_attn_f32_kernel<D_, STEP_>), dim3((unsigned)grid), dim3(kWave), 0, stream, qf, kf, vf, \
+                     prefix_lens, anc_mask, N, Hq, Hkv, S_max, sm_scale, of, lse, err_word, B, (int)attn_grid, pa)
+  if (D == 64) {
+    if (prep) SPEC_F32_LAUNCH(64, true);
+    else SPEC_F32_LAUNCH(64, false);
+  } else {
+    if (prep) SPEC_F32_LAUNCH(128, true);
+    else SPEC_F32_LAUNCH(128, false);
+  }
+#undef SPEC_F32_LAUNCH
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+namespace spectree {
+
+spec_status tree_attn_f32_with_prep(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* prefix_lens, int B, int N, int Hq, int Hkv, int D, int S_max,
+                                    float sm_scale, void* out, float* lse, uint32_t* err_word, const PrepArgs& prep,
+                                    hipStream_t stream) {
+  return launch_f32(q, k_cache, v_cache, prefix_lens, prep.anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse,
+                    err_word, &prep, stream);
+}
+
+}  // namespace spectree
+
 extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, const void* k_cache,
                                              const void* v_cache, spec_dtype kv_dtype,
                                              const float* k_scale, const float* v_scale,
@@ -1566,20 +1629,8 @@ extern "C" spec_status spec_tree_attn_verify(const void* q, spec_dtype q_dtype, 
   AttnPlan pl;
   make_plan(B, N, Hq, Hkv, D, S_max, &pl);
 
-  if (f32) {
-    const unsigned grid = (unsigned)(B * N * Hq);
-    if (D == 64)
-      hipLaunchKernelGGL(tree_attn_f32_kernel<64>, dim3(grid), dim3(kWave), 0, stream,
-                         static_cast<const float*>(q), static_cast<const float*>(k_cache),
-                         static_cast<const float*>(v_cache), prefix_lens, anc_mask, N, Hq, Hkv,
-                         S_max, sm_scale, static_cast<float*>(out), lse, err_word);
-    else
-      hipLaunchKernelGGL(tree_attn_f32_kernel<128>, dim3(grid), dim3(kWave), 0, stream,
-                         static_cast<const float*>(q), static_cast<const float*>(k_cache),
-                         static_cast<const float*>(v_cache), prefix_lens, anc_mask, N, Hq, Hkv,
-                         S_max, sm_scale, static_cast<float*>(out), lse, err_word);
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
-  }
+  if (f32) return launch_f32(q, k_cache, v_cache, prefix_lens, anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out,
+                            lse, err_word, nullptr, stream);
 
   return run_split(pl, bf16 ? SPEC_BF16 : SPEC_FP8_E4M3, q, k_cache, v_cache, k_scale, v_scale, prefix_lens,
                    anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word,
