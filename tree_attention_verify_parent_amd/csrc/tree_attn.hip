@@ -1222,22 +1222,27 @@ void tree_attn_split_kernel(
   if (held_g >= 0) prep_leave();
 }
 
-// fp32 Q/K/V: one wave per (request, node, head), exact fp32 arithmetic on the
-// VALU.  Per 64-key chunk: lane = key for the scores (its K row's loads all in
-// flight together), then lane = output column for the PV sum, with the
-// chunk's 64 V rows loaded at once.
+// fp32 Q/K/V: one workgroup of kF32Waves waves per (request, node, head),
+// exact fp32 arithmetic on the VALU.  Wave w takes the 64-key chunks w,
+// w + kF32Waves, ... with its own online softmax; per chunk: lane = key for
+// the scores (its K row's loads all in flight together), then lane = output
+// column for the PV sum, with the chunk's 64 V rows loaded at once and each
+// key's p read from its lane.  The waves' states are merged in LDS at the end.
 // The whole verify step in one launch (STEP): blocks past the attention's
 // grid take the prep role (masks, argmax, accept walk), and each attention
 // wave builds its node's ancestor set from pa.parents itself.
+constexpr int kF32Waves = 4;
+
 template <int D, bool STEP>
-__global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
+__global__ __launch_bounds__(kF32Waves * kWave) void tree_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ prefix_lens, const uint64_t* __restrict__ anc_mask, int N,
     int Hq, int Hkv, int S_max, float sm_scale, float* __restrict__ out, float* __restrict__ lse,
     uint32_t* __restrict__ err_word, int B, int attn_grid, const PrepArgs pa) {
+  constexpr int NT = kF32Waves * kWave;
   if constexpr (STEP) {
     if ((int)blockIdx.x >= attn_grid) {
-      prep_block<kWave, kPrepUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
+      prep_block<NT, kPrepUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
       return;
     }
   }
@@ -1245,11 +1250,12 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
   const int h = blockIdx.x % Hq;
   const int i = (blockIdx.x / Hq) % N;
   const int b = blockIdx.x / (Hq * N);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   const int kvh = h / (Hq / Hkv);
   const int P = prefix_lens[b];
   if (P < 0 || P > S_max - N) {
-    if (lane == 0 && i == 0 && h == 0) flag_error(err_word, SPEC_DERR_PREFIX);
+    if (threadIdx.x == 0 && i == 0 && h == 0) flag_error(err_word, SPEC_DERR_PREFIX);
     return;
   }
   const int L = P + N;
@@ -1278,9 +1284,8 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
   float o[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.f;
-  __shared__ float sp[kWave];
 
-  for (int c0 = 0; c0 < L; c0 += kWave) {
+  for (int c0 = wave * kWave; c0 < L; c0 += kF32Waves * kWave) {
     const int cmax = min(kWave, L - c0);
     // this chunk's V rows, one column set per lane, all loads in flight
     float vv[kWave][DPL];
@@ -1311,22 +1316,44 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32_kernel(
     const float p = exp2f(s - m_use);
     l_run = l_run * alpha + wave_sum(p);
     m_run = m_new;
-    sp[lane] = p;
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
       float acc = o[k] * alpha;
 #pragma unroll
-      for (int j = 0; j < kWave; ++j) acc = fmaf(sp[j], vv[j][k], acc);
+      for (int j = 0; j < kWave; ++j)
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j)), vv[j][k], acc);
       o[k] = acc;
     }
-    __syncthreads();
+  }
+  // merge the waves' states (a wave with no chunk holds m = -inf, l = 0, o = 0)
+  __shared__ float s_m[kF32Waves], s_l[kF32Waves];
+  __shared__ float s_o[kF32Waves][D];
+  if (lane == 0) {
+    s_m[wave] = m_run;
+    s_l[wave] = l_run;
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) s_o[wave][lane + k * kWave] = o[k];
+  __syncthreads();
+  if (wave != 0) return;
+  float m_tot = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kF32Waves; ++w) m_tot = fmaxf(m_tot, s_m[w]);   // finite: the node sees itself
+  float l_tot = 0.f, acc[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kF32Waves; ++w) {
+    const float a = exp2f(s_m[w] - m_tot);
+    l_tot = fmaf(s_l[w], a, l_tot);
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = fmaf(s_o[w][lane + k * kWave], a, acc[k]);
   }
   float* op = out + ((size_t)(b * N + i) * Hq + h) * D;
-  const float inv = 1.0f / l_run;
+  const float inv = 1.0f / l_tot;
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) op[lane + k * kWave] = o[k] * inv;
-  if (lse && lane == 0) lse[(size_t)(b * N + i) * Hq + h] = (m_run + log2f(l_run)) * kLn2;
+  for (int k = 0; k < DPL; ++k) op[lane + k * kWave] = acc[k] * inv;
+  if (lse && lane == 0) lse[(size_t)(b * N + i) * Hq + h] = (m_tot + log2f(l_tot)) * kLn2;
 }
 
 // ------------------------------------------------------------------ planning
@@ -1579,16 +1606,17 @@ static spec_status launch_f32(const void* q, const void* k_cache, const void* v_
   PrepArgs pa{};
   if (prep) {
     pa = *prep;
-    grid += plan_prep(&pa, B, N, kWave, 0, 0);
+    grid += plan_prep(&pa, B, N, kF32Waves * kWave, 0, 0);
   }
   if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
   const float* qf = static_cast<const float*>(q);
   const float* kf = static_cast<const float*>(k_cache);
   const float* vf = static_cast<const float*>(v_cache);
   float* of = static_cast<float*>(out);
-#define SPEC_F32_LAUNCH(D_, STEP_)                                                                             \
-  hipLaunchKernelGGL((tree_attn_f32_kernel<D_, STEP_>), dim3((unsigned)grid), dim3(kWave), 0, stream, qf, kf, vf, \
-                     prefix_lens, anc_mask, N, Hq, Hkv, S_max, sm_scale, of, lse, err_word, B, (int)attn_grid, pa)
+#define SPEC_F32_LAUNCH(D_, STEP_)                                                                   \
+  hipLaunchKernelGGL((tree_attn_f32_kernel<D_, STEP_>), dim3((unsigned)grid), dim3(kF32Waves * kWave), 0, \
+                     stream, qf, kf, vf, prefix_lens, anc_mask, N, Hq, Hkv, S_max, sm_scale, of, lse, err_word, B, \
+                     (int)attn_grid, pa)
   if (D == 64) {
     if (prep) SPEC_F32_LAUNCH(64, true);
     else SPEC_F32_LAUNCH(64, false);
