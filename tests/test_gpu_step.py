@@ -18,7 +18,7 @@ import torch
 import oracle
 import synth
 import tree_attention_verify_parent_amd as st
-from tests.gpu_util import check_integers, log, oracle_step, to_device
+from tests.gpu_util import check_integers, log, oracle_step, paginate, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -239,15 +239,34 @@ def test_fused_step_flags_a_bad_prefix_and_keeps_the_others():
     assert np.array_equal(r["mask"].cpu().numpy().view(np.uint64), want["mask"])
 
 
-def test_fused_step_replays_in_a_graph():
+# (workload, page size or 0 for a contiguous cache): the split kernel's step
+# on an e4m3 cache, the fp32 kernel's, and the paged step
+GRAPH_CASES = {
+    "fp8kv": (CASES["tree16_fp8kv"], 0),
+    "f32": (W[0].replace(B=2, V=3000), 0),
+    "bf16_paged_p16": (W[2].replace(B=3, prefix_lo=200, prefix_hi=900, V=3001), 16),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
+def test_fused_step_replays_in_a_graph(name):
     """Steps captured in a HIP graph on one workspace: every replay, with eager
     work and synchronisation in between, repeats the eager results bit for bit
     (the workspace's keys and counters are left zeroed by each step, and the
     step records no memset)."""
-    w = CASES["tree16_fp8kv"]
+    w, ps = GRAPH_CASES[name]
+    log(f"[step graph] {name} B={w.B} N={w.N} kv={w.kv_dtype} page={ps}")
     cases = [synth.make_inputs(w.replace(seed=s)) for s in (51, 52)]
     devs = [to_device(x) for x in cases]
-    ws = torch.zeros(st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max), dtype=torch.uint8,
+    S = w.S_max
+    if ps:
+        for j, x in enumerate(cases):
+            kp, table = paginate(x["k_cache"], ps, np.random.default_rng(j))
+            vp, _ = paginate(x["v_cache"], ps, np.random.default_rng(j))
+            devs[j]["k_cache"], devs[j]["v_cache"] = kp.cuda(), vp.cuda()
+            devs[j]["table"] = torch.from_numpy(table).cuda()
+            S = table.shape[1] * ps
+    ws = torch.zeros(st.verify_step_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, S), dtype=torch.uint8,
                      device="cuda")
     outs = [st.step_outputs(w.B, w.N, d["q"]) for d in devs]
 
@@ -255,7 +274,7 @@ def test_fused_step_replays_in_a_graph():
         d = devs[j]
         st.verify_step(d["parents"], d["draft_tokens"], d["prefix_lens"], d["q"], d["k_cache"], d["v_cache"],
                        d["logits"], cases[j]["sm_scale"], k_scale=d["k_scale"], v_scale=d["v_scale"], workspace=ws,
-                       outs=outs[j])
+                       outs=outs[j], block_table=d.get("table"))
 
     for j in range(2):
         step(j)
