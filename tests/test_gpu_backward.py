@@ -46,6 +46,9 @@ CASES = {
     "tree64_g2_deep": W[2].replace(B=2, N=64, Hq=4, Hkv=2, max_depth=30, max_children=2, prefix_lo=0,
                                    prefix_hi=200, seed=38),
     "chain6_f32": W[0],
+    # the fp32 path with a branching tree, D = 128, ragged prefixes over several key chunks per wave
+    "tree16_f32_d128_ragged": W[0].replace(B=3, N=16, Hq=8, Hkv=2, D=128, tree="random", max_depth=5, max_children=3,
+                                           prefix_lo=0, prefix_hi=700, seed=36),
 }
 
 

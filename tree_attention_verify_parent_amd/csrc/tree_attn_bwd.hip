@@ -29,7 +29,7 @@
 // MFMA v_mfma_f32_16x16x32_bf16 throughout; operands that contract over
 // keys or rows come from the LDS transpose reads (ds_read_b64_tr_b16).
 //
-// fp32 path: two plain kernels (dq; then dK / dV per key), exact fp32
+// fp32 path: one plain launch of 4-wave workgroups (dq per row, dK / dV per key), exact fp32
 // arithmetic, for small problems.
 #include <cmath>
 
@@ -534,81 +534,93 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
 }
 
 // ---------------------------------------------------------------- fp32
-// dq of one (request, node, head) per wave: lane = key for the scores, then
-// lane = column for the sum over the chunk's keys.
+// One launch, two roles, kBwdF32Waves waves a workgroup; each wave sums its
+// share and the shares are added in LDS.
+//  - Workgroups [0, B*N*Hq): dq of one (request, node, head).  Wave w takes
+//    the key chunks w, w + kBwdF32Waves, ...: lane = key for the scores, then
+//    lane = column for the sum over the chunk's keys, each key's ds read from
+//    its lane.
+//  - The rest: dK and dV of one (request, kv head, key), lane = column.  Wave
+//    w takes the (node, head) rows w, w + kBwdF32Waves, ... that see the key.
+constexpr int kBwdF32Waves = 4;
+
 template <int D>
-__global__ __launch_bounds__(kWave) void tree_attn_bwd_f32_dq_kernel(
+__global__ __launch_bounds__(kBwdF32Waves * kWave) void tree_attn_bwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ prefix_lens, const uint64_t* __restrict__ anc_mask,
-    const float* __restrict__ out, const float* __restrict__ lse, const float* __restrict__ dout, int N,
-    int Hq, int Hkv, int S_max, float sm_scale, float* __restrict__ dq, uint32_t* __restrict__ err_word) {
+    const float* __restrict__ out, const float* __restrict__ lse, const float* __restrict__ dout, int B, int N,
+    int Hq, int Hkv, int S_max, float sm_scale, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, uint32_t* __restrict__ err_word) {
   constexpr int DPL = D / kWave;
-  const int h = blockIdx.x % Hq;
-  const int i = (blockIdx.x / Hq) % N;
-  const int b = blockIdx.x / (Hq * N);
-  const int lane = threadIdx.x;
-  const int kvh = h / (Hq / Hkv);
-  const int P = prefix_lens[b];
-  if (P < 0 || P > S_max - N) {
-    if (lane == 0 && i == 0 && h == 0) flag_error(err_word, SPEC_DERR_PREFIX);
+  constexpr int NWV = kBwdF32Waves;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  __shared__ float s_acc[2][NWV][D];
+  const int n_dq = B * N * Hq;
+  if ((int)blockIdx.x < n_dq) {
+    const int h = blockIdx.x % Hq;
+    const int i = (blockIdx.x / Hq) % N;
+    const int b = blockIdx.x / (Hq * N);
+    const int kvh = h / (Hq / Hkv);
+    const int P = prefix_lens[b];
+    if (P < 0 || P > S_max - N) {
+      if (threadIdx.x == 0 && i == 0 && h == 0) flag_error(err_word, SPEC_DERR_PREFIX);
+      return;
+    }
+    const int L = P + N;
+    const uint64_t anc = anc_mask[(size_t)b * N + i];
+    const size_t row = ((size_t)(b * N + i) * Hq + h) * D;
+    float dm = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) dm = fmaf(dout[row + lane + k * kWave], out[row + lane + k * kWave], dm);
+    dm = wave_sum(dm);
+    const float l = lse[(size_t)(b * N + i) * Hq + h];
+    const float* kb = kc + (size_t)(b * Hkv + kvh) * S_max * D;
+    const float* vb = vc + (size_t)(b * Hkv + kvh) * S_max * D;
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    for (int c0 = wave * kWave; c0 < L; c0 += NWV * kWave) {
+      const int c = c0 + lane;
+      const bool ok = (c < L) && (c < P || ((anc >> (c - P)) & 1ull));
+      float ds = 0.f;
+      if (ok) {
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < D; ++d) {
+          s = fmaf(q[row + d], kb[(size_t)c * D + d], s);
+          dp = fmaf(dout[row + d], vb[(size_t)c * D + d], dp);
+        }
+        const float p = expf(s * sm_scale - l);
+        ds = p * (dp - dm) * sm_scale;
+      }
+      const int cmax = min(kWave, L - c0);
+#pragma unroll
+      for (int jj = 0; jj < kWave; ++jj) {
+        if (jj >= cmax) break;
+        const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ds), jj));
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(x, kb[(size_t)(c0 + jj) * D + lane + k * kWave], acc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) s_acc[0][wave][lane + k * kWave] = acc[k];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      float t = s_acc[0][0][lane + k * kWave];
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) t += s_acc[0][w][lane + k * kWave];
+      dq[row + lane + k * kWave] = t;
+    }
     return;
   }
-  const int L = P + N;
-  const uint64_t anc = anc_mask[(size_t)b * N + i];
-  const size_t row = ((size_t)(b * N + i) * Hq + h) * D;
-  float dm = 0.f;
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) dm = fmaf(dout[row + lane + k * kWave], out[row + lane + k * kWave], dm);
-  dm = wave_sum(dm);
-  const float l = lse[(size_t)(b * N + i) * Hq + h];
-  const float* kb = kc + (size_t)(b * Hkv + kvh) * S_max * D;
-  const float* vb = vc + (size_t)(b * Hkv + kvh) * S_max * D;
-  float acc[DPL];
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-  __shared__ float sds[kWave];
-  for (int c0 = 0; c0 < L; c0 += kWave) {
-    const int c = c0 + lane;
-    const bool ok = (c < L) && (c < P || ((anc >> (c - P)) & 1ull));
-    float ds = 0.f;
-    if (ok) {
-      float s = 0.f, dp = 0.f;
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(q[row + d], kb[(size_t)c * D + d], s);
-        dp = fmaf(dout[row + d], vb[(size_t)c * D + d], dp);
-      }
-      const float p = expf(s * sm_scale - l);
-      ds = p * (dp - dm) * sm_scale;
-    }
-    sds[lane] = ds;
-    __syncthreads();
-    const int cmax = min(kWave, L - c0);
-    for (int jj = 0; jj < cmax; ++jj) {
-      const float x = sds[jj];
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(x, kb[(size_t)(c0 + jj) * D + lane + k * kWave], acc[k]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) dq[row + lane + k * kWave] = acc[k];
-}
-
-// dK and dV of one (request, kv head, key) per wave, lane = column, looping
-// over the rows that can see the key.
-template <int D>
-__global__ __launch_bounds__(kWave) void tree_attn_bwd_f32_dkv_kernel(
-    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
-    const int32_t* __restrict__ prefix_lens, const uint64_t* __restrict__ anc_mask,
-    const float* __restrict__ out, const float* __restrict__ lse, const float* __restrict__ dout, int N,
-    int Hq, int Hkv, int S_max, float sm_scale, float* __restrict__ dk, float* __restrict__ dv) {
-  constexpr int DPL = D / kWave;
-  const int c = blockIdx.x % S_max;
-  const int kvh = (blockIdx.x / S_max) % Hkv;
-  const int b = blockIdx.x / (S_max * Hkv);
-  const int lane = threadIdx.x;
+  const int blk = (int)blockIdx.x - n_dq;
+  const int c = blk % S_max;
+  const int kvh = (blk / S_max) % Hkv;
+  const int b = blk / (S_max * Hkv);
   const int P = prefix_lens[b];
-  if (P < 0 || P > S_max - N) return;              // flagged by the dq kernel
+  if (P < 0 || P > S_max - N) return;              // flagged by the dq role
   const int L = P + N;
   if (c >= L) return;
   const int g = Hq / Hkv;
@@ -621,36 +633,48 @@ __global__ __launch_bounds__(kWave) void tree_attn_bwd_f32_dkv_kernel(
     gk[k] = 0.f;
     gv[k] = 0.f;
   }
-  for (int i = 0; i < N; ++i) {
+  for (int t = wave; t < N * g; t += NWV) {
+    const int i = t / g, hl = t % g;
     if (c >= P && !((anc_mask[(size_t)b * N + i] >> (c - P)) & 1ull)) continue;
-    for (int hl = 0; hl < g; ++hl) {
-      const int h = kvh * g + hl;
-      const size_t row = ((size_t)(b * N + i) * Hq + h) * D;
-      float s = 0.f, dp = 0.f, dm = 0.f;
+    const int h = kvh * g + hl;
+    const size_t row = ((size_t)(b * N + i) * Hq + h) * D;
+    float s = 0.f, dp = 0.f, dm = 0.f;
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) {
-        const int d = lane + k * kWave;
-        s = fmaf(q[row + d], kv[k], s);
-        dp = fmaf(dout[row + d], vv[k], dp);
-        dm = fmaf(dout[row + d], out[row + d], dm);
-      }
-      s = wave_sum(s);
-      dp = wave_sum(dp);
-      dm = wave_sum(dm);
-      const float p = expf(s * sm_scale - lse[(size_t)(b * N + i) * Hq + h]);
-      const float ds = p * (dp - dm) * sm_scale;
+    for (int k = 0; k < DPL; ++k) {
+      const int d = lane + k * kWave;
+      s = fmaf(q[row + d], kv[k], s);
+      dp = fmaf(dout[row + d], vv[k], dp);
+      dm = fmaf(dout[row + d], out[row + d], dm);
+    }
+    s = wave_sum(s);
+    dp = wave_sum(dp);
+    dm = wave_sum(dm);
+    const float p = expf(s * sm_scale - lse[(size_t)(b * N + i) * Hq + h]);
+    const float ds = p * (dp - dm) * sm_scale;
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) {
-        const int d = lane + k * kWave;
-        gv[k] = fmaf(p, dout[row + d], gv[k]);
-        gk[k] = fmaf(ds, q[row + d], gk[k]);
-      }
+    for (int k = 0; k < DPL; ++k) {
+      const int d = lane + k * kWave;
+      gv[k] = fmaf(p, dout[row + d], gv[k]);
+      gk[k] = fmaf(ds, q[row + d], gk[k]);
     }
   }
 #pragma unroll
   for (int k = 0; k < DPL; ++k) {
-    dk[krow + lane + k * kWave] = gk[k];
-    dv[krow + lane + k * kWave] = gv[k];
+    s_acc[0][wave][lane + k * kWave] = gk[k];
+    s_acc[1][wave][lane + k * kWave] = gv[k];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    float tk = s_acc[0][0][lane + k * kWave], tv = s_acc[1][0][lane + k * kWave];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) {
+      tk += s_acc[0][w][lane + k * kWave];
+      tv += s_acc[1][w][lane + k * kWave];
+    }
+    dk[krow + lane + k * kWave] = tk;
+    dv[krow + lane + k * kWave] = tv;
   }
 }
 
@@ -739,19 +763,14 @@ extern "C" spec_status spec_tree_attn_backward(const void* q, const void* k_cach
     if (reinterpret_cast<uintptr_t>(p) & 15u) return SPEC_ERR_ALIGN;
 
   if (dtype == SPEC_F32) {
-    const unsigned g1 = (unsigned)(B * N * Hq);
-    const unsigned g2 = (unsigned)(B * Hkv) * (unsigned)S_max;
+    const long long grid = (long long)B * N * Hq + (long long)B * Hkv * S_max;
+    if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
 #define SPEC_F32_BWD(D_)                                                                                      \
-  hipLaunchKernelGGL(tree_attn_bwd_f32_dq_kernel<D_>, dim3(g1), dim3(kWave), 0, stream,                       \
+  hipLaunchKernelGGL(tree_attn_bwd_f32_kernel<D_>, dim3((unsigned)grid), dim3(kBwdF32Waves * kWave), 0, stream, \
                      static_cast<const float*>(q), static_cast<const float*>(k_cache),                        \
                      static_cast<const float*>(v_cache), prefix_lens, anc_mask, static_cast<const float*>(out), \
-                     lse, static_cast<const float*>(d_out), N, Hq, Hkv, S_max, sm_scale, static_cast<float*>(dq), \
-                     err_word);                                                                               \
-  hipLaunchKernelGGL(tree_attn_bwd_f32_dkv_kernel<D_>, dim3(g2), dim3(kWave), 0, stream,                      \
-                     static_cast<const float*>(q), static_cast<const float*>(k_cache),                        \
-                     static_cast<const float*>(v_cache), prefix_lens, anc_mask, static_cast<const float*>(out), \
-                     lse, static_cast<const float*>(d_out), N, Hq, Hkv, S_max, sm_scale, static_cast<float*>(dk), \
-                     static_cast<float*>(dv))
+                     lse, static_cast<const float*>(d_out), B, N, Hq, Hkv, S_max, sm_scale,                   \
+                     static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), err_word)
     if (D == 64) { SPEC_F32_BWD(64); } else { SPEC_F32_BWD(128); }
 #undef SPEC_F32_BWD
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
