@@ -1,6 +1,6 @@
 // The verify step's "prep" work -- ancestor masks, per-node vocabulary argmax
-// and accept walk -- as a workgroup role that either a kernel of its own or
-// the tail workgroups of the attention kernel take on.
+// and accept walk -- as a workgroup role that the tail workgroups of an
+// attention kernel (the split kernel's, or the fp32 kernel's) take on.
 //
 // The walk needs the argmax and the tree, not the attention's output (under
 // greedy verification the target's token at a node is the argmax of its
