@@ -18,7 +18,7 @@ import torch
 import oracle
 import synth
 import tree_attention_verify_parent_amd as st
-from tests.gpu_util import check_integers, log, oracle_step, paginate, to_device
+from tests.gpu_util import check_attention, check_integers, log, oracle_step, paginate, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -302,3 +302,31 @@ def test_fused_step_replays_in_a_graph(name):
             assert torch.equal(outs[j]["out"].view(torch.int16), eager[j]["out"].view(torch.int16)), (rep, j)
         assert int(ws[:(w.B * w.N * 12 + w.B * 4 + 255) // 256 * 256].count_nonzero()) == 0
         torch.cuda.synchronize()
+
+
+# The largest batch the attention takes (1024 requests): the per-request
+# length table full, 256 mask workgroups in the step; ragged (balanced shares)
+# and uniform (fixed splits, one piece per sequence) prefixes.
+MAX_BATCH = {
+    "b1024_ragged": W[2].replace(B=1024, N=4, Hq=4, Hkv=1, D=64, prefix_lo=0, prefix_hi=120, V=50, seed=61,
+                                 max_depth=3, max_children=2),
+    "b1024_uniform": W[1].replace(B=1024, N=4, Hq=4, Hkv=1, D=64, prefix_lo=60, prefix_hi=60, V=50, seed=62),
+}
+
+
+@pytest.mark.parametrize("name", list(MAX_BATCH))
+def test_step_at_the_largest_batch(name):
+    w = MAX_BATCH[name]
+    log(f"[step max batch] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} P=[{w.prefix_lo},{w.prefix_hi}]")
+    x = synth.make_inputs(w)
+    d = to_device(x)
+    a = _run(d, x, fused=True)
+    b = _run(d, x, fused=False)
+    for k in KEYS:
+        assert np.array_equal(a[k].numpy(), b[k].numpy()), k
+    assert np.array_equal(_bits(a["out"]), _bits(b["out"]))
+    assert int(a["err"][0]) == 0
+    r = oracle_step(x)
+    got = {k: (v.numpy().view(np.uint64) if k == "mask" else v.numpy()) for k, v in a.items() if k in KEYS}
+    check_integers(got, r, name)
+    check_attention(a["out"].float().numpy(), r["out"], w.kv_dtype, name)
