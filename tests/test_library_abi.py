@@ -261,3 +261,21 @@ def test_commit_paged_host_checks(L):
     assert commit(shape=(4, 6, 2, 96)) == SPEC_ERR_SHAPE
     assert commit(shape=(4, 65, 2, 128)) == SPEC_ERR_SHAPE
     assert commit(k=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN
+
+
+def test_binding_constants_match_the_header():
+    """The binding's dtype codes, device error bits and node limit are the
+    header's (read from include/spectree.h, not from the library)."""
+    with open(HEADER) as f:
+        text = f.read()
+    defines = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (SPEC_\w+)\s+(\d+)u?\b", text)}
+    enums = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SPEC_(?:F32|BF16|FP8_E4M3|FP4_E2M1))\s*=\s*(\d+)", text)}
+    assert defines["SPEC_MAX_NODES"] == st.MAX_NODES
+    for name in ("ROOT", "PARENT", "PREFIX", "TOKEN", "PATH", "PAGE"):
+        assert defines["SPEC_DERR_" + name] == getattr(st, "DERR_" + name), name
+    assert (enums["SPEC_F32"], enums["SPEC_BF16"], enums["SPEC_FP8_E4M3"]) == (st.SPEC_F32, st.SPEC_BF16,
+                                                                               st.SPEC_FP8_E4M3)
+    statuses = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SPEC_(?:OK|ERR_\w+))\s*=\s*(\d+)", text)}
+    assert statuses == {"SPEC_OK": SPEC_OK, "SPEC_ERR_NULL": SPEC_ERR_NULL, "SPEC_ERR_SHAPE": SPEC_ERR_SHAPE,
+                        "SPEC_ERR_DTYPE": SPEC_ERR_DTYPE, "SPEC_ERR_WORKSPACE": SPEC_ERR_WORKSPACE,
+                        "SPEC_ERR_HIP": SPEC_ERR_HIP, "SPEC_ERR_ALIGN": SPEC_ERR_ALIGN}
