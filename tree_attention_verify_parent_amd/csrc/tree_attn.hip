@@ -680,8 +680,6 @@ void tree_attn_split_kernel(
 #pragma unroll
       for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qreg[rb][c]));
     }
-    // the loads above have drained, the chunk's fold with them
-    if (held_g >= 0 && !prep_counted) prep_count_in();
     if (own_masks) {
       // the request's ancestor-or-self sets by pointer doubling across the
       // wave (lane = node), then each row takes its node's set; a request
@@ -739,6 +737,10 @@ void tree_attn_split_kernel(
         continue;
       }
     }
+    // A prologue chunk counts in now: its fold has been performed (the wait
+    // above), and the count's round trip is not waited for before the loop
+    // (its first counted wait comes after NSTAGE - 1 tiles of compute).
+    if (held_g >= 0 && !prep_counted) prep_count_in();
 
     f32x4_t oacc[RB][DB];
     float m_run[RB], l_run[RB];
@@ -1030,7 +1032,9 @@ void tree_attn_split_kernel(
     int st = 0;
     for (int i = 0; i < ntiles; ++i) {
       const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
-      switch (ahead) {
+      // tiles 0 .. NSTAGE-2 went out before the loads' wait above and have
+      // landed; the counted waits start with the first tile the loop issued
+      if (i >= NSTAGE - 1) switch (ahead) {
         case 0: wait_vmcnt<0>(); break;
         case 1: wait_vmcnt<1 * PT>(); break;
         case 2: if constexpr (NSTAGE > 3) wait_vmcnt<2 * PT>(); break;
