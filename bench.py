@@ -175,8 +175,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: the verify step is measured per GPU and this build "
-              "has no multi-GPU path (requests would shard across GPUs with no exchange).",
+        print("bench.py runs on one GPU only: the verify step is measured per GPU, and the library has no "
+              "multi-GPU path (requests would shard across GPUs with no exchange).",
               file=sys.stderr)
         sys.exit(2)
 
