@@ -35,6 +35,9 @@ CASES = {
     "tree60_V4099": W[3].replace(B=2, prefix_lo=777, prefix_hi=777, V=4099, seed=23),
     "tree16_fp8kv": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=6000, seed=24),
     "chain6_f32_V1000": W[0],
+    # the fp32 kernel with ~32 key chunks per row, about 8 per wave
+    "tree16_f32_d128_p2000": W[0].replace(B=2, N=16, tree="random", max_depth=5, max_children=3, Hq=8, Hkv=2, D=128,
+                                          prefix_lo=1500, prefix_hi=2000, V=5000, seed=25),
 }
 
 KEYS = ("mask", "depth", "argmax", "accept_len", "path_nodes", "out_tokens", "err")
