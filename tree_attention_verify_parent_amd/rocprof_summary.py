@@ -1,10 +1,13 @@
 """Summarise rocprofv3 result databases into short text tables.
 
-    python -m tree_attention_verify_parent_amd.rocprof_summary stats DIR [--cmd "..."] [--by-grid]
+    python -m tree_attention_verify_parent_amd.rocprof_summary stats DIR [--cmd "..."] [--by-grid] [--by-segment N]
         per-kernel call count and average / min / max duration (kernel trace);
         --by-grid keeps launches of one kernel with different grids apart
         (the verify step's one-launch attention has a larger grid than the
-        attention alone)
+        attention alone); --by-segment N also keeps apart runs of consecutive
+        launches of one (kernel, grid) that other kernels interrupt, numbered
+        #1, #2, ... in launch order, and lists runs of at least N launches
+        (two workloads can launch the same kernel with the same grid)
     python -m tree_attention_verify_parent_amd.rocprof_summary pmc DIR [--cmd "..."]
         per-kernel average of every collected counter (one --pmc pass)
     python -m tree_attention_verify_parent_amd.rocprof_summary traffic \\
@@ -66,16 +69,29 @@ def dbs(d):
     return out
 
 
-def kernel_stats(d, by_grid=False):
-    agg = collections.defaultdict(list)
+def kernel_stats(d, by_grid=False, by_segment=0):
+    launches = []
     for db in dbs(d):
         c = sqlite3.connect(db)
         for name, start, end, gx, wx in c.execute("select name, start, end, grid_x, workgroup_x from kernels"):
             key = short_name(name)
-            if by_grid:
+            if by_grid or by_segment:
                 key += f" [{gx // max(wx, 1)} wg]"
+            launches.append((start, end, key))
+    launches.sort()
+    agg = collections.defaultdict(list)
+    if not by_segment:
+        for start, end, key in launches:
             agg[key].append((end - start) / 1e3)
-    return agg
+        return agg
+    runs = collections.Counter()
+    prev = None
+    for start, end, key in launches:
+        if key != prev:
+            runs[key] += 1
+            prev = key
+        agg[f"#{runs[key]} {key}"].append((end - start) / 1e3)
+    return {k: v for k, v in agg.items() if len(v) >= by_segment}
 
 
 def pmc(d):
@@ -114,15 +130,19 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=float, default=0)
     ap.add_argument("--out", default="")
     ap.add_argument("--by-grid", action="store_true")
+    ap.add_argument("--by-segment", type=int, default=0)
     a = ap.parse_args(argv)
     if a.cmd:
         print(f"command: {a.cmd}")
     if a.mode == "stats":
-        agg = kernel_stats(a.dirs[0], a.by_grid)
+        agg = kernel_stats(a.dirs[0], a.by_grid, a.by_segment)
         tot = sum(sum(v) for v in agg.values())
-        print(f"{'kernel':58s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
-        for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-            print(f"{k[:58]:58s} {len(v):7d} {sum(v)/len(v):9.3f} {min(v):9.3f} {max(v):9.3f} {100*sum(v)/tot:6.1f}")
+        w = 72 if a.by_segment else 58
+        print(f"{'kernel':{w}s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
+        # segments in launch order (of their first launch), kernels by total time
+        items = list(agg.items()) if a.by_segment else sorted(agg.items(), key=lambda kv: -sum(kv[1]))
+        for k, v in items:
+            print(f"{k[:w]:{w}s} {len(v):7d} {sum(v)/len(v):9.3f} {min(v):9.3f} {max(v):9.3f} {100*sum(v)/tot:6.1f}")
     elif a.mode == "pmc":
         agg = pmc(a.dirs[0])
         for k, ctrs in sorted(agg.items()):
