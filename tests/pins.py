@@ -354,6 +354,61 @@ def check_attention_ignores_rows_past_tree(tree_attention, seed: int = 7):
     np.testing.assert_array_equal(out, out2)
 
 
+def _pin_formats(q, k, v, fmt, rng):
+    """The rand_case arrays in the storage format fmt, as the oracle takes them,
+    and their exact float64 values decoded by torch's own conversions."""
+    if fmt == "f32":
+        return q, k, v, None, None, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    tq = torch.from_numpy(q).to(torch.bfloat16)
+    qb = tq.view(torch.int16).numpy().view(np.uint16)
+    if fmt == "bf16":
+        tk, tv = torch.from_numpy(k).to(torch.bfloat16), torch.from_numpy(v).to(torch.bfloat16)
+        return (qb, tk.view(torch.int16).numpy().view(np.uint16), tv.view(torch.int16).numpy().view(np.uint16),
+                None, None, tq.double().numpy(), tk.double().numpy(), tv.double().numpy())
+    # e4m3 caches with one float32 scale per KV head
+    ks = (np.abs(k).max(axis=(0, 2, 3)) / 448.0).astype(np.float32)
+    vs = (np.abs(v).max(axis=(0, 2, 3)) / 448.0).astype(np.float32)
+    tk = (torch.from_numpy(k) / torch.from_numpy(ks)[None, :, None, None]).to(torch.float8_e4m3fn)
+    tv = (torch.from_numpy(v) / torch.from_numpy(vs)[None, :, None, None]).to(torch.float8_e4m3fn)
+    kf = tk.double().numpy() * ks.astype(np.float64)[None, :, None, None]
+    vf = tv.double().numpy() * vs.astype(np.float64)[None, :, None, None]
+    return (qb, tk.view(torch.uint8).numpy(), tv.view(torch.uint8).numpy(), ks, vs, tq.double().numpy(), kf, vf)
+
+
+def check_attention_bh(tree_attention_bh, tree_attention, seed: int = 18):
+    """The one-(request, head) oracle call: bit for bit the batched call's
+    slice for every pair, and float64 SDPA over the request's kv head (head h
+    reads kv head h // g) with a dense mask from a parent chase written here;
+    fp32, bf16 and e4m3 caches, ragged prefixes, GQA groups of 1 to 6."""
+    rng = np.random.default_rng(seed)
+    for (B, N, Hq, Hkv, D, P, fmt) in [(3, 7, 6, 2, 8, [5, 0, 12], "f32"), (2, 5, 8, 2, 16, [9, 3], "bf16"),
+                                       (2, 6, 4, 4, 8, [2, 7], "e4m3"), (1, 4, 6, 1, 4, 3, "f32"),
+                                       (2, 9, 6, 3, 8, [11, 1], "e4m3")]:
+        parents, prefix, q, k, v = rand_case(rng, B, N, Hq, Hkv, D, P)
+        qo, ko, vo, ks, vs, qf, kf, vf = _pin_formats(q, k, v, fmt, rng)
+        qfmt = "f32" if fmt == "f32" else "bf16"
+        sc = 0.4
+        out, lse = tree_attention(qo, ko, vo, prefix, parents, sc, q_fmt=qfmt, kv_fmt=fmt, k_scale=ks, v_scale=vs)
+        g = Hq // Hkv
+        for b in range(B):
+            Pb = int(prefix[b])
+            L = Pb + N
+            mask = np.zeros((N, L), dtype=bool)
+            mask[:, :Pb] = True
+            for i in range(N):
+                j = i
+                while j != -1:
+                    mask[i, Pb + j] = True
+                    j = int(parents[b][j])
+            for h in range(Hq):
+                ob, lb = tree_attention_bh(qo, ko, vo, prefix, parents, sc, b, h, q_fmt=qfmt, kv_fmt=fmt,
+                                           k_scale=ks, v_scale=vs)
+                np.testing.assert_array_equal(ob, out[b, :, h])
+                np.testing.assert_array_equal(lb, lse[b, :, h])
+                ref = sdpa_f64(qf[b, :, h][None], kf[b, h // g, :L][None], vf[b, h // g, :L][None], mask, sc)[0]
+                np.testing.assert_allclose(ob, ref, rtol=1e-11, atol=1e-12)
+
+
 # ------------------------------------------------------------------ commit
 
 def _row_tagged_cache(B, Hkv, S, width=3):

@@ -1,7 +1,17 @@
-"""GPU parity of the fp8-arithmetic attention over e4m3 caches
+"""GPU checks of the fp8-arithmetic attention over e4m3 caches
 (spec_tree_attn_verify_f8) and e2m1 (FP4) caches (spec_tree_attn_verify_f4).
 
-Reference: the oracle's exact attention of the e4m3-quantized query
+These two entry points lie OUTSIDE the verify step's parity contract.
+Against the exact attention of the unquantized query, every element stays
+within the fp8-cache bound (6e-2 + 1e-2 |r|, asserted in
+test_f8_attention_against_exact_attention), but the relative L2 distance is
+about 3% -- above the contract's 1e-2 guard -- because q and p are rounded to
+e4m3 (3 mantissa bits) inside the kernel.  That test asserts the variant's
+own derived L2 bound of 5e-2 instead and logs the distance.
+
+The labelled quantized-q test (test_f8_attention_quantized_q_reference)
+checks the kernel's arithmetic itself.  Its reference: the oracle's exact
+attention of the e4m3-quantized query
 (``oracle.quantize_rows_e4m3``: the same per-row recipe the kernel follows,
 so the kernel and the reference see the same q codes) over the same e4m3
 cache.  What remains is the kernel's rounding of every probability to
@@ -28,6 +38,7 @@ pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
 REL_L2 = 5e-2
+FP8_CACHE_TOL = (6e-2, 1e-2)         # the fp8-cache elementwise bound, |g - r| <= 6e-2 + 1e-2 |r|
 
 CASES = {
     "tree16_g8_fp8": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=8, seed=61),
@@ -59,7 +70,17 @@ def max_visible_v(vdec, prefix, parents, N):
     return out
 
 
+_RUNS = {}
+
+
 def run_case(w):
+    if w in _RUNS:
+        return _RUNS[w]
+    _RUNS[w] = _run_case(w)
+    return _RUNS[w]
+
+
+def _run_case(w):
     x = synth.make_inputs(w, with_logits=False)
     d = to_device(x)
     anc, _, err = st.tree_mask_build(d["parents"])
@@ -84,10 +105,32 @@ def run_case(w):
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_f8_attention_matches_oracle(name, fmt):
+def test_f8_attention_against_exact_attention(name, fmt):
+    """Exact attention of the unquantized bf16 query over the same cache:
+    the fp8-cache elementwise bound holds; the relative L2 distance is
+    within the variant's 5e-2, not the contract's 1e-2 (outside the contract)."""
     w = CASES[name].replace(kv_dtype=fmt)
-    log(f"[f8] {name} cache={fmt} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P=[{w.prefix_lo},{w.prefix_hi}] "
+    log(f"[f8 exact] {name} cache={fmt} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P=[{w.prefix_lo},{w.prefix_hi}] "
         f"seed={w.seed}")
+    out, lse, err, ro, rl, ex, vmax = run_case(w)
+    assert err == 0
+    atol, rtol = FP8_CACHE_TOL
+    worst = float((np.abs(out - ex) / (atol + rtol * np.abs(ex))).max())
+    rel_exact = float(np.linalg.norm(out - ex) / np.linalg.norm(ex))
+    log(f"  vs exact attention: max_abs={np.abs(out - ex).max():.3e} worst/bound={worst:.3f} "
+        f"rel_l2={rel_exact:.3e} (contract guard 1e-2 not met by design; variant bound {REL_L2})")
+    assert worst <= 1.0, worst
+    assert rel_exact <= REL_L2, rel_exact
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_f8_attention_quantized_q_reference(name, fmt):
+    """The kernel's arithmetic against the oracle's attention of the same
+    e4m3-quantized query rows (only the rounding of p remains)."""
+    w = CASES[name].replace(kv_dtype=fmt)
+    log(f"[f8 quantized q] {name} cache={fmt} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} "
+        f"P=[{w.prefix_lo},{w.prefix_hi}] seed={w.seed}")
     out, lse, err, ro, rl, ex, vmax = run_case(w)
     assert err == 0
     assert np.isfinite(out).all()

@@ -31,6 +31,10 @@ def test_closed_form_two_and_three_nodes():
     pins.check_attention_closed_form(oracle.tree_attention)
 
 
+def test_one_request_one_head_call():
+    pins.check_attention_bh(oracle.tree_attention_bh, oracle.tree_attention)
+
+
 def test_rows_past_the_tree_are_ignored():
     pins.check_attention_ignores_rows_past_tree(oracle.tree_attention)
 

@@ -80,6 +80,13 @@ MUTANTS = {
                                   lambda o: pins.check_attention_chain_is_causal(o.attention.tree_attention)),
     "attn_kv_head_mod": ([("attention", "for h in range(kvh * g, (kvh + 1) * g):", "for h in range(kvh, Hq, Hkv):")],
                          lambda o: pins.check_attention_chain_is_causal(o.attention.tree_attention)),
+    "attn_bh_kv_head_mod": ([("attention", "    kvh = h // g\n", "    kvh = h % k_cache.shape[1]\n")],
+                            lambda o: pins.check_attention_bh(o.attention.tree_attention_bh,
+                                                              o.attention.tree_attention)),
+    "attn_bh_query_of_kv_head": ([("attention", "Q = _as_f64(np.asarray(q[b, :, h, :]), q_fmt)            # [N][D]",
+                                   "Q = _as_f64(np.asarray(q[b, :, kvh, :]), q_fmt)            # [N][D]")],
+                                 lambda o: pins.check_attention_bh(o.attention.tree_attention_bh,
+                                                                   o.attention.tree_attention)),
     "attn_no_scale": ([("attention", "s = float(sm_scale) * (Q @ Kf.T)                         # [N][L]", "s = Q @ Kf.T")],
                       lambda o: pins.check_attention_chain_is_causal(o.attention.tree_attention)),
     "attn_k_for_v": ([("attention", "out = w @ Vf", "out = w @ Kf")],

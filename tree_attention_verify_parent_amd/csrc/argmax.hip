@@ -41,6 +41,7 @@ extern "C" spec_status spec_vocab_argmax(const float* logits, int64_t rows, int6
   const bool vec = ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0) && (row_stride % 4 == 0);
   // Few rows: wide workgroups so a single row still has enough loads in
   // flight; many rows: 256 threads and several workgroups per CU.
+  hip_clear_error();
   if (rows < 256) {
     if (vec)
       hipLaunchKernelGGL((vocab_argmax_kernel<1024, 8, true>), dim3((unsigned)rows), dim3(1024), 0,
@@ -56,5 +57,5 @@ extern "C" spec_status spec_vocab_argmax(const float* logits, int64_t rows, int6
       hipLaunchKernelGGL((vocab_argmax_kernel<256, 8, false>), dim3((unsigned)rows), dim3(256), 0,
                          stream, logits, V, row_stride, out_idx);
   }
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  return launch_status();
 }

@@ -144,6 +144,7 @@ static spec_status commit_launch(void* k_cache, void* v_cache, spec_dtype kv_dty
   if ((long long)B * Hkv >= (1ll << 31)) return SPEC_ERR_SHAPE;
   const int row_bytes = D * eb;
   const size_t lds = (size_t)2 * (N - 1) * row_bytes;          // at most N - 1 accepted rows
+  hip_clear_error();
   if (pg.table)
     hipLaunchKernelGGL(commit_accepted_kernel<true>, dim3((unsigned)(B * Hkv)), dim3(kCommitThreads), lds, stream,
                        static_cast<unsigned char*>(k_cache), static_cast<unsigned char*>(v_cache), row_bytes,
@@ -154,7 +155,7 @@ static spec_status commit_launch(void* k_cache, void* v_cache, spec_dtype kv_dty
                        static_cast<unsigned char*>(k_cache), static_cast<unsigned char*>(v_cache), row_bytes,
                        prefix_lens, accept_len, path_nodes, N, Hkv, S_max, new_prefix_lens, node_labels, err_word,
                        pg);
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  return launch_status();
 }
 
 extern "C" spec_status spec_commit_accepted(void* k_cache, void* v_cache, spec_dtype kv_dtype,

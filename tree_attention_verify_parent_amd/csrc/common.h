@@ -32,6 +32,12 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// HIP keeps a thread's last error until it is read, so a failure of some
+// unrelated earlier call would come back from the next check.  Each entry
+// point clears it right before its launches and then reads only theirs.
+inline void hip_clear_error() { (void)hipGetLastError(); }
+inline spec_status launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
+
 __device__ __forceinline__ void flag_error(uint32_t* err_word, uint32_t bits) {
   if (err_word) atomicOr(err_word, bits);
 }

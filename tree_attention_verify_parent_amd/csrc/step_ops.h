@@ -106,9 +106,6 @@ inline long long plan_prep(PrepArgs* pa, int B, int N, int nt, long long host_wg
     return pa->n_mask_wg;
   }
   long long target = kPrepTargetWgs;
-#ifdef SPEC_PREP_HOOK
-  SPEC_PREP_HOOK(target);
-#endif
   const long long pass = (long long)nt * kPrepUnroll * 4;
   const long long max_chunks = (pa->V + pass - 1) / pass;
   long long want = (target + rows - 1) / rows;

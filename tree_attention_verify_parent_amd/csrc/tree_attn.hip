@@ -1395,9 +1395,6 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   const int lds_bf16 = p->nstage * 2 * kTile * D * 2 + kTableBytes;
   const long long per_cu = std::max(1, std::min(2, (160 * 1024) / lds_bf16));
   long long target_wgs = 256 * per_cu;
-#ifdef SPEC_PLAN_HOOK
-  SPEC_PLAN_HOOK(p, M, target_wgs);
-#endif
   p->mt_rows = p->rb * p->wm * 16;
   p->n_mt = (M + p->mt_rows - 1) / p->mt_rows;
   p->M_pad = p->n_mt * p->mt_rows;
@@ -1469,14 +1466,10 @@ constexpr bool split_fits() {
 }
 
 // (RB, WM, WT, NSTAGE) instantiations the planner may pick.
-#ifndef SPEC_SPLIT_PLANS
 #define SPEC_SPLIT_PLANS(X) X(1, 2, 2, 3) X(2, 2, 1, 2) X(2, 4, 1, 2)
-#endif
 // The fp8-arithmetic path: every wave covers whole tiles (WT = 1); for M <= 32
 // the plan keeps the 32-row tile of the bf16 plan, so the workspace is the same.
-#ifndef SPEC_F8_PLANS
 #define SPEC_F8_PLANS(X) X(1, 2, 1, 3) X(2, 2, 1, 2) X(2, 4, 1, 2)
-#endif
 
 template <int D, int KVF, bool PAGED>
 static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, const void* v,
@@ -1547,6 +1540,7 @@ static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const v
   }
 
   const bool paged = pg.table != nullptr;
+  hip_clear_error();
 #define SPEC_DISPATCH(D_, KVF_)                                                                           \
   (paged ? dispatch_shape<D_, KVF_, true>(pl, q, k, v, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, \
                                           S_max, sm_scale, out, lse, po, pml, cnt, err_word, pg, prep, stream)     \
@@ -1565,7 +1559,7 @@ static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const v
                                                                   lse, po, pml, cnt, err_word, pg, prep, stream);
 #undef SPEC_DISPATCH
   if (!launched) return SPEC_ERR_SHAPE;
-  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  if (launch_status() != SPEC_OK) return SPEC_ERR_HIP;
 
   return SPEC_OK;
 }
@@ -1613,6 +1607,7 @@ static spec_status launch_f32(const void* q, const void* k_cache, const void* v_
     grid += plan_prep(&pa, B, N, kF32Waves * kWave, 0, 0);
   }
   if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
+  hip_clear_error();
   const float* qf = static_cast<const float*>(q);
   const float* kf = static_cast<const float*>(k_cache);
   const float* vf = static_cast<const float*>(v_cache);
@@ -1629,7 +1624,7 @@ static spec_status launch_f32(const void* q, const void* k_cache, const void* v_
     else SPEC_F32_LAUNCH(128, false);
   }
 #undef SPEC_F32_LAUNCH
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  return launch_status();
 }
 
 namespace spectree {

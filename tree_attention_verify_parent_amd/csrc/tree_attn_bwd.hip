@@ -700,16 +700,10 @@ static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPl
   if (M > 128) return false;
   p->mp = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
   p->nstage = (D == 128 && p->mp == 128) ? 2 : 3;
-#ifdef SPEC_BWD_NSTAGE_HOOK
-  SPEC_BWD_NSTAGE_HOOK(p->nstage);
-#endif
   const long long seqs = (long long)B * Hkv;
   const int n_tiles = (S_max + kTile - 1) / kTile;
   const long long want = std::max<long long>((kCUs + seqs - 1) / seqs, (n_tiles + kMaxRun - 1) / kMaxRun);
   int split_len = (int)((n_tiles + want - 1) / want);
-#ifdef SPEC_BWD_SPLIT_HOOK
-  SPEC_BWD_SPLIT_HOOK(split_len, n_tiles);
-#endif
   p->split_len = split_len;
   p->n_splits = (n_tiles + split_len - 1) / split_len;
   if (seqs * p->n_splits >= (1ll << 31)) return false;
@@ -762,6 +756,7 @@ extern "C" spec_status spec_tree_attn_backward(const void* q, const void* k_cach
   for (const void* p : {q, k_cache, v_cache, out, d_out, (const void*)dq, (const void*)dk, (const void*)dv})
     if (reinterpret_cast<uintptr_t>(p) & 15u) return SPEC_ERR_ALIGN;
 
+  hip_clear_error();
   if (dtype == SPEC_F32) {
     const long long grid = (long long)B * N * Hq + (long long)B * Hkv * S_max;
     if (grid >= (1ll << 31)) return SPEC_ERR_SHAPE;
@@ -773,7 +768,7 @@ extern "C" spec_status spec_tree_attn_backward(const void* q, const void* k_cach
                      static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), err_word)
     if (D == 64) { SPEC_F32_BWD(64); } else { SPEC_F32_BWD(128); }
 #undef SPEC_F32_BWD
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+    return launch_status();
   }
 
   float* part = nullptr;
@@ -788,14 +783,9 @@ extern "C" spec_status spec_tree_attn_backward(const void* q, const void* k_cach
   if (D == D_ && pl.mp == MP_ && pl.nstage == NS_) {                                                           \
     launch_bwd<D_, MP_, NS_>(pl, q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, B, N, Hq, Hkv,   \
                              S_max, sm_scale, dq, dk, dv, part, cnt, err_word, stream);                        \
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;                                            \
+    return launch_status();                                            \
   }
   SPEC_BWD(128, 32, 3)
-#ifdef SPEC_BWD_NSTAGE_HOOK
-  SPEC_BWD(128, 32, 4)
-  SPEC_BWD(128, 64, 2)
-  SPEC_BWD(64, 32, 4)
-#endif
   SPEC_BWD(128, 64, 3)
   SPEC_BWD(128, 128, 2)
   SPEC_BWD(64, 32, 3)

@@ -45,9 +45,10 @@ extern "C" spec_status spec_tree_mask_build(const int32_t* parents, int B, int N
                                             uint32_t* err_word, hipStream_t stream) {
   if (!parents || !anc_mask) return SPEC_ERR_NULL;
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES) return SPEC_ERR_SHAPE;
+  hip_clear_error();
   hipLaunchKernelGGL(tree_mask_build_kernel, dim3(B), dim3(kWave), 0, stream, parents, N,
                      anc_mask, depth, err_word);
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  return launch_status();
 }
 
 extern "C" spec_status spec_accept_walk(const int32_t* parents, const uint64_t* anc_mask,
@@ -60,10 +61,11 @@ extern "C" spec_status spec_accept_walk(const int32_t* parents, const uint64_t* 
       !out_tokens)
     return SPEC_ERR_NULL;
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1) return SPEC_ERR_SHAPE;
+  hip_clear_error();
   hipLaunchKernelGGL(accept_walk_kernel, dim3(B), dim3(kWave), 0, stream, parents, anc_mask,
                      draft_tokens, target_argmax, N, V, accept_len, path_nodes, out_tokens,
                      err_word);
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  return launch_status();
 }
 
 extern "C" const char* spec_status_string(spec_status status) {
