@@ -305,10 +305,11 @@ spec_status spec_commit_accepted_paged(void* k_pages, void* v_pages, spec_dtype 
  *     sums        fp32; the softmax denominator sums the unquantized p
  * OUTSIDE THE PARITY CONTRACT of spec_tree_attn_verify: the e4m3 roundings
  * of q and p (3 mantissa bits) put the result about 3% (relative L2) from
- * the exact attention, above the contract's 1e-2 relative-L2 guard.  Every
- * element stays within the fp8-cache bound 6e-2 + 1e-2 |exact|, and the
- * relative L2 distance within 5e-2.  Use spec_tree_attn_verify where the
- * contract must hold.
+ * the exact attention, above the contract's 1e-2 relative-L2 guard (it
+ * stays within 5e-2).  Each element is within 2^-3 of the largest |V| its
+ * row sees; with at least 64 prefix tokens per request also within the
+ * fp8-cache bound 6e-2 + 1e-2 |exact|, which prefixes of a few tokens can
+ * exceed.  Use spec_tree_attn_verify where the contract must hold.
  *
  *   Arguments as spec_tree_attn_verify with q_dtype = SPEC_BF16 and
  *   kv_dtype = SPEC_FP8_E4M3 (k_scale, v_scale required), D = 128 only; the
@@ -331,8 +332,10 @@ spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cache, const v
  * byte j), with one fp32 scale per KV head for K and one for V (the same
  * scheme as the e4m3 cache): K = code * k_scale[kvh].  The codes are the A
  * operands of e2m1 x e4m3 matrix-core products; q and p are quantized to
- * e4m3 exactly as in spec_tree_attn_verify_f8.  The cache moves half the
- * bytes of an e4m3 one.
+ * e4m3 exactly as in spec_tree_attn_verify_f8, and like it this variant
+ * lies outside the parity contract (about 3% relative L2 from the exact
+ * attention of the same cache).  The cache moves half the bytes of an e4m3
+ * one.
  *
  *   k_cache,
  *   v_cache    [B][Hkv][S_max][D/2] bytes, 16-B aligned

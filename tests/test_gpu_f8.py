@@ -1,13 +1,16 @@
 """GPU checks of the fp8-arithmetic attention over e4m3 caches
 (spec_tree_attn_verify_f8) and e2m1 (FP4) caches (spec_tree_attn_verify_f4).
 
-These two entry points lie OUTSIDE the verify step's parity contract.
-Against the exact attention of the unquantized query, every element stays
-within the fp8-cache bound (6e-2 + 1e-2 |r|, asserted in
-test_f8_attention_against_exact_attention), but the relative L2 distance is
-about 3% -- above the contract's 1e-2 guard -- because q and p are rounded to
-e4m3 (3 mantissa bits) inside the kernel.  That test asserts the variant's
-own derived L2 bound of 5e-2 instead and logs the distance.
+These two entry points lie OUTSIDE the verify step's parity contract: q and
+p are rounded to e4m3 (3 mantissa bits) inside the kernel.  Against the
+exact attention of the unquantized query (test_f8_attention_against_exact_attention):
+  * the relative L2 distance is about 3%, above the contract's 1e-2 guard;
+    the variant's own bound of 5e-2 is asserted and the distance logged;
+  * every element is within 2^-3 of the largest |V| the row sees (twice the
+    p-rounding bound below, covering q's rounding too), plus 2^-8 |r| + 1e-3;
+  * the fp8-cache elementwise bound 6e-2 + 1e-2 |r| is asserted where every
+    request has at least 64 prefix tokens.  With fewer, a node's output mixes
+    a handful of rows and a weight's 2^-4 rounding can move it past 6e-2.
 
 The labelled quantized-q test (test_f8_attention_quantized_q_reference)
 checks the kernel's arithmetic itself.  Its reference: the oracle's exact
@@ -39,6 +42,7 @@ pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
 REL_L2 = 5e-2
 FP8_CACHE_TOL = (6e-2, 1e-2)         # the fp8-cache elementwise bound, |g - r| <= 6e-2 + 1e-2 |r|
+LONG_PREFIX = 64                     # every request at least this long: that bound is asserted too
 
 CASES = {
     "tree16_g8_fp8": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=8, seed=61),
@@ -100,27 +104,33 @@ def _run_case(w):
     dec = oracle.decode_e2m1_packed(vc, 1.0) if fmt == "e2m1" else oracle.decode_e4m3(vc, 1.0)
     vdec = dec * x["v_scale"][None, :, None, None]
     vmax = np.repeat(max_visible_v(vdec, x["prefix_lens"], x["parents"], w.N), w.Hq // w.Hkv, axis=2)
-    return out.float().cpu().numpy(), lse.cpu().numpy(), int(err[0]), ro, rl, ex, vmax
+    return out.float().cpu().numpy(), lse.cpu().numpy(), int(err[0]), ro, rl, ex, vmax, int(x["prefix_lens"].min())
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_f8_attention_against_exact_attention(name, fmt):
-    """Exact attention of the unquantized bf16 query over the same cache:
-    the fp8-cache elementwise bound holds; the relative L2 distance is
-    within the variant's 5e-2, not the contract's 1e-2 (outside the contract)."""
+    """Exact attention of the unquantized bf16 query over the same cache: the
+    derived elementwise bound and the variant's 5e-2 relative L2 bound (not
+    the contract's 1e-2: outside the contract); the fp8-cache elementwise
+    bound where every prefix has at least LONG_PREFIX tokens."""
     w = CASES[name].replace(kv_dtype=fmt)
     log(f"[f8 exact] {name} cache={fmt} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} P=[{w.prefix_lo},{w.prefix_hi}] "
         f"seed={w.seed}")
-    out, lse, err, ro, rl, ex, vmax = run_case(w)
+    out, lse, err, ro, rl, ex, vmax, pmin = run_case(w)
     assert err == 0
+    e = np.abs(out - ex)
     atol, rtol = FP8_CACHE_TOL
-    worst = float((np.abs(out - ex) / (atol + rtol * np.abs(ex))).max())
+    worst_cache = float((e / (atol + rtol * np.abs(ex))).max())
+    worst = float((e / (2.0 ** -3 * vmax + 2.0 ** -8 * np.abs(ex) + 1e-3)).max())
     rel_exact = float(np.linalg.norm(out - ex) / np.linalg.norm(ex))
-    log(f"  vs exact attention: max_abs={np.abs(out - ex).max():.3e} worst/bound={worst:.3f} "
-        f"rel_l2={rel_exact:.3e} (contract guard 1e-2 not met by design; variant bound {REL_L2})")
+    log(f"  vs exact attention: max_abs={e.max():.3e} worst/derived bound={worst:.3f} "
+        f"worst/fp8-cache bound={worst_cache:.3f} (shortest prefix {pmin}) rel_l2={rel_exact:.3e} "
+        f"(contract guard 1e-2 not met by design; variant bound {REL_L2})")
     assert worst <= 1.0, worst
     assert rel_exact <= REL_L2, rel_exact
+    if pmin >= LONG_PREFIX:
+        assert worst_cache <= 1.0, worst_cache
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
@@ -131,7 +141,7 @@ def test_f8_attention_quantized_q_reference(name, fmt):
     w = CASES[name].replace(kv_dtype=fmt)
     log(f"[f8 quantized q] {name} cache={fmt} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} "
         f"P=[{w.prefix_lo},{w.prefix_hi}] seed={w.seed}")
-    out, lse, err, ro, rl, ex, vmax = run_case(w)
+    out, lse, err, ro, rl, ex, vmax, _ = run_case(w)
     assert err == 0
     assert np.isfinite(out).all()
     e = np.abs(out - ro)
