@@ -57,7 +57,8 @@ typedef enum {
   SPEC_ERR_DTYPE = 3,     /* unsupported dtype or dtype pair                    */
   SPEC_ERR_WORKSPACE = 4, /* workspace missing or smaller than required         */
   SPEC_ERR_HIP = 5,       /* a kernel launch failed                             */
-  SPEC_ERR_ALIGN = 6      /* a pointer is not 16-byte aligned where required    */
+  SPEC_ERR_ALIGN = 6,     /* a pointer is not 16-byte aligned where required    */
+  SPEC_ERR_SCRATCH = 7    /* the sizes need more than the static scratch holds  */
 } spec_status;
 
 typedef enum {
@@ -482,6 +483,40 @@ spec_status spec_verify_step_paged(const int32_t* parents, const int32_t* draft_
                                    int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
                                    int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                                    uint32_t* err_word, hipStream_t stream);
+
+/*
+ * spec_verify_step_static -- spec_verify_step with the library's own scratch
+ * instead of a workspace argument.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call):
+ * the step's workspace is a file-scope device array of
+ * SPEC_STATIC_SCRATCH_BYTES (72 MiB, enough for 16 requests of 60-node trees
+ * over 32768-token prefixes with 64 query heads over 4 KV heads), of which
+ * every GPU the library runs on holds its own copy until the process ends.
+ *
+ *   Arguments as spec_verify_step, without workspace / workspace_bytes.
+ *   Returns SPEC_ERR_SCRATCH, before anything is enqueued, when
+ *   spec_verify_step_workspace_bytes(B, N, Hq, Hkv, D, S_max) exceeds
+ *   SPEC_STATIC_SCRATCH_BYTES; every other check as spec_verify_step's, also
+ *   before anything is enqueued.
+ * The first call on a device looks up the array's address and, unless
+ * `stream` is capturing, enqueues a zero fill of it on `stream` (a first
+ * call under capture relies on the array's zero initialisation at load).
+ * Every step leaves the array's counters and argmax keys at zero again.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must not be issued.
+ */
+#define SPEC_STATIC_SCRATCH_BYTES (72u << 20)
+spec_status spec_verify_step_static(const int32_t* parents, const int32_t* draft_tokens, const int32_t* prefix_lens,
+                                    const void* q, spec_dtype q_dtype, const void* k_cache, const void* v_cache,
+                                    spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                    const float* logits, int64_t V, int64_t logits_row_stride,
+                                    int B, int N, int Hq, int Hkv, int D, int S_max, float sm_scale,
+                                    uint64_t* anc_mask, int32_t* depth, void* out, float* lse,
+                                    int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
+                                    int32_t* out_tokens, uint32_t* err_word, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* spec_status_string(spec_status status);

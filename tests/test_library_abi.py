@@ -11,7 +11,8 @@ import tree_attention_verify_parent_amd as st
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spectree.h")
 
-SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_DTYPE, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP, SPEC_ERR_ALIGN = range(7)
+(SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_DTYPE, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP, SPEC_ERR_ALIGN,
+ SPEC_ERR_SCRATCH) = range(8)
 FAKE = ctypes.c_void_p(0x1000)        # never dereferenced: every call below fails host checks first
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert L.spec_status_string(s).decode().startswith("SPEC_")
     assert b"unknown" in L.spec_status_string(99)
 
@@ -216,6 +217,33 @@ def test_verify_step_host_checks(L):
     assert step(ws=ctypes.c_void_p(0x1008)) == SPEC_ERR_ALIGN
 
 
+def test_verify_step_static_host_checks(L):
+    """Refusals come before the scratch's set-up (which needs a GPU): bad
+    arguments as spec_verify_step's, sizes past the static scratch as
+    SPEC_ERR_SCRATCH."""
+    def step(parents=FAKE, logits=FAKE, out=FAKE, V=32000, stride=32000, qd=1, kvd=1,
+             shape=(8, 6, 32, 8, 128, 2054), scale=0.088, q=FAKE):
+        return L.spec_verify_step_static(parents, FAKE, FAKE, q, qd, FAKE, FAKE, kvd, None, None, logits, V, stride,
+                                         *shape, scale, FAKE, None, out, None, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert step(parents=None) == SPEC_ERR_NULL
+    assert step(logits=None) == SPEC_ERR_NULL
+    assert step(out=None) == SPEC_ERR_NULL
+    assert step(stride=31999) == SPEC_ERR_SHAPE
+    assert step(shape=(8, 65, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE
+    assert step(qd=0) == SPEC_ERR_DTYPE
+    assert step(kvd=2) == SPEC_ERR_NULL
+    assert step(scale=0.0) == SPEC_ERR_SHAPE
+    assert step(q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
+    limit = 72 << 20
+    big = (64, 60, 64, 4, 128, 32828)                       # a workspace of about 260 MB
+    assert L.spec_verify_step_workspace_bytes(*big) > limit
+    assert step(shape=big, V=1000, stride=1000) == SPEC_ERR_SCRATCH
+    ok = (16, 60, 64, 4, 128, 32828)
+    assert 0 < L.spec_verify_step_workspace_bytes(*ok) <= limit
+    with open(HEADER) as f:
+        assert "#define SPEC_STATIC_SCRATCH_BYTES (72u << 20)" in f.read()
+
+
 def test_verify_step_paged_host_checks(L):
     # 8 requests of 6 nodes over 16-token pages, 129 pages each (S_max 2064)
     need = L.spec_verify_step_workspace_bytes(8, 6, 32, 8, 128, 129 * 16)
@@ -278,4 +306,5 @@ def test_binding_constants_match_the_header():
     statuses = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SPEC_(?:OK|ERR_\w+))\s*=\s*(\d+)", text)}
     assert statuses == {"SPEC_OK": SPEC_OK, "SPEC_ERR_NULL": SPEC_ERR_NULL, "SPEC_ERR_SHAPE": SPEC_ERR_SHAPE,
                         "SPEC_ERR_DTYPE": SPEC_ERR_DTYPE, "SPEC_ERR_WORKSPACE": SPEC_ERR_WORKSPACE,
-                        "SPEC_ERR_HIP": SPEC_ERR_HIP, "SPEC_ERR_ALIGN": SPEC_ERR_ALIGN}
+                        "SPEC_ERR_HIP": SPEC_ERR_HIP, "SPEC_ERR_ALIGN": SPEC_ERR_ALIGN,
+                        "SPEC_ERR_SCRATCH": SPEC_ERR_SCRATCH}

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify", "tree_attn_verify_paged",
     "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "attn_backward_workspace_bytes",
-    "tree_attn_backward", "tree_attn_verify_f8", "tree_attn_verify_f4", "DERR_ROOT", "DERR_PARENT",
+    "tree_attn_backward", "tree_attn_verify_f8", "tree_attn_verify_f4", "verify_step_static", "DERR_ROOT",
+    "DERR_PARENT",
     "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "DERR_PAGE", "library_path", "verify_step_workspace_bytes", "step_outputs",
 ]
 
@@ -34,7 +35,7 @@ EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_
            "spec_tree_attn_verify_paged", "spec_tree_attn_verify_f8", "spec_tree_attn_verify_f4",
            "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted", "spec_commit_accepted_paged",
            "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_verify_step_workspace_bytes",
-           "spec_verify_step", "spec_verify_step_paged", "spec_status_string"]
+           "spec_verify_step", "spec_verify_step_paged", "spec_verify_step_static", "spec_status_string"]
 
 
 class SpecError(RuntimeError):
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
                                          c_p, c_i64, c_i64, c_i, c_i, c_i, c_i, c_i, c_f, c_p, c_p, c_p, c_p, c_p,
                                          c_p, c_p, c_p, c_p, c_sz, c_p, c_p]
     L.spec_verify_step_paged.restype = c_i
+    L.spec_verify_step_static.argtypes = L.spec_verify_step.argtypes[:-4] + [c_p, c_p]
+    L.spec_verify_step_static.restype = c_i
     L.spec_status_string.argtypes = [c_i]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -439,3 +442,28 @@ def verify_step(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits,
         if e:
             raise SpecError(f"device data error bits 0x{e:x}")
     return res
+
+
+def verify_step_static(parents, draft_tokens, prefix_lens, q, k_cache, v_cache, logits, sm_scale, *, outs,
+                       k_scale=None, v_scale=None, stream=None):
+    """spec_verify_step_static: the one-launch verify step on the library's
+    static scratch.  Allocates nothing, here or in the library: ``outs``
+    (from step_outputs, made beforehand) receives every result and its error
+    word is OR'ed into.  Calls that overlap in time on one GPU race."""
+    if outs is None:
+        raise SpecError("verify_step_static takes preallocated outputs (step_outputs)")
+    B, N = parents.shape
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] != B * N:
+        raise SpecError("logits must be a float32 [B*N][V] tensor with unit column stride")
+    if q.dtype not in _DTYPE or k_cache.dtype not in _DTYPE or v_cache.dtype != k_cache.dtype:
+        raise SpecError(f"unsupported dtypes q={q.dtype} k={k_cache.dtype} v={v_cache.dtype}")
+    o = outs
+    _check(lib().spec_verify_step_static(
+        _ptr(parents), _ptr(draft_tokens), _ptr(prefix_lens), _ptr(q), _DTYPE[q.dtype], _ptr(k_cache),
+        _ptr(v_cache), _DTYPE[k_cache.dtype], _ptr(k_scale), _ptr(v_scale), ctypes.c_void_p(logits.data_ptr()),
+        logits.shape[1], logits.stride(0), B, N, Hq, Hkv, D, S_max, float(sm_scale), _ptr(o["mask"]),
+        _ptr(o["depth"]), _ptr(o["out"]), _ptr(o["lse"]), _ptr(o["argmax"]), _ptr(o["accept_len"]),
+        _ptr(o["path_nodes"]), _ptr(o["out_tokens"]), _ptr(o["err"]), _stream(stream)))
+    return o

@@ -21,6 +21,12 @@ spec_status tree_attn_check(const void* q, spec_dtype q_dtype, const void* k_cac
                             int Hkv, int D, int S_max, float sm_scale, const void* out, const void* workspace,
                             size_t workspace_bytes);
 
+// tree_attn_check without the workspace: every other reason it can refuse.
+spec_status tree_attn_check_args(const void* q, spec_dtype q_dtype, const void* k_cache, const void* v_cache,
+                                 spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                 const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N, int Hq,
+                                 int Hkv, int D, int S_max, float sm_scale, const void* out);
+
 // spec_tree_attn_verify for bf16 or decoded-fp8 caches (arguments already
 // accepted by tree_attn_check), with the verify step's prep role (masks,
 // argmax, accept walk) added to the same launch.

@@ -1568,11 +1568,10 @@ namespace spectree {
 
 // Every reason spec_tree_attn_verify can refuse a call before it launches
 // anything (the fused verify step checks the same before its first launch).
-spec_status tree_attn_check(const void* q, spec_dtype q_dtype, const void* k_cache, const void* v_cache,
-                            spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
-                            const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N, int Hq,
-                            int Hkv, int D, int S_max, float sm_scale, const void* out, const void* workspace,
-                            size_t workspace_bytes) {
+spec_status tree_attn_check_args(const void* q, spec_dtype q_dtype, const void* k_cache, const void* v_cache,
+                                 spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                 const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N, int Hq,
+                                 int Hkv, int D, int S_max, float sm_scale, const void* out) {
   if (!q || !k_cache || !v_cache || !prefix_lens || !anc_mask || !out) return SPEC_ERR_NULL;
   const bool f32 = (q_dtype == SPEC_F32 && kv_dtype == SPEC_F32);
   const bool bf16 = (q_dtype == SPEC_BF16 && kv_dtype == SPEC_BF16);
@@ -1584,6 +1583,20 @@ spec_status tree_attn_check(const void* q, spec_dtype q_dtype, const void* k_cac
   if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return SPEC_ERR_ALIGN;
+  return SPEC_OK;
+}
+
+spec_status tree_attn_check(const void* q, spec_dtype q_dtype, const void* k_cache, const void* v_cache,
+                            spec_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                            const int32_t* prefix_lens, const uint64_t* anc_mask, int B, int N, int Hq,
+                            int Hkv, int D, int S_max, float sm_scale, const void* out, const void* workspace,
+                            size_t workspace_bytes) {
+  const spec_status st = tree_attn_check_args(q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, prefix_lens,
+                                              anc_mask, B, N, Hq, Hkv, D, S_max, sm_scale, out);
+  if (st != SPEC_OK) return st;
+  const bool f32 = (q_dtype == SPEC_F32 && kv_dtype == SPEC_F32);
+  AttnPlan pl;
+  make_plan(B, N, Hq, Hkv, D, S_max, &pl);
   if (!f32 && pl.ws_bytes) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ALIGN;

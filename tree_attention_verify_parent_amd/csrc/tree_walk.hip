@@ -77,6 +77,8 @@ extern "C" const char* spec_status_string(spec_status status) {
     case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace missing or too small";
     case SPEC_ERR_HIP: return "SPEC_ERR_HIP: kernel launch failed";
     case SPEC_ERR_ALIGN: return "SPEC_ERR_ALIGN: pointer not 16-byte aligned";
+    case SPEC_ERR_SCRATCH:
+      return "SPEC_ERR_SCRATCH: these sizes need more scratch than the library's static buffer holds";
   }
   return "unknown spec_status";
 }
