@@ -839,7 +839,12 @@ void tree_attn_split_kernel(
       return i32x8_t{t[0][0], t[0][1], t[1][0], t[1][1], 0, 0, 0, 0};
     };
 
-    auto compute_f8 = [&](int st, int i) {
+    // Tiles come in two kinds, told apart once per tile (the test is
+    // wave-uniform): plain tiles, whose tokens are all prefix and all inside
+    // the piece, and masked ones.  MASKED is a compile-time flag, so plain
+    // tiles carry no per-score select at all.
+    auto compute_f8 = [&](int st, int i, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value != 0;
       const unsigned char* ks = kst(st);
       const unsigned char* vs = vst(st);
       const int t0 = t_begin + i * TILE;
@@ -858,7 +863,6 @@ void tree_attn_split_kernel(
           for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
       }
-      const bool plain = (t0 + TILE <= min(P, t_end));
       // a 64-token half of the tile: all prefix inside the piece, past the
       // piece's end, or masked in registers
       auto half_vis = [&](uint64_t a, int th) -> uint64_t {
@@ -871,7 +875,7 @@ void tree_attn_split_kernel(
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         uint64_t vis[2] = {~0ull, ~0ull};
-        if (!plain) {
+        if constexpr (MASKED) {
           vis[0] = half_vis(anc[rb], t0);
           vis[1] = half_vis(anc[rb], t0 + kTile);
         }
@@ -881,7 +885,7 @@ void tree_attn_split_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float s = sacc[rb][kb][r];
-            if (!plain) s = ((vis[kb >> 2] >> (16 * (kb & 3) + 4 * lg + r)) & 1ull) ? s : -INFINITY;
+            if constexpr (MASKED) s = ((vis[kb >> 2] >> (16 * (kb & 3) + 4 * lg + r)) & 1ull) ? s : -INFINITY;
             sacc[rb][kb][r] = s;
             mx = fmaxf(mx, s);
           }
@@ -929,7 +933,8 @@ void tree_attn_split_kernel(
       }
     };
 
-    auto compute = [&](int st, int i) {
+    auto compute = [&](int st, int i, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value != 0;
       const unsigned char* ks = kst(st);
       const unsigned char* vs = vst(st);
       const int t0 = t_begin + i * kTile;
@@ -955,15 +960,15 @@ void tree_attn_split_kernel(
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       // ---- mask, online softmax (base 2), P in bf16
-      const bool plain = (t0 + kTile <= min(P, t_end));   // all 64 tokens are prefix, all in the piece
       bf16x8_t pb[RB][CPT];
       float alpha[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         // this lane's 8 tokens of chunk cp sit at bits 32*ch + 8*lg .. +7
         uint32_t vis8[CPT];
-        if (!plain) {
+        if constexpr (MASKED) {
           const uint64_t vis = tile_visibility(anc[rb], t0, P, t_end);
 #pragma unroll
           for (int cp = 0; cp < CPT; ++cp) vis8[cp] = (uint32_t)(vis >> (32 * (wt * CPT + cp) + 8 * lg)) & 0xFFu;
@@ -978,7 +983,7 @@ void tree_attn_split_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               float s = sacc[rb][cp][G][r];
-              if (!plain) s = ((vis8[cp] >> (4 * G + r)) & 1u) ? s : -INFINITY;
+              if constexpr (MASKED) s = ((vis8[cp] >> (4 * G + r)) & 1u) ? s : -INFINITY;
               sacc[rb][cp][G][r] = s;
               mx = fmaxf(mx, s);
             }
@@ -1014,6 +1019,7 @@ void tree_attn_split_kernel(
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
       }
+      __builtin_amdgcn_sched_barrier(0);
       // ---- O^T += V^T . P^T
 #pragma unroll
       for (int cp = 0; cp < CPT; ++cp) {
@@ -1030,7 +1036,7 @@ void tree_attn_split_kernel(
     // ring: wait for tile i (the tiles after it stay in flight), make it visible
     // to all waves, refill the stage tile i-1 used, compute tile i
     int st = 0;
-    for (int i = 0; i < ntiles; ++i) {
+    auto tile_step = [&](int i, auto masked_tag) {
       const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
       // tiles 0 .. NSTAGE-2 went out before the loads' wait above and have
       // landed; the counted waits start with the first tile the loop issued
@@ -1045,10 +1051,16 @@ void tree_attn_split_kernel(
       }
       wg_barrier();
       if (i + NSTAGE - 1 < ntiles) issue(st == 0 ? NSTAGE - 1 : st - 1, i + NSTAGE - 1);
-      if constexpr (F8) compute_f8(st, i);
-      else compute(st, i);
+      if constexpr (F8) compute_f8(st, i, masked_tag);
+      else compute(st, i, masked_tag);
       st = (st + 1 == NSTAGE) ? 0 : st + 1;
-    }
+    };
+    // Plain tiles (every token prefix and inside the piece) come first, the
+    // masked ones (tree rows, the piece's ragged end) after them: two loops,
+    // so the plain loop holds none of the masked path's registers.
+    const int n_plain = __builtin_amdgcn_readfirstlane(max(0, min(ntiles, (min(P, t_end) - t_begin) / TILE)));
+    for (int i = 0; i < n_plain; ++i) tile_step(i, Int<0>{});
+    for (int i = n_plain; i < ntiles; ++i) tile_step(i, Int<1>{});
     // ---- waves that split the tile's tokens combine their states in LDS
     if constexpr (WT == 2) {
       // scratch in the ring: O blocks (1 KB per row block and column block)
