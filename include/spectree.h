@@ -380,17 +380,21 @@ size_t spec_tree_attn_backward_workspace_bytes(int B, int N, int Hq, int Hkv, in
  *   dtype         SPEC_F32 (all fp32) or SPEC_BF16 (all bf16)
  *   lse           float[B][N][Hq], required
  *   D             64 or 128
- *   Hq/Hkv * N    at most 128
  *   dq            out: [B][N][Hq][D] of dtype
  *   dk, dv        out: [B][Hkv][S_max][D] of dtype; rows c < P_b + N are
  *                 written, later rows are left as they are
  *   workspace     >= spec_tree_attn_backward_workspace_bytes(...) bytes,
- *                 16-B aligned, zero-filled before its first use and left
- *                 zeroed by every call (the same rules as the forward pass's)
+ *                 16-B aligned, zero-filled before its first use; every call
+ *                 leaves its counters at zero again (the forward pass's
+ *                 rules).  With more than 128 packed rows (Hq/Hkv * N) in
+ *                 bf16 it also holds fp32 dK and dV sums, 2 * B * Hkv *
+ *                 S_max * D floats, which need no clearing.
  *   err_word      nullable: SPEC_DERR_PREFIX
- * Accumulation is fp32; bf16 results are rounded to nearest even.  The sum
- * over a request's keys is taken in a fixed order, so results are
- * deterministic.
+ * Accumulation is fp32; bf16 results are rounded to nearest even.  More
+ * than 128 packed rows in bf16 run as one launch per 128-row tile, in
+ * order, summing dK / dV in the workspace's fp32 arrays.  Every sum (over a
+ * request's keys, and over the row tiles) is taken in a fixed order, so
+ * results are deterministic.
  */
 spec_status spec_tree_attn_backward(const void* q, const void* k_cache, const void* v_cache, spec_dtype dtype,
                                     const int32_t* prefix_lens, const uint64_t* anc_mask, const void* out,

@@ -45,6 +45,15 @@ CASES = {
     "one_tile_direct": W[1].replace(B=3, prefix_lo=5, prefix_hi=50, seed=37),
     "tree64_g2_deep": W[2].replace(B=2, N=64, Hq=4, Hkv=2, max_depth=30, max_children=2, prefix_lo=0,
                                    prefix_hi=200, seed=38),
+    # more than 128 packed rows: one launch per 128-row tile, dK / dV summed in fp32 across them.
+    # The 60-node tree of 16 query heads per KV head (960 rows, 8 tiles) over short ragged prefixes
+    # (runs of one or two tiles, so dq partials merge too); two tiles (160 rows); D = 64 over three
+    # tiles (320 rows, the last one partial) with empty prefixes
+    "tree60_g16_d128_rowtiles": W[3].replace(B=2, prefix_lo=150, prefix_hi=400, seed=40),
+    "tree20_g8_d128_two_tiles": W[2].replace(B=2, N=20, max_depth=5, max_children=3, prefix_lo=64,
+                                             prefix_hi=700, seed=41),
+    "tree40_g8_d64_three_tiles": W[2].replace(B=2, N=40, D=64, max_depth=6, max_children=4, prefix_lo=0,
+                                              prefix_hi=300, seed=42),
     "chain6_f32": W[0],
     # the fp32 path with a branching tree, D = 128, ragged prefixes over several key chunks per wave
     "tree16_f32_d128_ragged": W[0].replace(B=3, N=16, Hq=8, Hkv=2, D=128, tree="random", max_depth=5, max_children=3,
@@ -151,12 +160,17 @@ def test_backward_flags_a_bad_prefix_and_keeps_the_others():
         check_grad(gg, ww, gname + " (good requests)", "bf16")
 
 
-def test_backward_rejects_too_many_packed_rows():
-    w = W[3].replace(B=1, prefix_lo=10, prefix_hi=10)          # 16 x 60 = 960 rows
+def test_backward_row_tiles_are_deterministic():
+    """More than 128 packed rows, two calls on one workspace: the row tiles
+    run in order and overwrite the fp32 sums, the run partials are summed in
+    run order, and the counters are left at zero, so the second call repeats
+    the first bit for bit."""
+    w = CASES["tree60_g16_d128_rowtiles"]
     x = synth.make_backward_inputs(w)
-    dev = "cuda"
-    q, k, v, do = (x[n].to(dev) for n in ("q", "k_cache", "v_cache", "d_out"))
-    lse = torch.zeros(q.shape[:3], dtype=torch.float32, device=dev)
-    anc = torch.zeros((1, w.N), dtype=torch.int64, device=dev)
-    with pytest.raises(st.SpecError):
-        st.tree_attn_backward(q, k, v, torch.from_numpy(x["prefix_lens"]).to(dev), anc, q, lse, do, x["sm_scale"])
+    ws = torch.zeros(st.attn_backward_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max), dtype=torch.uint8,
+                     device="cuda")
+    a = run_gpu(x, ws)
+    b = run_gpu(x, ws)
+    assert a[3] == 0 and b[3] == 0
+    for g1, g2 in zip(a[:3], b[:3]):
+        assert np.array_equal(g1, g2)
