@@ -561,7 +561,10 @@ def measure(w, x, args, steps, warmup, extras):
             bbytes = 2 * bytes_["kv"] + 4 * q_bytes + 4 * B * N * w.Hq + 8 * B * N + 4 * B
             # five products (S, dP, dV, dK, dq) against the forward pass's two
             bflops = bytes_["attn_flops"] * 5 // 2
-            res["backward"] = dict(kernel="tree_attn_bwd_kernel", launch_us=round(bwd_us, 3),
+            # more than 128 packed rows: row statistics, then the dq and dK / dV passes
+            kname = ("bwd_rowstat_kernel + tree_attn_bwd_dq_kernel + tree_attn_bwd_dkdv_kernel"
+                     if w.group * N > 128 else "tree_attn_bwd_kernel")
+            res["backward"] = dict(kernel=kname, launch_us=round(bwd_us, 3),
                                    bytes_per_launch=bbytes, achieved_gbs=round(bbytes / bwd_us / 1e3, 1),
                                    frac=round(bbytes / bwd_us / 1e3 / PEAK_HBM_GBS, 4),
                                    mfma_tflops=round(bflops / bwd_us / 1e6, 1))

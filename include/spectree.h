@@ -387,14 +387,16 @@ size_t spec_tree_attn_backward_workspace_bytes(int B, int N, int Hq, int Hkv, in
  *                 16-B aligned, zero-filled before its first use; every call
  *                 leaves its counters at zero again (the forward pass's
  *                 rules).  With more than 128 packed rows (Hq/Hkv * N) in
- *                 bf16 it also holds fp32 dK and dV sums, 2 * B * Hkv *
- *                 S_max * D floats, which need no clearing.
+ *                 bf16 it holds instead two floats per (request, node, head)
+ *                 row, written by the call before they are read: no
+ *                 clearing needed.
  *   err_word      nullable: SPEC_DERR_PREFIX
  * Accumulation is fp32; bf16 results are rounded to nearest even.  More
- * than 128 packed rows in bf16 run as one launch per 128-row tile, in
- * order, summing dK / dV in the workspace's fp32 arrays.  Every sum (over a
- * request's keys, and over the row tiles) is taken in a fixed order, so
- * results are deterministic.
+ * than 128 packed rows in bf16 run as three launches: per-row statistics,
+ * a dq pass (128 rows per workgroup, over all keys) and a dK / dV pass (a
+ * run of 128-key tiles per workgroup, over all rows), with no partial sums
+ * in memory.  Every sum is taken in a fixed order, so results are
+ * deterministic.
  */
 spec_status spec_tree_attn_backward(const void* q, const void* k_cache, const void* v_cache, spec_dtype dtype,
                                     const int32_t* prefix_lens, const uint64_t* anc_mask, const void* out,

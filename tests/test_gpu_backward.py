@@ -45,11 +45,13 @@ CASES = {
     "one_tile_direct": W[1].replace(B=3, prefix_lo=5, prefix_hi=50, seed=37),
     "tree64_g2_deep": W[2].replace(B=2, N=64, Hq=4, Hkv=2, max_depth=30, max_children=2, prefix_lo=0,
                                    prefix_hi=200, seed=38),
-    # more than 128 packed rows: one launch per 128-row tile, dK / dV summed in fp32 across them.
-    # The 60-node tree of 16 query heads per KV head (960 rows, 8 tiles) over short ragged prefixes
-    # (runs of one or two tiles, so dq partials merge too); two tiles (160 rows); D = 64 over three
-    # tiles (320 rows, the last one partial) with empty prefixes
+    # more than 128 packed rows: the separate dq pass (128-row tiles of the rows) and dK / dV pass
+    # (runs of 128-key tiles, the rows streamed 64 at a time).  The 60-node tree of 16 query heads per
+    # KV head (960 rows: 8 dq tiles, 15 row steps) over short ragged prefixes (runs of one key tile);
+    # the same tree over 16 requests (runs of two key tiles); 160 rows (a partial dq tile and row
+    # step); D = 64 over 320 rows with empty prefixes
     "tree60_g16_d128_rowtiles": W[3].replace(B=2, prefix_lo=150, prefix_hi=400, seed=40),
+    "tree60_g16_d128_key_runs": W[3].replace(B=16, prefix_lo=200, prefix_hi=600, seed=43),
     "tree20_g8_d128_two_tiles": W[2].replace(B=2, N=20, max_depth=5, max_children=3, prefix_lo=64,
                                              prefix_hi=700, seed=41),
     "tree40_g8_d64_three_tiles": W[2].replace(B=2, N=40, D=64, max_depth=6, max_children=4, prefix_lo=0,
@@ -133,8 +135,10 @@ def test_backward_is_deterministic_and_reuses_its_workspace():
     assert int(ws.view(torch.int32)[-w.B * w.Hkv:].abs().sum()) == 0
 
 
-def test_backward_flags_a_bad_prefix_and_keeps_the_others():
-    w = CASES["tree8_g8_d128"].replace(B=3, seed=39)
+@pytest.mark.parametrize("name", ["tree8_g8_d128", "tree20_g8_d128_two_tiles"])
+def test_backward_flags_a_bad_prefix_and_keeps_the_others(name):
+    w = CASES[name].replace(B=3, seed=39)
+    log(f"[backward bad prefix] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} seed={w.seed}")
     x = synth.make_backward_inputs(w)
     bad = x["prefix_lens"].copy()
     bad[1] = w.S_max - w.N + 1                                  # its tree would run past the cache
@@ -161,10 +165,9 @@ def test_backward_flags_a_bad_prefix_and_keeps_the_others():
 
 
 def test_backward_row_tiles_are_deterministic():
-    """More than 128 packed rows, two calls on one workspace: the row tiles
-    run in order and overwrite the fp32 sums, the run partials are summed in
-    run order, and the counters are left at zero, so the second call repeats
-    the first bit for bit."""
+    """More than 128 packed rows, two calls on one workspace: every gradient
+    element is summed by one workgroup in a fixed order (no partial sums, no
+    atomics), so the second call repeats the first bit for bit."""
     w = CASES["tree60_g16_d128_rowtiles"]
     x = synth.make_backward_inputs(w)
     ws = torch.zeros(st.attn_backward_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.S_max), dtype=torch.uint8,

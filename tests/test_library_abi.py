@@ -157,13 +157,11 @@ def test_backward_workspace_bytes(L):
     # no run longer than 64 tiles: 512 sequences of 129 tiles -> 3 runs of 43
     assert f(64, 16, 64, 8, 128, 8208) == 512 * 3 * 128 * 128 * 4 + 512 * 4
     assert f(64, 16, 64, 8, 128, 64) == 0                            # one tile: dq is written directly
-    # more than 128 packed rows (8 x 17 = 136): two 128-row tiles.  The dq partials (64 sequences x 4 runs
-    # of 9 tiles x 128 rows) and the counters come first, then at a 256-byte boundary the fp32 dK / dV sums
-    # (2 x 64 sequences x 2054 rows x 128 floats)
-    part = 64 * 4 * 128 * 128 * 4
-    assert f(8, 17, 64, 8, 128, 2054) == ((part + 64 * 4 + 255) & ~255) + 2 * 64 * 2054 * 128 * 4
-    # 16 x 60 = 960 rows, 8 tiles; one tile of keys: no partials
-    assert f(4, 60, 64, 4, 128, 64) == 2 * 16 * 64 * 128 * 4
+    # more than 128 packed rows (8 x 17 = 136): the separate dq and dK / dV passes keep no partial sums;
+    # the workspace holds D and lse * log2(e) of each (request, node, head) row, 256-byte aligned each
+    assert f(8, 17, 64, 8, 128, 2054) == 2 * ((8 * 17 * 64 * 4 + 255) & ~255)
+    # 16 x 60 = 960 rows: the same two arrays, whatever the cache length
+    assert f(4, 60, 64, 4, 128, 64) == f(4, 60, 64, 4, 128, 32828) == 2 * 4 * 60 * 64 * 4
     for bad in [(8, 6, 32, 8, 96, 2054), (8, 65, 64, 8, 128, 2054), (8, 6, 30, 8, 128, 2054),
                 (0, 6, 32, 8, 128, 2054), (8, 6, 32, 8, 128, 5)]:
         assert f(*bad) == 0, bad

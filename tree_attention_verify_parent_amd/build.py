@@ -12,7 +12,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB = os.path.join(PKG_DIR, "libspectree.so")
-SOURCES = ["tree_walk.hip", "argmax.hip", "tree_attn.hip", "commit.hip", "tree_attn_bwd.hip", "step.hip"]
+SOURCES = ["tree_walk.hip", "argmax.hip", "tree_attn.hip", "commit.hip", "tree_attn_bwd.hip",
+           "tree_attn_bwd_wide.hip", "step.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -29,19 +29,15 @@
 // MFMA v_mfma_f32_16x16x32_bf16 throughout; operands that contract over
 // keys or rows come from the LDS transpose reads (ds_read_b64_tr_b16).
 //
-// More than 128 packed rows: the rows are cut into 128-row tiles, one launch
-// each, in order.  A launch's dq rows are its own; dK / dV sum over every
-// row, so they accumulate across the launches in fp32 scratch (MODE 1 writes
-// it, MODE 2 adds to it, MODE 3 adds and writes the bf16 result): each tile
-// loads its keys' running sums straight into its accumulators, ahead of the
-// next tile's DMA, so the wait for them never drains the K/V prefetch.  The
-// sum over the row tiles is taken in a fixed order (deterministic).
+// More than 128 packed rows do not fit one workgroup's LDS: that case runs
+// as separate dq and dK / dV passes (tree_attn_bwd_wide.hip).
 //
 // fp32 path: one plain launch of 4-wave workgroups (dq per row, dK / dV per key), exact fp32
 // arithmetic, for small problems.
 #include <cmath>
 
 #include "gfx950.h"
+#include "host_api.h"
 
 namespace spectree {
 
@@ -122,30 +118,20 @@ struct Shape {
                                (NLOAD % kWaves == 0) && (MP % 32 == 0) && (MP <= 128);
 };
 
-// MODE 0: all rows in one launch, dK / dV written in bf16.  Row-tile
-// launches: MODE 1 (first tile) writes fp32 dK / dV sums to acc_k / acc_v,
-// MODE 2 adds to them, MODE 3 (last tile) adds and writes bf16 dK / dV.
-template <int D, int MP, int NSTAGE, int MODE>
+template <int D, int MP, int NSTAGE>
 __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ prefix_lens, const uint64_t* __restrict__ anc_mask,
     const __bf16* __restrict__ out, const float* __restrict__ lse, const __bf16* __restrict__ dout,
     int N, int Hq, int Hkv, int S_max, float sm_scale, int split_len, int n_splits,
     __bf16* __restrict__ dq, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-    float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word, int m0,
-    float* __restrict__ acc_k, float* __restrict__ acc_v) {
+    float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word) {
   using SH = Shape<D, MP, NSTAGE>;
   static_assert(SH::fits, "shape does not fit the LDS or the vmcnt counter");
-  static_assert(MODE == 0 || (NSTAGE == 2 && MP == 128), "row tiles are 128 rows with a two-stage ring");
   constexpr int RBYTES = SH::RBYTES, UPR = SH::UPR, TB = SH::TB, KPW = SH::KPW, PT = SH::PT;
   constexpr int RPI = SH::RPI, KC = SH::KC, DB = SH::DB, MB = SH::MB, KS = SH::KS, DN = SH::DN;
   constexpr int DS_STRIDE = SH::DS_STRIDE;
-  // stores per wave per tile, which the ring's waits count: bf16 rows turned
-  // around through LDS, or fp32 sums in the MFMA layout (one per column block
-  // and tensor)
-  constexpr bool F32_OUT = (MODE == 1 || MODE == 2);
-  constexpr bool F32_IN = (MODE == 2 || MODE == 3);
-  constexpr int SPT = F32_OUT ? 2 * DB : SH::SPT;
+  constexpr int SPT = SH::SPT;                     // dK / dV row stores per wave per tile
 
   __shared__ __align__(1024) unsigned char ring[NSTAGE * 2 * TB];
   __shared__ __align__(16) unsigned char sq[MP * RBYTES];
@@ -161,8 +147,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
   const int b = seq / Hkv;
   const int kvh = seq % Hkv;
   const int g = Hq / Hkv;
-  // this launch's rows: packed rows m0 .. m0+M-1 (all g*N of them in MODE 0)
-  const int M = MODE == 0 ? g * N : min(MP, g * N - m0);
+  const int M = g * N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
   // mask.  Rows m >= M repeat row M-1; their lse becomes +inf, so p = 0.
   {
     auto row_of = [&](int m) -> size_t {
-      const int mm = m0 + min(m, M - 1);
+      const int mm = min(m, M - 1);
       return (size_t)(b * N + mm / g) * Hq + kvh * g + mm % g;
     };
     constexpr int QI = MP * RBYTES / 1024;         // 1-KB DMA instructions per tensor
@@ -226,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
 #pragma unroll
       for (int j = 0; j < (2 * MP + 63) / 64; ++j) {
         const int idx = 64 * j + lane;             // dword idx of the per-row masks
-        const int m = m0 + min(idx >> 1, M - 1);
+        const int m = min(idx >> 1, M - 1);
         if ((idx >> 1) < MP)
           dma4(reinterpret_cast<const uint32_t*>(anc_mask) + 2 * ((size_t)b * N + m / g) + (idx & 1),
                LDS_ADDR(s_anc) + 256 * j);
@@ -338,12 +323,6 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
   // waits count on)
   const __amdgpu_buffer_rsrc_t rdk = dev_rsrc(dk + kv_off, L * RBYTES);
   const __amdgpu_buffer_rsrc_t rdv = dev_rsrc(dv + kv_off, L * RBYTES);
-  // fp32 running sums of dK / dV over the row tiles, same row layout as the
-  // caches (L rows in bounds)
-  const __amdgpu_buffer_rsrc_t rak = dev_rsrc(MODE != 0 ? (const void*)(acc_k + kv_off) : (const void*)dk,
-                                              MODE != 0 ? L * D * 4 : 0);
-  const __amdgpu_buffer_rsrc_t rav = dev_rsrc(MODE != 0 ? (const void*)(acc_v + kv_off) : (const void*)dv,
-                                              MODE != 0 ? L * D * 4 : 0);
 
   int st = 0;
   for (int i = 0; i < ntiles; ++i) {
@@ -353,19 +332,6 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
     const int sb = min(i, NSTAGE - 1);
     wait_ring<PT, SPT, NSTAGE - 2, NSTAGE - 1>(ahead, sb);
     wg_barrier();                                  // tile i visible; tile i-1 and its dS done
-    // the earlier row tiles' dK / dV sums of this wave's 16 keys, in the MFMA
-    // layout (column d = 16db + 4lg + r of key 16w + l16), ahead of the DMA
-    f32x4_t prev_k[F32_IN ? DB : 1], prev_v[F32_IN ? DB : 1];
-    if constexpr (F32_IN) {
-      const int t0p = (tile0 + i) * kTile;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = ((t0p + 16 * w + l16) * D + 16 * db + 4 * lg) * 4;
-        prev_k[db] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rak, off, 0, 0));
-        prev_v[db] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rav, off, 0, 0));
-      }
-    }
-    const bool dma_next = (i + NSTAGE - 1 < ntiles);
     if (i + NSTAGE - 1 < ntiles) {
       int nst = st + NSTAGE - 1;
       if (nst >= NSTAGE) nst -= NSTAGE;
@@ -422,23 +388,12 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
       *reinterpret_cast<bf16x4_t*>(sds + key * DS_STRIDE + (16 * mb + 4 * lg) * 2) = dsv;
     }
 
-    // ---- dV^T = dO^T . P and dK^T = Q^T . dS (rows d, column = key),
-    // on top of the earlier row tiles' sums
+    // ---- dV^T = dO^T . P and dK^T = Q^T . dS (rows d, column = key)
     f32x4_t dvacc[DB], dkacc[DB];
-    if constexpr (F32_IN) {
-      // the sums have landed once at most this tile's DMA is in flight
-      if (dma_next) wait_vmcnt<PT>();
-      else wait_vmcnt<0>();
-    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      if constexpr (F32_IN) {
-        dvacc[db] = prev_v[db];
-        dkacc[db] = prev_k[db];
-      } else {
-        dvacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        dkacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      dvacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dkacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -471,20 +426,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
         __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (t0 + 16 * w + row) * RBYTES + u * 16, 0, 0);
       }
     };
-    if constexpr (F32_OUT) {
-      // fp32 sums in the MFMA layout: 16 bytes per lane, keys at or past L
-      // outside the bounds and dropped
-      const int t0p = (tile0 + i) * kTile;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = ((t0p + 16 * w + l16) * D + 16 * db + 4 * lg) * 4;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, dvacc[db]), rav, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, dkacc[db]), rak, off, 0, 0);
-      }
-    } else {
-      stage_out(dvacc, rdv);
-      stage_out(dkacc, rdk);
-    }
+    stage_out(dvacc, rdv);
+    stage_out(dkacc, rdk);
 
     // ---- dq^T += K^T . dS^T over the tile's 64 keys, this wave's columns
     wait_lgkm0();
@@ -516,10 +459,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
   wait_vmcnt<0>();
 
   // ---- dq: rows d = 16*(w*DN + dn) + 4lg + r of column m = 16mb + l16
-  auto dq_row = [&](int m) -> size_t {
-    const int mm = m0 + m;
-    return ((size_t)(b * N + mm / g) * Hq + kvh * g + mm % g) * D;
-  };
+  auto dq_row = [&](int m) -> size_t { return ((size_t)(b * N + m / g) * Hq + kvh * g + m % g) * D; };
   if (direct) {
 #pragma unroll
     for (int dn = 0; dn < DN; ++dn)
@@ -746,10 +686,9 @@ __global__ __launch_bounds__(kBwdF32Waves * kWave) void tree_attn_bwd_f32_kernel
 // ---------------------------------------------------------------- host
 struct BwdPlan {
   int mp, nstage, split_len, n_splits;
-  int n_mt;                      // 128-row tiles of the packed rows (1: all rows in one launch)
+  bool wide;                     // more than 128 packed rows: the separate dq and dK / dV passes
   size_t part_bytes;             // dq partials of the runs (0 when every run covers its sequence)
   size_t cnt_off;                // byte offset of the per-sequence run counters
-  size_t acc_off;                // byte offset of the fp32 dK / dV sums (row tiles only)
   size_t ws_bytes;
 };
 
@@ -766,9 +705,18 @@ static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPl
   if (S_max < N || (long long)B * Hkv * S_max >= (1ll << 31) / 2 || (long long)S_max * D * 2 >= (1ll << 31))
     return false;
   const int M = (Hq / Hkv) * N;
+  p->wide = M > 128;
+  if (p->wide) {
+    p->mp = 0;
+    p->nstage = 0;
+    p->split_len = 0;
+    p->n_splits = 1;
+    p->part_bytes = p->cnt_off = 0;
+    p->ws_bytes = bwd_wide_workspace_bytes(B, N, Hq);
+    return true;
+  }
   p->mp = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
-  p->n_mt = (M + 127) / 128;
-  p->nstage = ((D == 128 && p->mp == 128) || p->n_mt > 1) ? 2 : 3;
+  p->nstage = (D == 128 && p->mp == 128) ? 2 : 3;
   const long long seqs = (long long)B * Hkv;
   const int n_tiles = (S_max + kTile - 1) / kTile;
   const long long want = std::max<long long>((kCUs + seqs - 1) / seqs, (n_tiles + kMaxRun - 1) / kMaxRun);
@@ -776,50 +724,24 @@ static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPl
   p->split_len = split_len;
   p->n_splits = (n_tiles + split_len - 1) / split_len;
   if (seqs * p->n_splits >= (1ll << 31)) return false;
-  // workspace: dq partials and run counters when runs split a sequence; then
-  // (256-byte aligned) the fp32 dK and dV sums over the row tiles
+  // workspace: dq partials and run counters when runs split a sequence
   p->part_bytes = p->n_splits > 1 ? (size_t)seqs * p->n_splits * p->mp * D * sizeof(float) : 0;
   p->cnt_off = p->part_bytes;
-  size_t end = p->n_splits > 1 ? p->cnt_off + (size_t)seqs * sizeof(uint32_t) : 0;
-  p->acc_off = (end + 255) & ~(size_t)255;
-  if (p->n_mt > 1) end = p->acc_off + 2 * (size_t)seqs * S_max * D * sizeof(float);
-  p->ws_bytes = end;
+  p->ws_bytes = p->n_splits > 1 ? p->cnt_off + (size_t)seqs * sizeof(uint32_t) : 0;
   return true;
 }
 
-template <int D, int MP, int NS, int MODE>
+template <int D, int MP, int NS>
 static void launch_bwd(const BwdPlan& pl, const void* q, const void* k, const void* v, const int32_t* pre,
                        const uint64_t* anc, const void* out, const float* lse, const void* dout, int B, int N,
                        int Hq, int Hkv, int S_max, float sm_scale, void* dq, void* dk, void* dv, float* part,
-                       uint32_t* cnt, uint32_t* err, int m0, float* acc_k, float* acc_v, hipStream_t st) {
+                       uint32_t* cnt, uint32_t* err, hipStream_t st) {
   const unsigned grid = (unsigned)(B * Hkv) * (unsigned)pl.n_splits;
-  hipLaunchKernelGGL((tree_attn_bwd_kernel<D, MP, NS, MODE>), dim3(grid), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((tree_attn_bwd_kernel<D, MP, NS>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
                      pre, anc, static_cast<const __bf16*>(out), lse, static_cast<const __bf16*>(dout), N, Hq, Hkv,
                      S_max, sm_scale, pl.split_len, pl.n_splits, static_cast<__bf16*>(dq),
-                     static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), part, cnt, err, m0, acc_k, acc_v);
-}
-
-// The row tiles of the packed rows, one launch each in order (first, middle
-// ones, last), for M > 128.
-template <int D>
-static void launch_bwd_tiles(const BwdPlan& pl, const void* q, const void* k, const void* v, const int32_t* pre,
-                             const uint64_t* anc, const void* out, const float* lse, const void* dout, int B,
-                             int N, int Hq, int Hkv, int S_max, float sm_scale, void* dq, void* dk, void* dv,
-                             float* part, uint32_t* cnt, uint32_t* err, float* acc_k, float* acc_v,
-                             hipStream_t st) {
-  for (int t = 0; t < pl.n_mt; ++t) {
-    const int m0 = 128 * t;
-    if (t == 0)
-      launch_bwd<D, 128, 2, 1>(pl, q, k, v, pre, anc, out, lse, dout, B, N, Hq, Hkv, S_max, sm_scale, dq, dk, dv,
-                               part, cnt, err, m0, acc_k, acc_v, st);
-    else if (t + 1 < pl.n_mt)
-      launch_bwd<D, 128, 2, 2>(pl, q, k, v, pre, anc, out, lse, dout, B, N, Hq, Hkv, S_max, sm_scale, dq, dk, dv,
-                               part, cnt, err, m0, acc_k, acc_v, st);
-    else
-      launch_bwd<D, 128, 2, 3>(pl, q, k, v, pre, anc, out, lse, dout, B, N, Hq, Hkv, S_max, sm_scale, dq, dk, dv,
-                               part, cnt, err, m0, acc_k, acc_v, st);
-  }
+                     static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), part, cnt, err);
 }
 
 }  // namespace bwd
@@ -867,33 +789,22 @@ extern "C" spec_status spec_tree_attn_backward(const void* q, const void* k_cach
 
   float* part = nullptr;
   uint32_t* cnt = nullptr;
-  float *acc_k = nullptr, *acc_v = nullptr;
   if (pl.ws_bytes) {
     if (!workspace || workspace_bytes < pl.ws_bytes) return SPEC_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 15u) return SPEC_ERR_ALIGN;
     char* ws = static_cast<char*>(workspace);
-    if (pl.n_splits > 1) {
+    if (!pl.wide && pl.n_splits > 1) {
       part = reinterpret_cast<float*>(ws);
       cnt = reinterpret_cast<uint32_t*>(ws + pl.cnt_off);
     }
-    if (pl.n_mt > 1) {
-      acc_k = reinterpret_cast<float*>(ws + pl.acc_off);
-      acc_v = acc_k + (size_t)B * Hkv * S_max * D;
-    }
   }
-  if (pl.n_mt > 1) {
-    if (D == 128)
-      launch_bwd_tiles<128>(pl, q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, B, N, Hq, Hkv, S_max,
-                            sm_scale, dq, dk, dv, part, cnt, err_word, acc_k, acc_v, stream);
-    else
-      launch_bwd_tiles<64>(pl, q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, B, N, Hq, Hkv, S_max,
-                           sm_scale, dq, dk, dv, part, cnt, err_word, acc_k, acc_v, stream);
-    return launch_status();
-  }
+  if (pl.wide)
+    return bwd_wide_launch(q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, B, N, Hq, Hkv, D, S_max,
+                           sm_scale, dq, dk, dv, workspace, err_word, stream);
 #define SPEC_BWD(D_, MP_, NS_)                                                                                 \
   if (D == D_ && pl.mp == MP_ && pl.nstage == NS_) {                                                           \
-    launch_bwd<D_, MP_, NS_, 0>(pl, q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, B, N, Hq, Hkv, \
-                                S_max, sm_scale, dq, dk, dv, part, cnt, err_word, 0, nullptr, nullptr, stream);   \
+    launch_bwd<D_, MP_, NS_>(pl, q, k_cache, v_cache, prefix_lens, anc_mask, out, lse, d_out, B, N, Hq, Hkv,    \
+                             S_max, sm_scale, dq, dk, dv, part, cnt, err_word, stream);                          \
     return launch_status();                                                                                    \
   }
   SPEC_BWD(128, 32, 3)
