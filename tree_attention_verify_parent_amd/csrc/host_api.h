@@ -61,13 +61,4 @@ spec_status tree_attn_verify_paged_run(const void* q, spec_dtype q_dtype, const 
                                        void* workspace, size_t workspace_bytes, uint32_t* err_word,
                                        const PrepArgs* prep, hipStream_t stream);
 
-// The backward pass for more than 128 packed rows: row statistics, then the
-// dq pass, then the dK / dV pass (arguments already checked; bf16).  The
-// workspace holds bwd_wide_workspace_bytes(B, N, Hq) bytes.
-size_t bwd_wide_workspace_bytes(int B, int N, int Hq);
-spec_status bwd_wide_launch(const void* q, const void* k, const void* v, const int32_t* prefix_lens,
-                            const uint64_t* anc_mask, const void* out, const float* lse, const void* dout, int B,
-                            int N, int Hq, int Hkv, int D, int S_max, float sm_scale, void* dq, void* dk, void* dv,
-                            void* workspace, uint32_t* err_word, hipStream_t stream);
-
 }  // namespace spectree

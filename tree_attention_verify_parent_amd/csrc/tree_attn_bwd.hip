@@ -37,7 +37,7 @@
 #include <cmath>
 
 #include "gfx950.h"
-#include "host_api.h"
+#include "bwd_wide.h"
 
 namespace spectree {
 

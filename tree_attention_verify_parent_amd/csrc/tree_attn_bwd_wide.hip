@@ -30,7 +30,7 @@
 #include <type_traits>
 
 #include "gfx950.h"
-#include "host_api.h"
+#include "bwd_wide.h"
 
 namespace spectree {
 namespace bwd_wide {
