@@ -50,7 +50,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Both enums are int-sized.  In C++ they get int as their fixed underlying
+ * type, so any int a C caller passes (say an unknown dtype) is a value of
+ * the type, which the library then rejects with a status. */
+#ifdef __cplusplus
+#define SPEC_ENUM_INT : int
+#else
+#define SPEC_ENUM_INT
+#endif
+
+typedef enum SPEC_ENUM_INT {
   SPEC_OK = 0,
   SPEC_ERR_NULL = 1,      /* a required pointer is NULL                         */
   SPEC_ERR_SHAPE = 2,     /* a size is out of range or inconsistent             */
@@ -61,7 +70,7 @@ typedef enum {
   SPEC_ERR_SCRATCH = 7    /* the sizes need more than the static scratch holds  */
 } spec_status;
 
-typedef enum {
+typedef enum SPEC_ENUM_INT {
   SPEC_F32 = 0,
   SPEC_BF16 = 1,
   SPEC_FP8_E4M3 = 2,      /* OCP FP8 E4M3 ("e4m3fn"): bias 7, no inf, max 448 */
@@ -524,8 +533,9 @@ spec_status spec_verify_step_static(const int32_t* parents, const int32_t* draft
                                     int32_t* target_argmax, int32_t* accept_len, int32_t* path_nodes,
                                     int32_t* out_tokens, uint32_t* err_word, hipStream_t stream);
 
-/* Human-readable name of a status code (static storage). */
-const char* spec_status_string(spec_status status);
+/* Human-readable name of a status code (static storage).  Takes any int:
+ * codes outside spec_status give "unknown spec_status". */
+const char* spec_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -1400,6 +1400,8 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   if (D != 64 && D != 128) return false;
   if (S_max < N) return false;
   if ((long long)B * S_max >= (1ll << 31) || (long long)Hkv * S_max >= (1ll << 31)) return false;
+  // query rows index in int (B * N * Hq of them; the packed M = g * N is at most that)
+  if ((long long)B * N * Hq >= (1ll << 31)) return false;
   const int M = (Hq / Hkv) * N;
   if (M <= 32) { p->rb = 1; p->wm = 2; p->wt = 2; p->nstage = 3; }
   else if (M <= 64) { p->rb = 2; p->wm = 2; p->wt = 1; p->nstage = 2; }

@@ -704,6 +704,7 @@ static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPl
   if (D != 64 && D != 128) return false;
   if (S_max < N || (long long)B * Hkv * S_max >= (1ll << 31) / 2 || (long long)S_max * D * 2 >= (1ll << 31))
     return false;
+  if ((long long)B * N * Hq >= (1ll << 31)) return false;   // query rows index in int
   const int M = (Hq / Hkv) * N;
   p->wide = M > 128;
   if (p->wide) {

@@ -68,7 +68,7 @@ extern "C" spec_status spec_accept_walk(const int32_t* parents, const uint64_t* 
   return launch_status();
 }
 
-extern "C" const char* spec_status_string(spec_status status) {
+extern "C" const char* spec_status_string(int status) {
   switch (status) {
     case SPEC_OK: return "SPEC_OK";
     case SPEC_ERR_NULL: return "SPEC_ERR_NULL: a required pointer is NULL";
