@@ -531,6 +531,19 @@ def measure(w, x, args, steps, warmup, extras):
         res["f8_attention"] = f8
         del k4s, v4s
 
+    # ---- bf16 caches: the scores on the fp8 matrix cores (q per row and each
+    # K tile rounded to e4m3 in the kernel, p and V in bf16); outside the
+    # parity contract, like the fp8 arithmetic above
+    if w.kv_dtype == "bf16" and w.D == 128:
+        kq = torch.ones(w.Hkv, dtype=torch.float32, device=dev)
+        s8_us = time_graph_calls(
+            lambda r: st.tree_attn_verify_f8_scores(qs[r], kcs[r], vcs[r], prefix, anc, x["sm_scale"], kq, out=out,
+                                                    lse=lse, workspace=ws, err=err), R, calls, reps)
+        res["f8_scores"] = dict(kernel="tree_attn_split_kernel (fp8 scores over a bf16 cache)",
+                                launch_us=round(s8_us, 3), achieved_tflops=round(bytes_["attn_flops"] / s8_us / 1e6, 1),
+                                achieved_gbs=round(bytes_["attention"] / s8_us / 1e3, 1),
+                                vs_bf16=round(attn_us / s8_us, 3))
+
     # ---- the attention's backward pass (training on the verified tree):
     # back-to-back calls over the replicas, each writing its own dK / dV.
     # Shapes the backward pass refuses (its status says so) are skipped.
@@ -671,7 +684,7 @@ def main(argv=None):
         "per_workload": per,
         "bench_wall_s": round(time.perf_counter() - t_start, 1),
     }
-    for k in ("commit_step", "paged_attention", "backward", "f8_attention"):
+    for k in ("commit_step", "paged_attention", "backward", "f8_attention", "f8_scores"):
         if k in hres:
             line[k] = hres[k]
     print(json.dumps(line), flush=True)

@@ -334,6 +334,32 @@ spec_status spec_tree_attn_verify_f8(const void* q, const void* k_cache, const v
                                      uint32_t* err_word, hipStream_t stream);
 
 /*
+ * spec_tree_attn_verify_f8_scores -- spec_tree_attn_verify over bf16 caches
+ * with the scores on the fp8 matrix cores (16x16x128 e4m3 MFMA).
+ * OUTSIDE THE PARITY CONTRACT: q is rounded per row to e4m3 (as in
+ * spec_tree_attn_verify_f8) and each K tile, once per workgroup in LDS, to
+ * e4m3 codes K / kq; the probabilities and V stay bf16, so only the scores
+ * are rounded (both operands to 3 mantissa bits: a few percent relative L2
+ * against the exact attention on the test data).
+ *
+ *   q, out        [B][N][Hq][D] bf16, 16-B aligned
+ *   k_cache,
+ *   v_cache       [B][Hkv][S_max][D] bf16, 16-B aligned
+ *   k_scale       nullable float[Hkv]: kq for kv head h is the power of two
+ *                 of k_scale[h] (its exponent; positive normal floats);
+ *                 NULL means kq = 1.  Precondition: |K| < 448 kq, else the
+ *                 codes are NaN.
+ *   D             128
+ * Other arguments, workspace and results as spec_tree_attn_verify.
+ */
+spec_status spec_tree_attn_verify_f8_scores(const void* q, const void* k_cache, const void* v_cache,
+                                            const float* k_scale, const int32_t* prefix_lens,
+                                            const uint64_t* anc_mask, int B, int N, int Hq, int Hkv, int D,
+                                            int S_max, float sm_scale, void* out, float* lse,
+                                            void* workspace, size_t workspace_bytes,
+                                            uint32_t* err_word, hipStream_t stream);
+
+/*
  * spec_tree_attn_verify_f4 -- the same attention over an e2m1 (FP4) cache,
  * in the fp8 arithmetic of spec_tree_attn_verify_f8.
  *

@@ -136,6 +136,16 @@ void entry_points() {
   expect("f4 D=64", spec_tree_attn_verify_f4(F, F, F, f32, f32, i32, u64, B, N, Hq, Hkv, 64, S, sc, F, nullptr, F, ws,
                                              nullptr, nullptr), SPEC_ERR_SHAPE);
 
+  // fp8 scores over a bf16 cache
+  auto s8 = [&](const void* q, int d, void* w, size_t wb) {
+    return spec_tree_attn_verify_f8_scores(q, F, F, nullptr, i32, u64, B, N, Hq, Hkv, d, S, sc, F, nullptr, w, wb,
+                                           nullptr, nullptr);
+  };
+  expect("f8 scores null", s8(nullptr, D, F, ws), SPEC_ERR_NULL);
+  expect("f8 scores D=64", s8(F, 64, F, ws), SPEC_ERR_SHAPE);
+  expect("f8 scores misaligned", s8(MIS, D, F, ws), SPEC_ERR_ALIGN);
+  expect("f8 scores short workspace", s8(F, D, F, ws - 1), SPEC_ERR_WORKSPACE);
+
   // backward
   const size_t bws = spec_tree_attn_backward_workspace_bytes(B, N, Hq, Hkv, D, S);
   auto bwd = [&](const void* q, spec_dtype dt, int n, void* w, size_t wb) {

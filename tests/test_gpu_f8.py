@@ -170,3 +170,145 @@ def test_f8_rejects_what_it_does_not_cover():
     lib = st.lib()
     assert lib.spec_tree_attn_verify_f8(None, None, None, None, None, None, None, 1, 1, 1, 1, 128, 8, 0.1,
                                         None, None, None, 0, None, None) == 1
+
+
+# ---------------------------------------------------------------------------
+# fp8 scores over bf16 caches (spec_tree_attn_verify_f8_scores), also outside
+# the parity contract: q is rounded per row to e4m3 and K to e4m3 codes
+# K / kq (kq the power of two of k_scale[h]); p and V stay bf16.
+#
+# Kernel arithmetic (test_f8_scores_quantized_reference): the oracle's exact
+# attention of the same e4m3 q rows over the same K codes (times kq) and the
+# bf16 V.  Only the bf16 rounding of p remains (2^-9 relative per weight, in
+# the numerator only), so every element is within 2^-8 of the largest |V|
+# the row sees, plus 2^-8 |r| and 1e-3; the log-sum-exp sums the fp32 p.
+#
+# Against the exact attention of the bf16 q and K (test_f8_scores_against_
+# exact_attention): each score moves by at most
+#     delta = sm_scale * sum_d (|dq_d| |k_d| + |q_d| |dk_d| + |dq_d| |dk_d|)
+# with |dq_d| <= 2^-4 |q_d| + 2^-10 qs and |dk_d| <= 2^-4 |k_d| + 2^-10 kq
+# (half a step of 3 mantissa bits, or of the subnormal step, qs the row's
+# scale amax/448).  Weights then move by at most a factor exp(+-delta_max)
+# each, so the output moves by at most (exp(2 delta_max) - 1) times the
+# largest |V| the row sees (plus the bf16 terms above).  Asserted with the
+# variant's relative L2 bound of 5e-2.
+# ---------------------------------------------------------------------------
+S8_CASES = {
+    "tree60_g16_bf16": W[3].replace(B=2, prefix_lo=150, prefix_hi=400, V=8, seed=71),
+    "tree16_g8_bf16_ragged": W[2].replace(B=3, prefix_lo=0, prefix_hi=1500, V=8, seed=72),
+    "chain6_g4_bf16_m24": W[1].replace(B=3, prefix_lo=700, prefix_hi=700, V=8, seed=73),
+    "tree8_g8_bf16_m64": W[2].replace(B=3, N=8, max_depth=3, prefix_lo=250, prefix_hi=600, V=8, seed=74),
+    "one_node_bf16": W[2].replace(B=3, N=1, tree="chain", prefix_lo=1, prefix_hi=200, V=8, seed=75),
+}
+_S8_RUNS = {}
+
+
+def pow2_scale(k_bits):
+    """Per kv head: the power of two kq with max |K| / kq <= 448 (float32 [Hkv])."""
+    kf = oracle.bf16_bits_to_f64(k_bits)                          # [B][Hkv][S][D]
+    amax = np.abs(kf).max(axis=(0, 2, 3))
+    e = np.ceil(np.log2(np.maximum(amax, 1e-30) / 448.0))
+    return (2.0 ** e).astype(np.float32)
+
+
+def run_s8(name, with_scale=True):
+    key = (name, with_scale)
+    if key in _S8_RUNS:
+        return _S8_RUNS[key]
+    w = S8_CASES[name]
+    x = synth.make_inputs(w, with_logits=False)
+    d = to_device(x)
+    anc, _, err = st.tree_mask_build(d["parents"])
+    qb, kb, vb = bits16(x["q"]), bits16(x["k_cache"]), bits16(x["v_cache"])
+    kq = pow2_scale(kb) if with_scale else np.ones(w.Hkv, dtype=np.float32)
+    ks = torch.from_numpy(kq).cuda() if with_scale else None
+    out, lse, err = st.tree_attn_verify_f8_scores(d["q"], d["k_cache"], d["v_cache"], d["prefix_lens"], anc,
+                                                  x["sm_scale"], ks, err=err)
+    torch.cuda.synchronize()
+    # references: the same quantized q rows and K codes; the exact attention
+    codes, qscale = oracle.quantize_rows_e4m3(oracle.bf16_bits_to_f64(qb).astype(np.float32))
+    qh = oracle.dequantize_rows_e4m3(codes, qscale)
+    kf = oracle.bf16_bits_to_f64(kb)
+    kcodes = oracle.encode_e4m3(kf / kq[None, :, None, None])
+    kh = oracle.decode_e4m3(kcodes, 1.0) * kq[None, :, None, None]
+    vf = oracle.bf16_bits_to_f64(vb)
+    ro, rl = oracle.tree_attention(qh, kh, vf, x["prefix_lens"], x["parents"], x["sm_scale"], q_fmt="f64",
+                                   kv_fmt="f64")
+    ex, _ = oracle.tree_attention(qb, kb, vb, x["prefix_lens"], x["parents"], x["sm_scale"], q_fmt="bf16",
+                                  kv_fmt="bf16")
+    vmax = np.repeat(max_visible_v(vf, x["prefix_lens"], x["parents"], w.N), w.Hq // w.Hkv, axis=2)
+    # the largest score shift each row can see (over its visible keys)
+    qf = oracle.bf16_bits_to_f64(qb)
+    g = w.Hq // w.Hkv
+    dmax = np.zeros((w.B, w.N, w.Hq))
+    for b in range(w.B):
+        A = oracle.dense_tree_mask(x["parents"][b], int(x["prefix_lens"][b]))
+        L = A.shape[1]
+        for h in range(w.Hq):
+            kvh = h // g
+            Q = np.abs(qf[b, :, h, :])                                       # [N][D]
+            K = np.abs(kf[b, kvh, :L, :])                                    # [L][D]
+            dq = 2.0 ** -4 * Q + 2.0 ** -10 * qscale[b, :, h][:, None]
+            dk = 2.0 ** -4 * K + 2.0 ** -10 * float(kq[kvh])
+            delta = x["sm_scale"] * (dq @ K.T + Q @ dk.T + dq @ dk.T)        # [N][L]
+            dmax[b, :, h] = np.where(A, delta, 0.0).max(axis=1)
+    r = (out.float().cpu().numpy(), lse.cpu().numpy(), int(err[0]), ro, rl, ex, vmax, dmax)
+    _S8_RUNS[key] = r
+    return r
+
+
+@pytest.mark.parametrize("name", list(S8_CASES))
+def test_f8_scores_quantized_reference(name):
+    w = S8_CASES[name]
+    log(f"[f8 scores, quantized reference] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} "
+        f"P=[{w.prefix_lo},{w.prefix_hi}] seed={w.seed}")
+    out, lse, err, ro, rl, ex, vmax, _ = run_s8(name)
+    assert err == 0 and np.isfinite(out).all()
+    e = np.abs(out - ro)
+    worst = float((e / (2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(ro) + 1e-3)).max())
+    rel = float(np.linalg.norm(out - ro) / np.linalg.norm(ro))
+    log(f"  max_abs={e.max():.3e} rel_l2={rel:.3e} worst/bound={worst:.3f} lse max_abs={np.abs(lse - rl).max():.3e}")
+    assert worst <= 1.0 and rel <= 1e-2, (worst, rel)
+    np.testing.assert_allclose(lse, rl, rtol=1e-4, atol=1e-3)
+
+
+@pytest.mark.parametrize("name", list(S8_CASES))
+def test_f8_scores_against_exact_attention(name):
+    w = S8_CASES[name]
+    out, lse, err, ro, rl, ex, vmax, dmax = run_s8(name)
+    assert err == 0
+    e = np.abs(out - ex)
+    bound = (np.exp(2.0 * dmax)[..., None] - 1.0) * vmax + 2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(ex) + 1e-3
+    worst = float((e / bound).max())
+    rel = float(np.linalg.norm(out - ex) / np.linalg.norm(ex))
+    log(f"[f8 scores vs exact] {name}: max_abs={e.max():.3e} rel_l2={rel:.3e} (variant bound {REL_L2}) "
+        f"worst/derived bound={worst:.3f} max score shift bound={dmax.max():.3f}")
+    assert worst <= 1.0, worst
+    assert rel <= REL_L2, rel
+
+
+def test_f8_scores_without_k_scale():
+    """No k_scale: the codes are K itself (kq = 1)."""
+    out, lse, err, ro, rl, ex, vmax, _ = run_s8("tree16_g8_bf16_ragged", with_scale=False)
+    assert err == 0
+    e = np.abs(out - ro)
+    assert float((e / (2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(ro) + 1e-3)).max()) <= 1.0
+    np.testing.assert_allclose(lse, rl, rtol=1e-4, atol=1e-3)
+
+
+def test_f8_scores_rejects_what_it_does_not_cover():
+    w = S8_CASES["chain6_g4_bf16_m24"]
+    x = synth.make_inputs(w, with_logits=False)
+    d = to_device(x)
+    anc, _, _ = st.tree_mask_build(d["parents"])
+    with pytest.raises(st.SpecError):          # an e4m3 cache goes to spec_tree_attn_verify_f8
+        st.tree_attn_verify_f8_scores(d["q"], d["k_cache"].to(torch.float8_e4m3fn), d["v_cache"],
+                                      d["prefix_lens"], anc, x["sm_scale"])
+    lib = st.lib()
+    assert lib.spec_tree_attn_verify_f8_scores(None, None, None, None, None, None, 1, 1, 1, 1, 128, 8, 0.1,
+                                               None, None, None, 0, None, None) == 1
+    q64 = torch.zeros((1, 1, 1, 64), dtype=torch.bfloat16, device="cuda")
+    kv64 = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(st.SpecError):          # D = 128 only
+        st.tree_attn_verify_f8_scores(q64, kv64, kv64, torch.zeros(1, dtype=torch.int32, device="cuda"),
+                                      torch.ones(1, dtype=torch.int64, device="cuda"), 0.125)

@@ -113,6 +113,20 @@ def test_attention_host_checks(L):
     assert _attn(L, ws=FAKE, wsb=need - 1) == SPEC_ERR_WORKSPACE
 
 
+def test_f8_scores_host_checks(L):
+    def f(q=FAKE, shape=(8, 6, 32, 8, 128, 2054), scale=0.088, ws=None, wsb=0):
+        return L.spec_tree_attn_verify_f8_scores(q, FAKE, FAKE, None, FAKE, FAKE, *shape, scale, FAKE, None, ws, wsb,
+                                                 None, None)
+    assert f(q=None) == SPEC_ERR_NULL
+    assert f(shape=(8, 6, 32, 8, 64, 2054)) == SPEC_ERR_SHAPE      # D = 128 only
+    assert f(shape=(8, 65, 32, 8, 128, 2054)) == SPEC_ERR_SHAPE
+    assert f(scale=-1.0) == SPEC_ERR_SHAPE
+    assert f(q=ctypes.c_void_p(0x1004)) == SPEC_ERR_ALIGN
+    assert f() == SPEC_ERR_WORKSPACE
+    need = L.spec_tree_attn_workspace_bytes(8, 6, 32, 8, 128, 2054)
+    assert f(ws=FAKE, wsb=need - 1) == SPEC_ERR_WORKSPACE
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(st.SpecError):

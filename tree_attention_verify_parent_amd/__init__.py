@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "SpecError", "lib", "tree_mask_build", "attn_workspace_bytes", "tree_attn_verify", "tree_attn_verify_paged",
     "vocab_argmax", "accept_walk", "commit_accepted", "verify_step", "attn_backward_workspace_bytes",
-    "tree_attn_backward", "tree_attn_verify_f8", "tree_attn_verify_f4", "verify_step_static", "DERR_ROOT",
+    "tree_attn_backward", "tree_attn_verify_f8", "tree_attn_verify_f4", "tree_attn_verify_f8_scores", "verify_step_static", "DERR_ROOT",
     "DERR_PARENT",
     "DERR_PREFIX", "DERR_TOKEN", "DERR_PATH", "DERR_PAGE", "library_path", "verify_step_workspace_bytes", "step_outputs",
 ]
@@ -33,6 +33,7 @@ _DTYPE = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16, torch.float8_e4m3f
 
 EXPORTS = ["spec_tree_mask_build", "spec_tree_attn_workspace_bytes", "spec_tree_attn_verify",
            "spec_tree_attn_verify_paged", "spec_tree_attn_verify_f8", "spec_tree_attn_verify_f4",
+           "spec_tree_attn_verify_f8_scores",
            "spec_vocab_argmax", "spec_accept_walk", "spec_commit_accepted", "spec_commit_accepted_paged",
            "spec_tree_attn_backward_workspace_bytes", "spec_tree_attn_backward", "spec_verify_step_workspace_bytes",
            "spec_verify_step", "spec_verify_step_paged", "spec_verify_step_static", "spec_status_string"]
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
     L.spec_tree_attn_verify_f8.restype = c_i
     L.spec_tree_attn_verify_f4.argtypes = L.spec_tree_attn_verify_f8.argtypes
     L.spec_tree_attn_verify_f4.restype = c_i
+    L.spec_tree_attn_verify_f8_scores.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_i, c_i, c_f,
+                                                  c_p, c_p, c_p, c_sz, c_p, c_p]
+    L.spec_tree_attn_verify_f8_scores.restype = c_i
     L.spec_vocab_argmax.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_p]
     L.spec_vocab_argmax.restype = c_i
     L.spec_accept_walk.argtypes = [c_p, c_p, c_p, c_p, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p]
@@ -227,6 +231,34 @@ def tree_attn_verify_f8(q, k_cache, v_cache, prefix_lens, anc_mask, sm_scale, k_
     err = _err_word(err, dev)
     _check(lib().spec_tree_attn_verify_f8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(prefix_lens), _ptr(anc_mask),
+        B, N, Hq, Hkv, D, S_max, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _ptr(err),
+        _stream(stream)))
+    return out, lse, err
+
+
+def tree_attn_verify_f8_scores(q, k_cache, v_cache, prefix_lens, anc_mask, sm_scale, k_scale=None, *, out=None,
+                               lse=None, want_lse=True, workspace=None, err=None, stream=None):
+    """Tree-masked attention over bf16 caches with the scores on the fp8 matrix
+    cores: q [B][N][Hq][128] and caches [B][Hkv][S_max][128] bf16; k_scale
+    (optional float32 [Hkv]) sets the power of two K is divided by before
+    rounding to e4m3.  Returns (out bf16, lse, err)."""
+    B, N, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise SpecError(f"fp8 scores take bf16 q and bf16 caches, not {q.dtype} / {k_cache.dtype}")
+    if tuple(k_cache.shape) != (B, Hkv, S_max, D) or tuple(v_cache.shape) != (B, Hkv, S_max, D):
+        raise SpecError("k_cache / v_cache must be [B][Hkv][S_max][D] matching q")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    ws_need = attn_workspace_bytes(B, N, Hq, Hkv, D, S_max)
+    if workspace is None and ws_need:
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, dev)
+    _check(lib().spec_tree_attn_verify_f8_scores(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(prefix_lens), _ptr(anc_mask),
         B, N, Hq, Hkv, D, S_max, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _ptr(err),
         _stream(stream)))
     return out, lse, err

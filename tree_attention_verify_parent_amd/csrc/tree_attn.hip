@@ -72,6 +72,12 @@ __device__ __forceinline__ int swz_f8(int row) { return ((row >> 1) & 3) | ((((r
 // the A operands of fp4 x fp8 MFMAs (q and p stay e4m3).
 constexpr int kKvF4Mma = 16 + SPEC_FP4_E2M1;
 
+// bf16 caches with the scores on the fp8 matrix cores: the workgroup turns
+// each K tile into e4m3 codes in LDS once (K divided by a per-head power of
+// two), Q is quantized per row as in the fp8 path, and S^T = K . Q^T runs on
+// the 16x16x128 e4m3 MFMA; the probabilities and V stay bf16.
+constexpr int kKvBf16F8S = 32 + SPEC_BF16;
+
 // LDS swizzle of the fp4 path (64-byte rows, 4 units): its K reads take 16
 // consecutive rows at one unit, its V transpose reads the 16 tokens
 // {16a + 4g' + r} of one contraction run; both land on distinct banks.
@@ -168,7 +174,11 @@ void tree_attn_split_kernel(
   constexpr int NW = WM * WT;
   constexpr bool F4 = (KVF == kKvF4Mma);             // fp8 arithmetic on an e2m1 cache
   constexpr bool F8 = (KVF == kKvF8Mma) || F4;       // fp8 arithmetic (e4m3 or e2m1 cache)
-  constexpr int EB = (KVF == SPEC_BF16) ? 2 : 1;     // bytes per cached element (fp4: half)
+  constexpr bool S8 = (KVF == kKvBf16F8S);          // bf16 cache, scores on the fp8 matrix cores
+  constexpr bool BF = (KVF == SPEC_BF16) || S8;      // bf16 rows in the ring
+  constexpr bool QF8 = F8 || S8;                     // Q quantized per row to e4m3
+  constexpr int EB = BF ? 2 : 1;                     // bytes per cached element (fp4: half)
+  static_assert(!S8 || D == 128, "fp8 scores over a bf16 cache: D = 128");
   static_assert(!F8 || (WT == 1 && D == 128), "the fp8 path covers whole tiles per wave, D = 128");
   constexpr int CPT = 2 / WT;                        // 32-token chunks per wave per tile
   constexpr int RBYTES = F4 ? D / 2 : D * EB;        // bytes per K/V row
@@ -192,7 +202,7 @@ void tree_attn_split_kernel(
   // ancestor masks from pa.parents itself.  They come last, so they fill the
   // CUs that the attention's workgroups leave as they finish.
   constexpr bool FUSABLE = STEP;
-  static_assert(!STEP || !F8, "the one-launch step covers bf16 / decoded-fp8 caches");
+  static_assert(!STEP || (!F8 && !S8), "the one-launch step covers bf16 / decoded-fp8 caches");
   if constexpr (FUSABLE) {
     if ((int)blockIdx.x >= attn_grid) {
       prep_block<NW * kWave, kPrepUnroll>(pa, (int)blockIdx.x - attn_grid, B, N, err_word);
@@ -206,6 +216,7 @@ void tree_attn_split_kernel(
   __shared__ int s_cum[kMaxBatch + 1];
   __shared__ uint32_t s_last;
   __shared__ int s_pages[PAGED ? kMaxPages : 1];
+  __shared__ __align__(16) unsigned char s_k8[S8 ? kTile * 128 : 16];   // e4m3 codes of the K tile
   auto kst = [&](int st) -> unsigned char* { return smem + (2 * st) * TB; };
   auto vst = [&](int st) -> unsigned char* { return smem + (2 * st + 1) * TB; };
 
@@ -418,7 +429,7 @@ void tree_attn_split_kernel(
         // 32lg .. 32lg+31 the lane quantizes for its 16x16x128 B operand
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-          qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + (F8 ? 32 * lg + 8 * c : 32 * c + 8 * lg));
+          qreg[rb][c] = *reinterpret_cast<const bf16x8_t*>(qp + (QF8 ? 32 * lg + 8 * c : 32 * c + 8 * lg));
         anc[rb] = own_masks ? 0ull : anc_mask[(size_t)b * N + i];
       } else {
 #pragma unroll
@@ -627,7 +638,10 @@ void tree_attn_split_kernel(
 
     float scale_log2 = sm_scale * kLog2e;
     float out_scale = 1.0f;
-    if constexpr (KVF != SPEC_BF16) {
+    if constexpr (S8) {
+      // K's codes are K / 2^e, e the exponent of k_scale[kvh] (1 without scales)
+      if (k_scale) scale_log2 *= __uint_as_float(__float_as_uint(k_scale[kvh]) & 0x7F800000u);
+    } else if constexpr (KVF != SPEC_BF16) {
       scale_log2 *= k_scale[kvh];
       out_scale = v_scale[kvh];
     }
@@ -697,12 +711,12 @@ void tree_attn_split_kernel(
     // fp8 arithmetic: each (node, head) row of Q as e4m3 codes with its own
     // scale amax / 448 (rows of zeros get scale 1); the four lanes of a row
     // hold a quarter each.  srow is the row's score scale in base 2.
-    i32x8_t qf8[F8 ? RB : 1];
+    i32x8_t qf8[QF8 ? RB : 1];
     float srow[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       srow[rb] = scale_log2;
-      if constexpr (F8) {
+      if constexpr (QF8) {
         float amax = 0.0f;
 #pragma unroll
         for (int c = 0; c < KC; ++c)
@@ -755,7 +769,7 @@ void tree_attn_split_kernel(
 
     // A operand of S^T = K . Q^T: lane (m = l16, lg) holds K[row][32c + 8lg .. +7]
     auto read_k = [&](const unsigned char* st, int row, int c) -> bf16x8_t {
-      if constexpr (KVF == SPEC_BF16) {
+      if constexpr (BF) {
         return *reinterpret_cast<const bf16x8_t*>(st + row * RBYTES + (((4 * c + lg) ^ swz<UPR>(row)) << 4));
       } else {
         const uint2 w = *reinterpret_cast<const uint2*>(
@@ -768,7 +782,7 @@ void tree_attn_split_kernel(
     // E and lane j receives E[j + 16k]; so lanes 4k'..4k'+3 (bf16) or 2k, 2k+1
     // (fp8) point at the 16 columns of token k.
     auto read_v = [&](const unsigned char* st, int ch, int db) -> bf16x8_t {
-      if constexpr (KVF == SPEC_BF16) {
+      if constexpr (BF) {
         i16x4_t t[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -933,6 +947,42 @@ void tree_attn_split_kernel(
       }
     };
 
+    // fp8 scores over a bf16 cache: the workgroup's waves turn the K tile of
+    // stage st into e4m3 codes in s_k8, 16 elements (one 16-byte unit of a
+    // 128-byte code row, unit u of row r at (u ^ swz<8>(r))) at a time, then
+    // meet at a barrier.  The codes are K / kq, kq the power of two of the
+    // head's k_scale (values past 448 kq become NaN: a precondition).
+    auto convert_k = [&](int stg) {
+      if constexpr (S8) {
+        constexpr int CPL = (kTile * 8) / (NW * kWave);   // 16-element units per lane
+        static_assert(CPL * NW * kWave == kTile * 8, "code units split evenly over the lanes");
+        const float kq = k_scale ? __uint_as_float(__float_as_uint(k_scale[kvh]) & 0x7F800000u) : 1.0f;
+        const unsigned char* ks = kst(stg);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const int ci = lane + kWave * (wave + NW * k);
+          const int row = ci >> 3, c8 = ci & 7;
+          typedef short s16x2_t __attribute__((ext_vector_type(2)));
+          u32x4_t wd;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const bf16x8_t x =
+                *reinterpret_cast<const bf16x8_t*>(ks + row * RBYTES + (((2 * c8 + h) ^ swz<UPR>(row)) << 4));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              s16x2_t r{0, 0};
+              r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, bf16x2_t{x[4 * j], x[4 * j + 1]}, kq, false);
+              r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, bf16x2_t{x[4 * j + 2], x[4 * j + 3]}, kq, true);
+              wd[2 * h + j] = __builtin_bit_cast(uint32_t, r);
+            }
+          }
+          *reinterpret_cast<u32x4_t*>(s_k8 + row * 128 + ((c8 ^ swz<8>(row)) << 4)) = wd;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): the codes are in LDS
+        wg_barrier();
+      }
+    };
+
     auto compute = [&](int st, int i, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value != 0;
       const unsigned char* ks = kst(st);
@@ -940,23 +990,44 @@ void tree_attn_split_kernel(
       const int t0 = t_begin + i * kTile;
       // ---- S^T = K . Q^T for this wave's chunks of the tile
       f32x4_t sacc[RB][CPT][2];
+      if constexpr (S8) {
+        // one 16x16x128 e4m3 MFMA per 16 tokens and row block: lane (m =
+        // l16, lg) holds the codes K8[row][32lg .. 32lg+31] (contraction slot
+        // 32lg + byte), rows in the chunk_token order of the bf16 path, so the
+        // accumulators come out in its layout
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int cp = 0; cp < CPT; ++cp)
-#pragma unroll
-          for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cp = 0; cp < CPT; ++cp) {
-        const int ch = wt * CPT + cp;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
+        for (int cp = 0; cp < CPT; ++cp) {
+          const int ch = wt * CPT + cp;
 #pragma unroll
           for (int G = 0; G < 2; ++G) {
-            const bf16x8_t a = read_k(ks, 32 * ch + chunk_token(G, l16), c);
+            const int row = 32 * ch + chunk_token(G, l16);
+            const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(s_k8 + row * 128 + (((2 * lg) ^ swz<8>(row)) << 4));
+            const u32x4_t a1 =
+                *reinterpret_cast<const u32x4_t*>(s_k8 + row * 128 + (((2 * lg + 1) ^ swz<8>(row)) << 4));
+            const i32x8_t a{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
+            for (int rb = 0; rb < RB; ++rb) sacc[rb][cp][G] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          }
+        }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cp = 0; cp < CPT; ++cp)
+#pragma unroll
+            for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cp = 0; cp < CPT; ++cp) {
+          const int ch = wt * CPT + cp;
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+              const bf16x8_t a = read_k(ks, 32 * ch + chunk_token(G, l16), c);
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb)
+                sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
+            }
           }
         }
       }
@@ -1051,6 +1122,7 @@ void tree_attn_split_kernel(
       }
       wg_barrier();
       if (i + NSTAGE - 1 < ntiles) issue(st == 0 ? NSTAGE - 1 : st - 1, i + NSTAGE - 1);
+      convert_k(st);
       if constexpr (F8) compute_f8(st, i, masked_tag);
       else compute(st, i, masked_tag);
       st = (st + 1 == NSTAGE) ? 0 : st + 1;
@@ -1449,7 +1521,7 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
   if constexpr (STEP) {
     pa = *prep;
     constexpr int TBB = (KVF == kKvF8Mma || KVF == kKvF4Mma ? 2 * kTile : kTile) *
-                        (KVF == kKvF4Mma ? D / 2 : D * (KVF == SPEC_BF16 ? 2 : 1));
+                        (KVF == kKvF4Mma ? D / 2 : D * (KVF == SPEC_BF16 || KVF == kKvBf16F8S ? 2 : 1));
     constexpr int PU = std::min(kPrepUnroll, (2 * TBB) / (WM * WT * kWave * 16));
     grid += plan_prep(&pa, B, N, WM * WT * kWave, attn_grid, PU);
   }
@@ -1468,10 +1540,12 @@ static void launch_split(const AttnPlan& pl, const void* q, const void* k, const
 template <int D, int KVF, int RB, int WM, int WT, int NS, bool PAGED>
 constexpr bool split_fits() {
   constexpr bool FA = (KVF == kKvF8Mma || KVF == kKvF4Mma);
-  constexpr int TB = (FA ? 2 * kTile : kTile) * (KVF == kKvF4Mma ? D / 2 : D * ((KVF == SPEC_BF16) ? 2 : 1));
+  constexpr bool S8 = (KVF == kKvBf16F8S);
+  constexpr int TB = (FA ? 2 * kTile : kTile) * (KVF == kKvF4Mma ? D / 2 : D * ((KVF == SPEC_BF16 || S8) ? 2 : 1));
   constexpr int NW = WM * WT;
   constexpr int NLOAD = TB / 1024;
-  if (NS * 2 * TB + kTableBytes + (PAGED ? 4 * kMaxPages : 0) > 160 * 1024) return false;
+  if (NS * 2 * TB + kTableBytes + (PAGED ? 4 * kMaxPages : 0) + (S8 ? kTile * 128 : 0) > 160 * 1024) return false;
+  if (S8 && (D != 128 || PAGED || (kTile * 8) % (WM * WT * kWave) != 0)) return false;
   if (NLOAD % NW != 0) return false;
   if ((NS - 1) * 2 * (NLOAD / NW) >= 64) return false;   // a full ring start fits the vmcnt counter
   if ((KVF == kKvF8Mma || KVF == kKvF4Mma) && (WT != 1 || D != 128 || PAGED)) return false;
@@ -1501,7 +1575,7 @@ static bool dispatch_shape(const AttnPlan& pl, const void* q, const void* k, con
                                                                pg, prep, st);                          \
         return true;                                                                                  \
       }                                                                                               \
-      if constexpr (KVF != kKvF8Mma && KVF != kKvF4Mma) {                                             \
+      if constexpr (KVF != kKvF8Mma && KVF != kKvF4Mma && KVF != kKvBf16F8S) {                         \
         launch_split<D, KVF, RB_, WM_, WT_, NS_, PAGED, true>(pl, q, k, v, ks, vs, pre, anc, B, N, Hq, Hkv, \
                                                               S_max, sm_scale, out, lse, po, pml, cnt, err, pg, \
                                                               prep, st);                              \
@@ -1563,6 +1637,10 @@ static spec_status run_split(const AttnPlan& pl, int kvf, const void* q, const v
   bool launched;
   if (kvf == SPEC_BF16) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_BF16) : SPEC_DISPATCH(128, SPEC_BF16);
   else if (kvf == SPEC_FP8_E4M3) launched = (D == 64) ? SPEC_DISPATCH(64, SPEC_FP8_E4M3) : SPEC_DISPATCH(128, SPEC_FP8_E4M3);
+  else if (kvf == kKvBf16F8S)
+    launched = (D == 128) && dispatch_shape<128, kKvBf16F8S, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
+                                                                     anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
+                                                                     lse, po, pml, cnt, err_word, pg, prep, stream);
   else if (kvf == kKvF8Mma)
     launched = (D == 128) && dispatch_shape<128, kKvF8Mma, false>(pl, q, k, v, k_scale, v_scale, prefix_lens,
                                                                   anc_mask, B, N, Hq, Hkv, S_max, sm_scale, out,
@@ -1721,6 +1799,22 @@ extern "C" spec_status spec_tree_attn_verify_f4(const void* q, const void* k_cac
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_ERR_ALIGN;
   pl.wt = 1;
   return run_split(pl, kKvF4Mma, q, k_cache, v_cache, k_scale, v_scale, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
+                   S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word, PagedArgs{nullptr, 0, 0, 0},
+                   stream);
+}
+
+extern "C" spec_status spec_tree_attn_verify_f8_scores(const void* q, const void* k_cache, const void* v_cache,
+                                                       const float* k_scale, const int32_t* prefix_lens,
+                                                       const uint64_t* anc_mask, int B, int N, int Hq, int Hkv, int D,
+                                                       int S_max, float sm_scale, void* out, float* lse,
+                                                       void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                                       hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !prefix_lens || !anc_mask || !out) return SPEC_ERR_NULL;
+  AttnPlan pl;
+  if (!make_plan(B, N, Hq, Hkv, D, S_max, &pl) || D != 128) return SPEC_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return SPEC_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return SPEC_ERR_ALIGN;
+  return run_split(pl, kKvBf16F8S, q, k_cache, v_cache, k_scale, nullptr, prefix_lens, anc_mask, B, N, Hq, Hkv, D,
                    S_max, sm_scale, out, lse, workspace, workspace_bytes, err_word, PagedArgs{nullptr, 0, 0, 0},
                    stream);
 }
