@@ -52,6 +52,9 @@ CASES = {
     # step); D = 64 over 320 rows with empty prefixes
     "tree60_g16_d128_rowtiles": W[3].replace(B=2, prefix_lo=150, prefix_hi=400, seed=40),
     "tree60_g16_d128_key_runs": W[3].replace(B=16, prefix_lo=200, prefix_hi=600, seed=43),
+    # three (request, kv head) sequences: the workgroup grid pads them to a multiple of 8
+    "tree20_g16_hkv1_three_seqs": W[2].replace(B=3, N=20, Hq=16, Hkv=1, max_depth=5, max_children=3, prefix_lo=30,
+                                               prefix_hi=500, seed=44),
     "tree20_g8_d128_two_tiles": W[2].replace(B=2, N=20, max_depth=5, max_children=3, prefix_lo=64,
                                              prefix_hi=700, seed=41),
     "tree40_g8_d64_three_tiles": W[2].replace(B=2, N=40, D=64, max_depth=6, max_children=4, prefix_lo=0,
