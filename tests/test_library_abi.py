@@ -168,8 +168,8 @@ def test_backward_workspace_bytes(L):
     # counter per sequence
     assert f(8, 6, 32, 8, 128, 2054) == 64 * 4 * 32 * 128 * 4 + 64 * 4
     assert f(1, 6, 4, 1, 64, 134) == 3 * 32 * 64 * 4 + 4             # 3 tiles: runs of one tile
-    # no run longer than 64 tiles: 512 sequences of 129 tiles -> 3 runs of 43
-    assert f(64, 16, 64, 8, 128, 8208) == 512 * 3 * 128 * 128 * 4 + 512 * 4
+    # no run longer than 24 tiles: 512 sequences of 129 tiles -> 6 runs of 22
+    assert f(64, 16, 64, 8, 128, 8208) == 512 * 6 * 128 * 128 * 4 + 512 * 4
     assert f(64, 16, 64, 8, 128, 64) == 0                            # one tile: dq is written directly
     # more than 128 packed rows (8 x 17 = 136): the separate dq and dK / dV passes keep no partial sums;
     # the workspace holds D and lse * log2(e) of each (request, node, head) row, 256-byte aligned each

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ prefix_lens, const uint64_t* __restrict__ anc_mask,
     const __bf16* __restrict__ out, const float* __restrict__ lse, const __bf16* __restrict__ dout,
-    int N, int Hq, int Hkv, int S_max, float sm_scale, int split_len, int n_splits,
+    int B, int N, int Hq, int Hkv, int S_max, float sm_scale, int split_len, int n_splits,
     __bf16* __restrict__ dq, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
     float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ err_word) {
   using SH = Shape<D, MP, NSTAGE>;
@@ -141,24 +141,128 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bwd_kernel(
   __shared__ __align__(16) float s_dm[MP];
   __shared__ uint64_t s_anc[MP];
   __shared__ uint32_t s_last;
+  __shared__ int s_hist[kWave];
+  __shared__ int s_pick[2];
 
-  const int seq = blockIdx.x / n_splits;
-  const int split = blockIdx.x % n_splits;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- The run this workgroup takes.  The runs of every (request, kv head)
+  // sequence are ordered longest first: all full runs (split_len tiles), in
+  // sequence order, then the partial last runs by decreasing length (ties in
+  // sequence order).  Workgroups are dispatched in id order as CUs free up,
+  // so on ragged batches this approximates a longest-first schedule.  Wave 0
+  // derives the order from the prefix lengths; a length out of range gives
+  // its request no runs (flagged once, by workgroup 0).
+  if (w == 0) {
+    const int R = split_len;
+    s_hist[lane] = 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+    auto tiles_of = [&](int bb) -> int {
+      const int pb = prefix_lens[bb];
+      if (pb < 0 || pb > S_max - N) {
+        if (blockIdx.x == 0) flag_error(err_word, SPEC_DERR_PREFIX);
+        return 0;
+      }
+      return (pb + N + kTile - 1) / kTile;
+    };
+    int F = 0;                                     // full runs in all
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const int bb = c0 + lane;
+      const int T = bb < B ? tiles_of(bb) : 0;
+      int f = T / R;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) f += __shfl_xor(f, o, kWave);
+      F += Hkv * f;
+      if (T % R) atomicAdd(&s_hist[T % R], Hkv);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const int id = (int)blockIdx.x;
+    int pick_seq = -1, pick_split = 0;
+    if (id < F) {
+      // the id-th full run: sequence order, then run order
+      int before = 0;
+      for (int c0 = 0; c0 < B && pick_seq < 0; c0 += kWave) {
+        const int bb = c0 + lane;
+        int pb = 0, f = 0;
+        if (bb < B) {
+          pb = prefix_lens[bb];
+          f = (pb < 0 || pb > S_max - N) ? 0 : ((pb + N + kTile - 1) / kTile) / R;
+        }
+        int incl = Hkv * f;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const int t = __shfl_up(incl, d);
+          if (lane >= d) incl += t;
+        }
+        const int excl = before + incl - Hkv * f;
+        const uint64_t hit = __ballot(f > 0 && excl <= id && id < before + incl);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          const int fb = __shfl(f, src), eb = __shfl(excl, src);
+          const int r = id - eb;                   // kvh-major, then run
+          pick_seq = (c0 + src) * Hkv + r / fb;
+          pick_split = r % fb;
+        }
+        before += __shfl(incl, kWave - 1);
+      }
+    } else {
+      // the k-th partial run, by decreasing length: lengths above lane's own
+      const int k = id - F;
+      const int cnt = s_hist[lane];                // runs whose partial length is lane
+      int suf = cnt;                               // suffix sum over lengths >= lane
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_down(suf, d);
+        if (lane + d < kWave) suf += t;
+      }
+      const int above = suf - cnt;                 // runs with a longer partial length
+      const uint64_t in = __ballot(cnt > 0 && above <= k && k < above + cnt);
+      if (in) {
+        const int len = __builtin_ctzll(in);       // the partial length that holds rank k
+        const int kk = k - __shfl(above, len);     // rank among runs of that length
+        const int nb = kk / Hkv;                   // the nb-th request with that partial length
+        int seen = 0;
+        for (int c0 = 0; c0 < B && pick_seq < 0; c0 += kWave) {
+          const int bb = c0 + lane;
+          int T = 0;
+          if (bb < B) {
+            const int pb = prefix_lens[bb];
+            T = (pb < 0 || pb > S_max - N) ? 0 : (pb + N + kTile - 1) / kTile;
+          }
+          const uint64_t m = __ballot(bb < B && T % R == len);
+          const int c = __popcll(m);
+          if (nb < seen + c) {
+            // the (nb - seen)-th set bit of m
+            uint64_t mm = m;
+            for (int j = 0; j < nb - seen; ++j) mm &= mm - 1;
+            const int src = __builtin_ctzll(mm);
+            const int Tb = __shfl(T, src);
+            pick_seq = (c0 + src) * Hkv + kk % Hkv;
+            pick_split = Tb / R;
+          }
+          seen += c;
+        }
+      }
+    }
+    if (lane == 0) {
+      s_pick[0] = pick_seq;
+      s_pick[1] = pick_split;
+    }
+  }
+  __syncthreads();
+  const int seq = s_pick[0];
+  if (seq < 0) return;                             // past the last run
+  const int split = s_pick[1];
   const int b = seq / Hkv;
   const int kvh = seq % Hkv;
   const int g = Hq / Hkv;
   const int M = g * N;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
-  const int P = prefix_lens[b];
-  if (P < 0 || P > S_max - N) {
-    if (split == 0 && kvh == 0 && tid == 0) flag_error(err_word, SPEC_DERR_PREFIX);
-    return;
-  }
+  const int P = prefix_lens[b];                    // in range: the pick skips the others
   const int L = P + N;
   const int T = (L + kTile - 1) / kTile;           // tiles of the sequence
   const int n_act = (T + split_len - 1) / split_len;   // runs with work
@@ -694,10 +798,13 @@ struct BwdPlan {
 
 // Runs of tiles, sized from the largest possible sequence (S_max keys): at
 // least one workgroup per CU (a workgroup fills a CU's LDS), and no run
-// longer than kMaxRun tiles, which bounds the imbalance when prefix lengths
-// differ.  Longer runs pay the prologue and the dq merge less often.
+// longer than kMaxRun tiles, which bounds the tail of the longest-first
+// schedule when prefix lengths differ.  Longer runs pay the prologue and the
+// dq merge less often: at 16-node trees over 512..8192-token prefixes, 64
+// gave 397 us, 32 388 us and 24 375 us (and 345 / 354 / 355 us with every
+// prefix at the mean length).
 constexpr int kCUs = 256;
-constexpr int kMaxRun = 64;
+constexpr int kMaxRun = 24;
 
 static bool make_bwd_plan(int B, int N, int Hq, int Hkv, int D, int S_max, BwdPlan* p) {
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hkv < 1 || Hq < 1 || Hq % Hkv) return false;
@@ -740,8 +847,8 @@ static void launch_bwd(const BwdPlan& pl, const void* q, const void* k, const vo
   const unsigned grid = (unsigned)(B * Hkv) * (unsigned)pl.n_splits;
   hipLaunchKernelGGL((tree_attn_bwd_kernel<D, MP, NS>), dim3(grid), dim3(kThreads), 0, st,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                     pre, anc, static_cast<const __bf16*>(out), lse, static_cast<const __bf16*>(dout), N, Hq, Hkv,
-                     S_max, sm_scale, pl.split_len, pl.n_splits, static_cast<__bf16*>(dq),
+                     pre, anc, static_cast<const __bf16*>(out), lse, static_cast<const __bf16*>(dout), B, N, Hq,
+                     Hkv, S_max, sm_scale, pl.split_len, pl.n_splits, static_cast<__bf16*>(dq),
                      static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), part, cnt, err);
 }
 
