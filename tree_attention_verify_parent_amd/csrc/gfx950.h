@@ -101,6 +101,19 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
                : "memory", "m0");
 }
+// The same with a wave-uniform global base (held in SGPRs) and a 32-bit lane
+// offset: the saddr form of the DMA, which needs no 64-bit per-lane address
+// arithmetic.  Lane l's 16 bytes come from sbase + voff.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = (uint64_t)sbase;
+  // the builtin returns int: take each half back as unsigned before widening
+  // (a sign-extended low half would corrupt the upper address bits)
+  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bu), "s"(lds_addr)
+               : "memory", "m0");
+}
 // LDS byte address of a __shared__ object (the cast of the object itself
 // folds to a constant; callers add byte offsets to it)
 #define LDS_ADDR(obj) ((uint32_t)(size_t)(lds_void_t*)(obj))

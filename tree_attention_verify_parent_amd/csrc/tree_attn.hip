@@ -144,6 +144,13 @@ struct SplitOccupancy {
 // end of its (request, kv head) sequence: a unit boundary that would leave a
 // shorter remainder moves to that end.
 constexpr int kMinPiece = 128;
+// K and V operand fragments a wave keeps in flight: the tile loop reads them
+// in batches, the next batch's reads issued before the current batch's
+// products (ds_read latency is otherwise exposed on every fragment).
+constexpr int kFragBatch = 4;
+// How far (base 2) a row's running max may rise above the reference max the
+// row's p = 2^(s - m) are taken against before the reference moves.
+constexpr float kMaxLag = 8.0f;
 // Requests per launch: every workgroup keeps a table of their lengths in LDS.
 constexpr int kMaxBatch = 1024;
 // Paged caches: a workgroup stages the page ids of its current piece in LDS.
@@ -360,6 +367,27 @@ void tree_attn_split_kernel(
   // Hkv * RBYTES bytes per token.
   auto dma_tile = [&](const unsigned char* kbase, const unsigned char* vbase, int t0, int t_end, int st,
                       int wave, int lane, int pg0) {
+    if constexpr (!PAGED) {
+      if (t0 + TILE <= t_end) {
+        // a whole tile: the wave-uniform tile base in SGPRs, the lane's 32-bit
+        // offset in a VGPR (no per-lane 64-bit address arithmetic)
+        const unsigned char* kt = kbase + (size_t)t0 * RBYTES;
+        const unsigned char* vt = vbase + (size_t)t0 * RBYTES;
+#pragma unroll
+        for (int qd = 0; qd < KPW; ++qd) {
+          const int j = wave + qd * NW;
+          const int row = j * RPI + lane / UPR;
+          int sw;
+          if constexpr (F4) sw = swz_f4(row);
+          else if constexpr (F8) sw = swz_f8(row);
+          else sw = swz<UPR>(row);
+          const uint32_t lo = (uint32_t)(row * RBYTES + ((lane % UPR) ^ sw) * 16);
+          dma16s(kt, lo, LDS_ADDR(smem) + (2 * st) * TB + j * 1024);
+          dma16s(vt, lo, LDS_ADDR(smem) + (2 * st + 1) * TB + j * 1024);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int qd = 0; qd < KPW; ++qd) {
       const int j = wave + qd * NW;
@@ -1016,20 +1044,36 @@ void tree_attn_split_kernel(
           for (int cp = 0; cp < CPT; ++cp)
 #pragma unroll
             for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // K fragments (cp, c, G) in batches: batch j+1's reads go out before
+        // batch j's products, so each wave keeps PFB fragments in flight
+        constexpr int NF = CPT * KC * 2;
+        constexpr int PFB = NF < kFragBatch ? NF : kFragBatch;
+        static_assert(NF % PFB == 0, "whole batches");
+        bf16x8_t ka[NF];
+        auto kread = [&](int f) {
+          const int cp = f / (KC * 2), c = (f / 2) % KC, G = f % 2;
+          ka[f] = read_k(ks, 32 * (wt * CPT + cp) + chunk_token(G, l16), c);
+        };
+        auto kmma = [&](int f) {
+          const int cp = f / (KC * 2), c = (f / 2) % KC, G = f % 2;
 #pragma unroll
-        for (int cp = 0; cp < CPT; ++cp) {
-          const int ch = wt * CPT + cp;
+          for (int rb = 0; rb < RB; ++rb)
+            sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[f], qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
+        };
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int c = 0; c < KC; ++c) {
+        for (int f = 0; f < PFB; ++f) kread(f);
 #pragma unroll
-            for (int G = 0; G < 2; ++G) {
-              const bf16x8_t a = read_k(ks, 32 * ch + chunk_token(G, l16), c);
+        for (int j = 0; j < NF / PFB; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (j + 1 < NF / PFB) {
 #pragma unroll
-              for (int rb = 0; rb < RB; ++rb)
-                sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
-            }
+            for (int f = 0; f < PFB; ++f) kread((j + 1) * PFB + f);
           }
+#pragma unroll
+          for (int f = 0; f < PFB; ++f) kmma(j * PFB + f);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- mask, online softmax (base 2), P in bf16
@@ -1060,9 +1104,16 @@ void tree_attn_split_kernel(
             }
         mx = row4_max(mx) * srow[rb];
         const float m_new = fmaxf(m_run[rb], mx);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        alpha[rb] = fast_exp2(m_run[rb] - m_use);
-        m_run[rb] = m_new;
+        // the reference max moves only when the tile's max passes it by more
+        // than 8 (base 2): p then stays at most 2^8, which bf16 and the fp32
+        // sums hold exactly as well as p <= 1, and O, l and m stay
+        // consistent, so the result is the same softmax; O is rescaled on
+        // about the first tile only
+        const bool bump = m_new > m_run[rb] + kMaxLag;
+        const float m_keep = bump ? m_new : m_run[rb];
+        const float m_use = (m_keep == -INFINITY) ? 0.0f : m_keep;
+        alpha[rb] = bump ? fast_exp2(m_run[rb] - m_use) : 1.0f;
+        m_run[rb] = m_keep;
         // p = 2^(s*scale - m) with one fma; the row sum (for the output's
         // normalisation and the exact log-sum-exp) is over the fp32 p
         float lsum = 0.0f;
@@ -1078,9 +1129,7 @@ void tree_attn_split_kernel(
             }
         l_run[rb] = l_run[rb] * alpha[rb] + lsum;
       }
-      // rescale O only when some row's running max moved (alpha != 1): after the
-      // first tiles that is rare, and skipping a multiply by exactly 1 changes
-      // nothing
+      // rescale O only when some row's reference max moved (alpha != 1)
       bool moved = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) moved |= (alpha[rb] != 1.0f);
@@ -1091,15 +1140,29 @@ void tree_attn_split_kernel(
           for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
       }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- O^T += V^T . P^T
-#pragma unroll
-      for (int cp = 0; cp < CPT; ++cp) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8_t a = read_v(vs, wt * CPT + cp, db);
+      // ---- O^T += V^T . P^T, V fragments (cp, db) in batches as K's
+      {
+        constexpr int NF = CPT * DB;
+        constexpr int PFB = NF < kFragBatch ? NF : kFragBatch;
+        static_assert(NF % PFB == 0, "whole batches");
+        bf16x8_t va[NF];
+        auto vread = [&](int f) { va[f] = read_v(vs, wt * CPT + f / DB, f % DB); };
+        auto vmma = [&](int f) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
-            oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb][cp], oacc[rb][db], 0, 0, 0);
+            oacc[rb][f % DB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pb[rb][f / DB], oacc[rb][f % DB], 0, 0, 0);
+        };
+#pragma unroll
+        for (int f = 0; f < PFB; ++f) vread(f);
+#pragma unroll
+        for (int j = 0; j < NF / PFB; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (j + 1 < NF / PFB) {
+#pragma unroll
+            for (int f = 0; f < PFB; ++f) vread((j + 1) * PFB + f);
+          }
+#pragma unroll
+          for (int f = 0; f < PFB; ++f) vmma(j * PFB + f);
         }
       }
     };
@@ -1107,6 +1170,26 @@ void tree_attn_split_kernel(
     // ring: wait for tile i (the tiles after it stay in flight), make it visible
     // to all waves, refill the stage tile i-1 used, compute tile i
     int st = 0;
+    // the ring stage is a compile-time constant in the unrolled plain loop
+    // (LDS addresses then take it as an immediate offset)
+    auto tile_step_c = [&](int i, auto masked_tag, auto stage_tag) {
+      constexpr int sc = decltype(stage_tag)::value;
+      const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
+      if (i >= NSTAGE - 1) switch (ahead) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1 * PT>(); break;
+        case 2: if constexpr (NSTAGE > 3) wait_vmcnt<2 * PT>(); break;
+        case 3: if constexpr (NSTAGE > 4) wait_vmcnt<3 * PT>(); break;
+        case 4: if constexpr (NSTAGE > 5) wait_vmcnt<4 * PT>(); break;
+        case 5: if constexpr (NSTAGE > 6) wait_vmcnt<5 * PT>(); break;
+        default: if constexpr (NSTAGE > 7) wait_vmcnt<6 * PT>(); break;
+      }
+      wg_barrier();
+      if (i + NSTAGE - 1 < ntiles) issue(sc == 0 ? NSTAGE - 1 : sc - 1, i + NSTAGE - 1);
+      convert_k(sc);
+      if constexpr (F8) compute_f8(sc, i, masked_tag);
+      else compute(sc, i, masked_tag);
+    };
     auto tile_step = [&](int i, auto masked_tag) {
       const int ahead = min(NSTAGE - 2, ntiles - 1 - i);
       // tiles 0 .. NSTAGE-2 went out before the loads' wait above and have
@@ -1131,7 +1214,15 @@ void tree_attn_split_kernel(
     // masked ones (tree rows, the piece's ragged end) after them: two loops,
     // so the plain loop holds none of the masked path's registers.
     const int n_plain = __builtin_amdgcn_readfirstlane(max(0, min(ntiles, (min(P, t_end) - t_begin) / TILE)));
-    for (int i = 0; i < n_plain; ++i) tile_step(i, Int<0>{});
+    const int n_unr = n_plain - n_plain % NSTAGE;
+    for (int i = 0; i < n_unr; i += NSTAGE) {
+      tile_step_c(i, Int<0>{}, Int<0>{});
+      tile_step_c(i + 1, Int<0>{}, Int<1>{});
+      if constexpr (NSTAGE > 2) tile_step_c(i + 2, Int<0>{}, Int<2 % NSTAGE>{});
+      if constexpr (NSTAGE > 3) tile_step_c(i + 3, Int<0>{}, Int<3 % NSTAGE>{});
+    }
+    static_assert(NSTAGE <= 4, "the plain loop unrolls up to 4 stages");
+    for (int i = n_unr; i < n_plain; ++i) tile_step(i, Int<0>{});
     for (int i = n_plain; i < ntiles; ++i) tile_step(i, Int<1>{});
     // ---- waves that split the tile's tokens combine their states in LDS
     if constexpr (WT == 2) {
