@@ -1023,19 +1023,21 @@ void tree_attn_split_kernel(
         // l16, lg) holds the codes K8[row][32lg .. 32lg+31] (contraction slot
         // 32lg + byte), rows in the chunk_token order of the bf16 path, so the
         // accumulators come out in its layout
+        // the CPT * 2 code fragments (cp, G): all reads first, then the products
+        u32x4_t a0[CPT * 2], a1[CPT * 2];
 #pragma unroll
-        for (int cp = 0; cp < CPT; ++cp) {
-          const int ch = wt * CPT + cp;
+        for (int f = 0; f < CPT * 2; ++f) {
+          const int row = 32 * (wt * CPT + f / 2) + chunk_token(f % 2, l16);
+          a0[f] = *reinterpret_cast<const u32x4_t*>(s_k8 + row * 128 + (((2 * lg) ^ swz<8>(row)) << 4));
+          a1[f] = *reinterpret_cast<const u32x4_t*>(s_k8 + row * 128 + (((2 * lg + 1) ^ swz<8>(row)) << 4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int G = 0; G < 2; ++G) {
-            const int row = 32 * ch + chunk_token(G, l16);
-            const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(s_k8 + row * 128 + (((2 * lg) ^ swz<8>(row)) << 4));
-            const u32x4_t a1 =
-                *reinterpret_cast<const u32x4_t*>(s_k8 + row * 128 + (((2 * lg + 1) ^ swz<8>(row)) << 4));
-            const i32x8_t a{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        for (int f = 0; f < CPT * 2; ++f) {
+          const i32x8_t a{(int)a0[f][0], (int)a0[f][1], (int)a0[f][2], (int)a0[f][3],
+                          (int)a1[f][0], (int)a1[f][1], (int)a1[f][2], (int)a1[f][3]};
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) sacc[rb][cp][G] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
-          }
+          for (int rb = 0; rb < RB; ++rb) sacc[rb][f / 2][f % 2] = mfma_f8(a, qf8[rb], f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
       } else {
 #pragma unroll
@@ -1079,6 +1081,11 @@ void tree_attn_split_kernel(
       // ---- mask, online softmax (base 2), P in bf16
       bf16x8_t pb[RB][CPT];
       float alpha[RB];
+      // each lane's max over its raw scores (the scale is positive, so it
+      // keeps the order and commutes with the max exactly), masked tokens to
+      // -inf
+      float mxl[RB];
+      bool over = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         // this lane's 8 tokens of chunk cp sit at bits 32*ch + 8*lg .. +7
@@ -1088,8 +1095,6 @@ void tree_attn_split_kernel(
 #pragma unroll
           for (int cp = 0; cp < CPT; ++cp) vis8[cp] = (uint32_t)(vis >> (32 * (wt * CPT + cp) + 8 * lg)) & 0xFFu;
         }
-        // max over the raw scores (the scale is positive, so it keeps the order
-        // and commutes with the max exactly), masked tokens to -inf
         float mx = -INFINITY;
 #pragma unroll
         for (int cp = 0; cp < CPT; ++cp)
@@ -1102,18 +1107,28 @@ void tree_attn_split_kernel(
               sacc[rb][cp][G][r] = s;
               mx = fmaxf(mx, s);
             }
-        mx = row4_max(mx) * srow[rb];
-        const float m_new = fmaxf(m_run[rb], mx);
-        // the reference max moves only when the tile's max passes it by more
-        // than 8 (base 2): p then stays at most 2^8, which bf16 and the fp32
-        // sums hold exactly as well as p <= 1, and O, l and m stay
-        // consistent, so the result is the same softmax; O is rescaled on
-        // about the first tile only
-        const bool bump = m_new > m_run[rb] + kMaxLag;
-        const float m_keep = bump ? m_new : m_run[rb];
-        const float m_use = (m_keep == -INFINITY) ? 0.0f : m_keep;
-        alpha[rb] = bump ? fast_exp2(m_run[rb] - m_use) : 1.0f;
-        m_run[rb] = m_keep;
+        mxl[rb] = mx;
+        over = over || (mx * srow[rb] > m_run[rb] + kMaxLag);
+      }
+      // The reference max of a row moves only when the tile's max passes it
+      // by more than kMaxLag (base 2): p then stays at most 2^8, which bf16
+      // and the fp32 sums hold exactly as well as p <= 1, and O, l and m stay
+      // consistent, so the result is the same softmax; O is rescaled on about
+      // the first tile only.  No lane's own max passing its row's reference
+      // means no row's max does (the row max is the largest lane max), so the
+      // cross-lane reduction runs only when some lane's does.
+      const bool any_over = __any(over);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        alpha[rb] = 1.0f;
+        if (any_over) {
+          const float m_new = fmaxf(m_run[rb], row4_max(mxl[rb]) * srow[rb]);
+          const bool bump = m_new > m_run[rb] + kMaxLag;
+          const float m_keep = bump ? m_new : m_run[rb];
+          alpha[rb] = bump ? fast_exp2(m_run[rb] - ((m_keep == -INFINITY) ? 0.0f : m_keep)) : 1.0f;
+          m_run[rb] = m_keep;
+        }
+        const float m_use = (m_run[rb] == -INFINITY) ? 0.0f : m_run[rb];
         // p = 2^(s*scale - m) with one fma; the row sum (for the output's
         // normalisation and the exact log-sum-exp) is over the fp32 p
         float lsum = 0.0f;
