@@ -41,6 +41,9 @@ constexpr int kRowsDq = kWavesDq * 2 * 16;         // packed rows per dq workgro
 constexpr int kWavesKv = 8;
 constexpr int kKeysKv = kWavesKv * 16;             // keys per dK / dV tile
 constexpr int kRowStep = 64;                       // packed rows per streamed step of the dK / dV pass
+// operand fragments a wave keeps in flight: the product loops read them in
+// batches, the next batch's reads issued before the current batch's products
+constexpr int kFragBatch = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- dq pass: K / V tiles, row-major with XOR-swizzled 16-byte units.  The
@@ -245,19 +248,36 @@ void tree_attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restr
           sacc[rb][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           pacc[rb][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-#pragma unroll
-        for (int G = 0; G < 2; ++G) {
-          const int krow = 32 * cp + chunk_key(G, l16);
-          const bf16x8_t ak = read_unit<RBYTES>(ks, krow, 4 * c + lg, swz);
-          const bf16x8_t av = read_unit<RBYTES>(vs, krow, 4 * c + lg, swz);
+      {
+        constexpr int NF = KC * 2 * 2, PB = kFragBatch;
+        bf16x8_t fr[NF];
+        auto rd = [&](int x) {
+          const int c = x / 4, G = (x / 2) % 2;
+          fr[x] = read_unit<RBYTES>((x & 1) ? vs : ks, 32 * cp + chunk_key(G, l16), 4 * c + lg, swz);
+        };
+        auto mm = [&](int x) {
+          const int c = x / 4, G = (x / 2) % 2;
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            sacc[rb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[rb][c], sacc[rb][G], 0, 0, 0);
-            pacc[rb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, doreg[rb][c], pacc[rb][G], 0, 0, 0);
+            if (x & 1) pacc[rb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], doreg[rb][c], pacc[rb][G], 0, 0, 0);
+            else sacc[rb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], qreg[rb][c], sacc[rb][G], 0, 0, 0);
           }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < PB; ++x) rd(x);
+#pragma unroll
+        for (int jb = 0; jb < NF / PB; ++jb) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (jb + 1 < NF / PB) {
+#pragma unroll
+            for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
+          }
+#pragma unroll
+          for (int x = 0; x < PB; ++x) mm(jb * PB + x);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // p and ds in registers, ds in bf16 as the dq product's B operand
       bf16x8_t dsb[RB];
 #pragma unroll
@@ -274,20 +294,39 @@ void tree_attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restr
           }
       }
       // dq^T += K^T . dS^T over the chunk's keys
+      {
+        constexpr int PB = kFragBatch < DB ? kFragBatch : DB;
+        bf16x8_t fr[DB];
+        auto rd = [&](int db) {
+          i16x4_t t[2];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        i16x4_t t[2];
+          for (int h = 0; h < 2; ++h) {
+            const int row = 32 * cp + 8 * lg + 4 * h + (l16 >> 2);
+            const int u = 2 * db + ((l16 >> 1) & 1);
+            const int off = row * RBYTES + ((u ^ kv_swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
+            t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(ks + off));
+          }
+          fr[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        auto mm = [&](int db) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 32 * cp + 8 * lg + 4 * h + (l16 >> 2);
-          const int u = 2 * db + ((l16 >> 1) & 1);
-          const int off = row * RBYTES + ((u ^ kv_swz<UPR>(row)) << 4) + ((l16 & 1) << 3);
-          t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(ks + off));
+          for (int rb = 0; rb < RB; ++rb)
+            dqacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[db], dsb[rb], dqacc[rb][db], 0, 0, 0);
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < PB; ++x) rd(x);
+#pragma unroll
+        for (int jb = 0; jb < DB / PB; ++jb) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (jb + 1 < DB / PB) {
+#pragma unroll
+            for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
+          }
+#pragma unroll
+          for (int x = 0; x < PB; ++x) mm(jb * PB + x);
         }
-        const bf16x8_t akt = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          dqacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akt, dsb[rb], dqacc[rb][db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -423,24 +462,50 @@ void tree_attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __res
       sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       pacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    {
+      // fragments (c, mb, Q or dO) in batches of PB, the next batch's reads
+      // issued before the current batch's products
+      constexpr int NF = KC * MB * 2, PB = kFragBatch;
+      bf16x8_t fr[NF];
+      auto rd = [&](int x) {
+        const int c = x / (MB * 2), mb = (x / 2) % MB;
+        fr[x] = read_unit<RBYTES>((x & 1) ? sdo : sq, 16 * mb + l16, 4 * c + lg, swz);
+      };
+      auto mm = [&](int x) {
+        const int c = x / (MB * 2), mb = (x / 2) % MB;
+        if (x & 1) pacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], vf[c], pacc[mb], 0, 0, 0);
+        else sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], kf[c], sacc[mb], 0, 0, 0);
+      };
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
+      for (int x = 0; x < PB; ++x) rd(x);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_unit<RBYTES>(sq, 16 * mb + l16, 4 * c + lg, swz),
-                                                           kf[c], sacc[mb], 0, 0, 0);
-        pacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_unit<RBYTES>(sdo, 16 * mb + l16, 4 * c + lg, swz),
-                                                           vf[c], pacc[mb], 0, 0, 0);
+      for (int jb = 0; jb < NF / PB; ++jb) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (jb + 1 < NF / PB) {
+#pragma unroll
+          for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
+        }
+#pragma unroll
+        for (int x = 0; x < PB; ++x) mm(jb * PB + x);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // ---- p and ds of rows 16mb + 4lg + r at this lane's key; K-slot t of
     // k-step s holds row 32s + 4lg + t (t < 4) or 32s + 16 + 4lg + t - 4
     const int key = kt * kKeysKv + 16 * w + l16;
     const int j = key - P;                         // tree node of the key, if >= 0
     bf16x8_t pb[KS], dsb[KS];
+    f32x4_t l2s[MB], dms[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const f32x4_t l2 = *reinterpret_cast<const f32x4_t*>(s_l2 + 16 * mb + 4 * lg);
-      const f32x4_t dmv = *reinterpret_cast<const f32x4_t*>(s_dm + 16 * mb + 4 * lg);
+      l2s[mb] = *reinterpret_cast<const f32x4_t*>(s_l2 + 16 * mb + 4 * lg);
+      dms[mb] = *reinterpret_cast<const f32x4_t*>(s_dm + 16 * mb + 4 * lg);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const f32x4_t l2 = l2s[mb];
+      const f32x4_t dmv = dms[mb];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = fast_exp2(__builtin_fmaf(sacc[mb][r], scale_log2, -l2[r]));
@@ -454,15 +519,34 @@ void tree_attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __res
       }
     }
     // ---- dV^T += dO^T . P and dK^T += Q^T . dS (rows d, column = key)
+    {
+      // fragments (s, db, dO or Q), two transpose reads each, batched as above
+      constexpr int NF = KS * DB * 2, PB = kFragBatch;
+      bf16x8_t fr[NF];
+      auto rd = [&](int x) {
+        const int sx = x / (DB * 2), db = (x / 2) % DB;
+        fr[x] = read_cols<RBYTES>((x & 1) ? sq : sdo, 32 * sx + 4 * lg, 32 * sx + 16 + 4 * lg, db, l16, swz);
+      };
+      auto mm = [&](int x) {
+        const int sx = x / (DB * 2), db = (x / 2) % DB;
+        if (x & 1) dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], dsb[sx], dkacc[db], 0, 0, 0);
+        else dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], pb[sx], dvacc[db], 0, 0, 0);
+      };
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+      for (int x = 0; x < PB; ++x) rd(x);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            read_cols<RBYTES>(sdo, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db, l16, swz), pb[s], dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            read_cols<RBYTES>(sq, 32 * s + 4 * lg, 32 * s + 16 + 4 * lg, db, l16, swz), dsb[s], dkacc[db], 0, 0, 0);
+      for (int jb = 0; jb < NF / PB; ++jb) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (jb + 1 < NF / PB) {
+#pragma unroll
+          for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
+        }
+#pragma unroll
+        for (int x = 0; x < PB; ++x) mm(jb * PB + x);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   for (int f = 0; f < F; ++f) {
