@@ -52,6 +52,8 @@ CASES = {
     "tree64_g2_fp8_deep": W[4].replace(B=2, N=64, Hq=4, Hkv=2, max_depth=30, max_children=2, prefix_lo=0,
                                        prefix_hi=130, V=8, seed=65),
     "one_node_fp8": W[4].replace(B=3, N=1, tree="chain", prefix_lo=1, prefix_hi=200, V=8, seed=66),
+    # 960 packed rows: the 8-wave, 256-row plan
+    "tree60_g16_fp8_m960": W[3].replace(B=2, kv_dtype="e4m3", prefix_lo=150, prefix_hi=700, V=8, seed=67),
 }
 
 

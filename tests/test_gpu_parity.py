@@ -28,6 +28,9 @@ SMALL = {
     "tree16_ragged_bf16": W[2].replace(B=4, prefix_lo=100, prefix_hi=1500, V=5003, seed=12),
     "tree60_bf16": W[3].replace(B=2, prefix_lo=777, prefix_hi=777, V=4099, seed=13),
     "tree16_fp8kv": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=6000, seed=14),
+    # 960 packed rows (the 8-wave, 256-row plan): ragged prefixes, and an e4m3 cache
+    "tree60_ragged_bf16": W[3].replace(B=3, prefix_lo=90, prefix_hi=1900, V=3001, seed=15),
+    "tree60_fp8kv": W[3].replace(B=2, kv_dtype="e4m3", prefix_lo=600, prefix_hi=600, V=3001, seed=16),
 }
 
 
