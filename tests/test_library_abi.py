@@ -55,6 +55,12 @@ def test_workspace_bytes_is_pure_and_rejects_bad_shapes(L):
     # 256 units of one 32-row tile for M = 24; 512 units of one 128-row tile for M = 128
     assert f(8, 6, 32, 8, 128, 2054) == 2 * 256 * 32 * (128 * 4 + 8) + 8 * 8 * 4
     assert f(64, 16, 64, 8, 128, 4112) == 2 * 512 * 128 * (128 * 4 + 8) + 64 * 8 * 4
+    # M = 960 (an even number of 128-row tiles): one 8-wave workgroup a CU over 256-row tiles, so 4 M-tiles,
+    # 64 units of one split each, slots for 2 per unit
+    assert f(16, 60, 64, 4, 128, 32828) == 2 * 64 * 1024 * (128 * 4 + 8) + 64 * 4 * 4
+    # M = 376 (three 128-row tiles, which 256-row tiles would pad to 512): the 4-wave plan, 512 // 3 units
+    # of 3 splits (a sequence of 33 tiles), two slots per unit
+    assert f(8, 47, 64, 8, 128, 2054) == 2 * (512 // 3) * 384 * (128 * 4 + 8) + 64 * 3 * 4
     assert f(1024, 6, 32, 8, 128, 2 ** 21 - 1) > 0
     for bad in [(0, 6, 32, 8, 128, 2054), (8, 0, 32, 8, 128, 2054), (8, 65, 32, 8, 128, 2054),
                 (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 96, 2054), (8, 6, 32, 8, 128, 5),
