@@ -32,8 +32,8 @@ import sqlite3
 import sys
 
 SHORT = ("tree_attn_split_kernel", "tree_attn_f32_kernel", "vocab_argmax_kernel", "accept_walk_kernel",
-         "tree_mask_build_kernel", "commit_accepted_kernel", "tree_attn_bwd_kernel", "tree_attn_bwd_f32_dq_kernel",
-         "tree_attn_bwd_f32_dkv_kernel")
+         "tree_mask_build_kernel", "commit_accepted_kernel", "tree_attn_bwd_kernel", "tree_attn_bwd_f32_kernel",
+         "tree_attn_bwd_dq_kernel", "tree_attn_bwd_dkdv_kernel", "bwd_rowstat_kernel")
 
 
 def _mangled_args(tail: str) -> str:
