@@ -114,6 +114,29 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bu), "s"(lds_addr)
                : "memory", "m0");
 }
+// NF operand fragments read in batches of PB: batch j+1's reads are issued
+// before batch j's products, so PB fragments stay in flight.  rd(x) issues the
+// LDS reads of fragment x and mm(x) its products; scheduling barriers pin that
+// order (left to itself the compiler issues each fragment's read right before
+// its products and waits for it).
+template <int NF, int PB, typename R, typename F>
+__device__ __forceinline__ void batched_products(R rd, F mm) {
+  static_assert(NF % PB == 0, "whole batches");
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int x = 0; x < PB; ++x) rd(x);
+#pragma unroll
+  for (int j = 0; j < NF / PB; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < NF / PB) {
+#pragma unroll
+      for (int x = 0; x < PB; ++x) rd((j + 1) * PB + x);
+    }
+#pragma unroll
+    for (int x = 0; x < PB; ++x) mm(j * PB + x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
 // LDS byte address of a __shared__ object (the cast of the object itself
 // folds to a constant; callers add byte offsets to it)
 #define LDS_ADDR(obj) ((uint32_t)(size_t)(lds_void_t*)(obj))

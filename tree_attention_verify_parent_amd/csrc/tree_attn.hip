@@ -1046,36 +1046,20 @@ void tree_attn_split_kernel(
           for (int cp = 0; cp < CPT; ++cp)
 #pragma unroll
             for (int G = 0; G < 2; ++G) sacc[rb][cp][G] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // K fragments (cp, c, G) in batches: batch j+1's reads go out before
-        // batch j's products, so each wave keeps PFB fragments in flight
+        // K fragments (cp, c, G), kFragBatch in flight
         constexpr int NF = CPT * KC * 2;
-        constexpr int PFB = NF < kFragBatch ? NF : kFragBatch;
-        static_assert(NF % PFB == 0, "whole batches");
         bf16x8_t ka[NF];
-        auto kread = [&](int f) {
-          const int cp = f / (KC * 2), c = (f / 2) % KC, G = f % 2;
-          ka[f] = read_k(ks, 32 * (wt * CPT + cp) + chunk_token(G, l16), c);
-        };
-        auto kmma = [&](int f) {
-          const int cp = f / (KC * 2), c = (f / 2) % KC, G = f % 2;
+        batched_products<NF, (NF < kFragBatch ? NF : kFragBatch)>(
+            [&](int f) {
+              const int cp = f / (KC * 2), c = (f / 2) % KC, G = f % 2;
+              ka[f] = read_k(ks, 32 * (wt * CPT + cp) + chunk_token(G, l16), c);
+            },
+            [&](int f) {
+              const int cp = f / (KC * 2), c = (f / 2) % KC, G = f % 2;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[f], qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
-        };
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int f = 0; f < PFB; ++f) kread(f);
-#pragma unroll
-        for (int j = 0; j < NF / PFB; ++j) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (j + 1 < NF / PFB) {
-#pragma unroll
-            for (int f = 0; f < PFB; ++f) kread((j + 1) * PFB + f);
-          }
-#pragma unroll
-          for (int f = 0; f < PFB; ++f) kmma(j * PFB + f);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+              for (int rb = 0; rb < RB; ++rb)
+                sacc[rb][cp][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[f], qreg[rb][c], sacc[rb][cp][G], 0, 0, 0);
+            });
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- mask, online softmax (base 2), P in bf16
@@ -1155,30 +1139,17 @@ void tree_attn_split_kernel(
           for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
       }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- O^T += V^T . P^T, V fragments (cp, db) in batches as K's
+      // ---- O^T += V^T . P^T, V fragments (cp, db) batched as K's
       {
         constexpr int NF = CPT * DB;
-        constexpr int PFB = NF < kFragBatch ? NF : kFragBatch;
-        static_assert(NF % PFB == 0, "whole batches");
         bf16x8_t va[NF];
-        auto vread = [&](int f) { va[f] = read_v(vs, wt * CPT + f / DB, f % DB); };
-        auto vmma = [&](int f) {
+        batched_products<NF, (NF < kFragBatch ? NF : kFragBatch)>(
+            [&](int f) { va[f] = read_v(vs, wt * CPT + f / DB, f % DB); },
+            [&](int f) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            oacc[rb][f % DB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pb[rb][f / DB], oacc[rb][f % DB], 0, 0, 0);
-        };
-#pragma unroll
-        for (int f = 0; f < PFB; ++f) vread(f);
-#pragma unroll
-        for (int j = 0; j < NF / PFB; ++j) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (j + 1 < NF / PFB) {
-#pragma unroll
-            for (int f = 0; f < PFB; ++f) vread((j + 1) * PFB + f);
-          }
-#pragma unroll
-          for (int f = 0; f < PFB; ++f) vmma(j * PFB + f);
-        }
+              for (int rb = 0; rb < RB; ++rb)
+                oacc[rb][f % DB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pb[rb][f / DB], oacc[rb][f % DB], 0, 0, 0);
+            });
       }
     };
 

@@ -263,20 +263,7 @@ void tree_attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restr
             else sacc[rb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], qreg[rb][c], sacc[rb][G], 0, 0, 0);
           }
         };
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int x = 0; x < PB; ++x) rd(x);
-#pragma unroll
-        for (int jb = 0; jb < NF / PB; ++jb) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (jb + 1 < NF / PB) {
-#pragma unroll
-            for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
-          }
-#pragma unroll
-          for (int x = 0; x < PB; ++x) mm(jb * PB + x);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        batched_products<NF, PB>(rd, mm);
       }
       // p and ds in registers, ds in bf16 as the dq product's B operand
       bf16x8_t dsb[RB];
@@ -313,20 +300,7 @@ void tree_attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restr
           for (int rb = 0; rb < RB; ++rb)
             dqacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[db], dsb[rb], dqacc[rb][db], 0, 0, 0);
         };
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int x = 0; x < PB; ++x) rd(x);
-#pragma unroll
-        for (int jb = 0; jb < DB / PB; ++jb) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (jb + 1 < DB / PB) {
-#pragma unroll
-            for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
-          }
-#pragma unroll
-          for (int x = 0; x < PB; ++x) mm(jb * PB + x);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        batched_products<DB, PB>(rd, mm);
       }
     }
   };
@@ -476,20 +450,7 @@ void tree_attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __res
         if (x & 1) pacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], vf[c], pacc[mb], 0, 0, 0);
         else sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], kf[c], sacc[mb], 0, 0, 0);
       };
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int x = 0; x < PB; ++x) rd(x);
-#pragma unroll
-      for (int jb = 0; jb < NF / PB; ++jb) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (jb + 1 < NF / PB) {
-#pragma unroll
-          for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
-        }
-#pragma unroll
-        for (int x = 0; x < PB; ++x) mm(jb * PB + x);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      batched_products<NF, PB>(rd, mm);
     }
     // ---- p and ds of rows 16mb + 4lg + r at this lane's key; K-slot t of
     // k-step s holds row 32s + 4lg + t (t < 4) or 32s + 16 + 4lg + t - 4
@@ -532,20 +493,7 @@ void tree_attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __res
         if (x & 1) dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], dsb[sx], dkacc[db], 0, 0, 0);
         else dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[x], pb[sx], dvacc[db], 0, 0, 0);
       };
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int x = 0; x < PB; ++x) rd(x);
-#pragma unroll
-      for (int jb = 0; jb < NF / PB; ++jb) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (jb + 1 < NF / PB) {
-#pragma unroll
-          for (int x = 0; x < PB; ++x) rd((jb + 1) * PB + x);
-        }
-#pragma unroll
-        for (int x = 0; x < PB; ++x) mm(jb * PB + x);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      batched_products<NF, PB>(rd, mm);
     }
   };
 
