@@ -230,6 +230,34 @@ def test_attention_edge_cases(name):
     _attn_case(w, name)
 
 
+RAMPS = {
+    # 960 packed rows (the 8-wave plan), one piece per sequence
+    "m960_rising": (W[3].replace(B=1, prefix_lo=900, prefix_hi=900, V=10, seed=81), "rising"),
+    # 128 rows over ragged prefixes (balanced pieces, split merges)
+    "m128_rising_ragged": (W[2].replace(B=3, prefix_lo=300, prefix_hi=2500, V=10, seed=82), "rising"),
+    "m128_sawtooth": (W[2].replace(B=2, prefix_lo=1500, prefix_hi=1500, V=10, seed=83), "sawtooth"),
+    # 24 rows, fixed splits and their merge
+    "m24_sawtooth": (W[1].replace(B=2, prefix_lo=2000, prefix_hi=2000, V=10, seed=84), "sawtooth"),
+}
+
+
+@pytest.mark.parametrize("name", list(RAMPS))
+def test_attention_moving_row_max(name):
+    """Scores whose row maxima keep rising along the sequence (K rows scaled up
+    to 16x with the token position) or jump up every 256 tokens (a sawtooth of
+    scales 1..12): the running reference max of the online softmax then moves
+    on many tiles, by more and by less than its lag, inside pieces and across
+    the split merge."""
+    w, shape = RAMPS[name]
+    x = synth.make_inputs(w, with_logits=False)
+    k = x["k_cache"].float()
+    t = torch.arange(k.shape[2], dtype=torch.float32)
+    f = 1.0 + 15.0 * t / k.shape[2] if shape == "rising" else 1.0 + (t // 256) % 12
+    k = (k * f[None, None, :, None]).to(x["k_cache"].dtype)
+    log(f"[moving max] {name}: K scaled {shape}, up to {float(f.max()):.0f}x")
+    _attn_case(w, name, k_cache=k)
+
+
 def test_attention_many_splits_short_requests():
     """Cache capacity far above the used length: many splits per request in the
     grid, most of them empty; requests of 1, 2 and several splits side by side."""
