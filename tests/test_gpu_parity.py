@@ -218,6 +218,9 @@ EDGE = {
                              tree="random", max_depth=5, max_children=3),
     "m48_four_waves_rb1": W[1].replace(B=2, N=12, Hq=16, Hkv=4, prefix_lo=190, prefix_hi=190, V=10, seed=35),
     "m960_tiles": W[3].replace(B=1, prefix_lo=130, prefix_hi=130, V=10, seed=36),
+    # 256 packed rows with D = 64 (128-row tiles: the 8-wave plan is for D = 128), bf16 and e4m3 caches
+    "m256_d64": W[2].replace(B=2, N=32, D=64, prefix_lo=200, prefix_hi=700, V=10, seed=38),
+    "m256_d64_fp8": W[2].replace(B=2, N=32, D=64, kv_dtype="e4m3", prefix_lo=300, prefix_hi=300, V=10, seed=39),
     "f32_d128": W[0].replace(B=2, D=128, Hq=6, Hkv=3, N=9, prefix_lo=31, prefix_hi=300, tree="random",
                              max_depth=4, max_children=3, V=10, seed=37),
 }

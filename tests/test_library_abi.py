@@ -61,6 +61,8 @@ def test_workspace_bytes_is_pure_and_rejects_bad_shapes(L):
     # M = 376 (three 128-row tiles, which 256-row tiles would pad to 512): the 4-wave plan, 512 // 3 units
     # of 3 splits (a sequence of 33 tiles), two slots per unit
     assert f(8, 47, 64, 8, 128, 2054) == 2 * (512 // 3) * 384 * (128 * 4 + 8) + 64 * 3 * 4
+    # M = 256 with D = 64: 128-row tiles (two M-tiles, so two counters per sequence), 512 slots / 2 = 256 units
+    assert f(2, 32, 64, 8, 64, 1000) == 2 * 256 * 256 * (64 * 4 + 8) + 16 * 2 * 4
     assert f(1024, 6, 32, 8, 128, 2 ** 21 - 1) > 0
     for bad in [(0, 6, 32, 8, 128, 2054), (8, 0, 32, 8, 128, 2054), (8, 65, 32, 8, 128, 2054),
                 (8, 6, 30, 8, 128, 2054), (8, 6, 32, 8, 96, 2054), (8, 6, 32, 8, 128, 5),

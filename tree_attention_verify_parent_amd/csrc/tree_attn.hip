@@ -1536,8 +1536,10 @@ constexpr int kTableBytes = 4 * (1024 + 1) + 4;
 // Rows per workgroup follow the packed M = g*N.  Small M (<= 32) lets the
 // waves also split each tile's tokens (a 3-stage K/V ring, one workgroup per
 // CU); larger M splits rows over the waves (a 2-stage ring, two workgroups per
-// CU, so two waves share each SIMD).  Above 128 rows, when 256-row tiles pad M
-// no further than 128-row ones, one 8-wave workgroup a CU takes 256 rows: each
+// CU, so two waves share each SIMD).  Above 128 rows with D = 128, when 256-row
+// tiles pad M no further than 128-row ones, one 8-wave workgroup a CU takes
+// 256 rows (with D = 64 an e4m3 tile is too small to give all 8 waves a DMA
+// instruction, so D = 64 keeps 128-row tiles): each
 // K/V tile then reaches LDS once for 256 rows instead of twice for 128 (60-node
 // trees of 16 heads at 32768 tokens: 971 -> 920 us).  Work then comes in about one unit per
 // resident workgroup slot (256 CUs), each unit for all M-tiles, under one of
@@ -1557,7 +1559,7 @@ static bool make_plan(int B, int N, int Hq, int Hkv, int D, int S_max, AttnPlan*
   const int M = (Hq / Hkv) * N;
   if (M <= 32) { p->rb = 1; p->wm = 2; p->wt = 2; p->nstage = 3; }
   else if (M <= 64) { p->rb = 2; p->wm = 2; p->wt = 1; p->nstage = 2; }
-  else if (((M + 127) / 128) % 2 == 1) { p->rb = 2; p->wm = 4; p->wt = 1; p->nstage = 2; }
+  else if (D != 128 || ((M + 127) / 128) % 2 == 1) { p->rb = 2; p->wm = 4; p->wt = 1; p->nstage = 2; }
   else { p->rb = 2; p->wm = 8; p->wt = 1; p->nstage = 2; }
   const int lds_bf16 = p->nstage * 2 * kTile * D * 2 + kTableBytes;
   // an 8-wave workgroup takes both of a CU's wave slots per SIMD at this
