@@ -23,6 +23,8 @@ CASES = {
     "chain6_bf16_p32": (W[1].replace(B=4, prefix_lo=700, prefix_hi=700, V=10, seed=63), 32),
     "tree16_fp8kv_p16": (W[4].replace(B=3, prefix_lo=500, prefix_hi=500, V=10, seed=64), 16),
     "tree60_bf16_p128": (W[3].replace(B=1, prefix_lo=900, prefix_hi=900, V=10, seed=65), 128),
+    # 960 packed rows over e4m3 pages and ragged prefixes (the 8-wave plan's paged path)
+    "tree60_fp8kv_ragged_p16": (W[3].replace(B=2, kv_dtype="e4m3", prefix_lo=200, prefix_hi=1100, V=10, seed=67), 16),
     "tree16_d64_p1": (W[2].replace(B=3, D=64, Hq=8, Hkv=2, prefix_lo=40, prefix_hi=300, V=10, seed=66), 1),
 }
 

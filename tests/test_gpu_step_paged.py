@@ -28,6 +28,7 @@ CASES = {
     "chain6_b8_bf16_p16": (W[1], 16),
     "tree16_ragged_V5003_p64": (W[2].replace(B=4, prefix_lo=100, prefix_hi=1500, V=5003, seed=41), 64),
     "tree60_V4099_p128": (W[3].replace(B=2, prefix_lo=777, prefix_hi=777, V=4099, seed=42), 128),
+    "tree60_fp8kv_ragged_p32": (W[3].replace(B=2, kv_dtype="e4m3", prefix_lo=150, prefix_hi=900, V=2000, seed=46), 32),
     "tree16_fp8kv_p32": (W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=6000, seed=43), 32),
     "tree16_d64_p1": (W[2].replace(B=3, D=64, Hq=8, Hkv=2, prefix_lo=40, prefix_hi=300, V=1000, seed=44), 1),
     # the largest page: every request's tokens in one page of 4096
