@@ -34,6 +34,8 @@ CASES = {
     "tree16_V151936": W[2].replace(B=3, prefix_lo=64, prefix_hi=300, seed=22),
     "tree60_V4099": W[3].replace(B=2, prefix_lo=777, prefix_hi=777, V=4099, seed=23),
     "tree16_fp8kv": W[4].replace(B=4, prefix_lo=333, prefix_hi=333, V=6000, seed=24),
+    # 960 packed rows (the 8-wave plan) over an e4m3 cache and ragged prefixes
+    "tree60_fp8kv_ragged": W[3].replace(B=2, kv_dtype="e4m3", prefix_lo=200, prefix_hi=1000, V=3001, seed=26),
     "chain6_f32_V1000": W[0],
     # the fp32 kernel with ~32 key chunks per row, about 8 per wave
     "tree16_f32_d128_p2000": W[0].replace(B=2, N=16, tree="random", max_depth=5, max_children=3, Hq=8, Hkv=2, D=128,
